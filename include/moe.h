@@ -1,0 +1,275 @@
+/*
+ * moe.h -- C ABI of the paged fused-MoE layer for MI355X (gfx950).
+ *
+ * One MoE layer routes each token to k experts and runs every chosen expert's
+ * SwiGLU FFN, y_t = sum_j w_{t,j} * W2_e (silu(W1_e x_t) * (W3_e x_t)), reading
+ * the expert weights in place: from pages of a shared pool addressed through a
+ * per-expert page table, or from a slot of one of two load buffers, never from
+ * a copy gathered into a contiguous weight array.
+ *
+ * Source: "Rimuru: Unified Memory Management for Modern LLM Serving via Elastic
+ * Expert Offloading" (paper-daily.com digest), sections
+ *   "One pool for data whose sizes differ by orders of magnitude" (one
+ *     contiguous pool read through typed views; expert pages),
+ *   "Expert weights are scattered across pages. How does the kernel read them?"
+ *     (location metadata per expert: a page number when cached, a buffer slot
+ *     when just copied in; W1/W3 picked by column half; the address formula
+ *     addr_e(n,t) = B_P + p_e(n)*f*d + (n mod f)*d + t; two alternating load
+ *     buffers),
+ *   "The adjuster: when to evict an expert, and which one?" (three pages per
+ *     expert: W1 gate, W3 up, W2 down; copies finish before the page table
+ *     points at them, pages are reused only after the forward pass ends).
+ *
+ * Conventions for every entry point:
+ *   - Every data pointer is caller-owned memory.  "device" means memory of the
+ *     current HIP device (e.g. a torch tensor's data_ptr); "host" means plain
+ *     CPU memory; "pinned host" means page-locked memory from hipHostMalloc or
+ *     torch's pin_memory.  The library never frees caller memory.
+ *   - bf16 means IEEE bfloat16 bit patterns (uint16), row-major, no padding.
+ *     bf16 arrays, load buffers and workspaces must be 16-byte aligned
+ *     (workspaces 256-byte), int32 / fp32 arrays 4-byte and int64 arrays
+ *     8-byte aligned (MOE_ERR_ALIGN otherwise).
+ *   - `stream` is a hipStream_t passed as void* (NULL = the legacy default
+ *     stream).  Work is enqueued asynchronously; no entry point synchronises
+ *     the host with the device except where stated.
+ *   - Return value: MOE_OK (0) or a negative MOE_ERR_* code.  Arguments are
+ *     validated on the host before anything is launched; on error nothing is
+ *     launched and moe_last_error() describes the problem.  A device fault of an
+ *     earlier launch surfaces as MOE_ERR_HIP on a later call.  No exception
+ *     crosses this boundary.
+ *   - T = 0 tokens is a valid no-op.
+ */
+#ifndef PMOE_MOE_H
+#define PMOE_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_OK 0
+#define MOE_ERR_INVALID_ARG (-1) /* null pointer, size out of range, bad flag */
+#define MOE_ERR_PAGE_RANGE (-2)  /* a page number outside [0, num_pages) */
+#define MOE_ERR_PAGE_ALIAS (-3)  /* two expert matrices on one page */
+#define MOE_ERR_SLOT_RANGE (-4)  /* a load-buffer slot outside [0, loadbuf_slots) or used twice */
+#define MOE_ERR_ALIGN (-5)       /* a device pointer not 16-byte aligned */
+#define MOE_ERR_WORKSPACE (-6)   /* workspace or output capacity too small */
+#define MOE_ERR_STATE (-7)       /* double-buffer misuse, e.g. reading a never-filled buffer */
+#define MOE_ERR_HIP (-8)         /* a HIP runtime call failed */
+#define MOE_ERR_UNSUPPORTED (-9) /* shape the kernels do not handle (see moe_pool_desc) */
+
+/* kinds of one location-table entry */
+#define MOE_LOC_POOL 0    /* idx = {W1 page, W3 page, W2 page} */
+#define MOE_LOC_LOADBUF 1 /* idx[0] = slot in the active load buffer; idx[1], idx[2] ignored */
+
+/* forward flags */
+#define MOE_FLAG_ATOMIC_COMBINE 1u /* combine the k partial outputs with fp32 atomics
+                                      (faster, summation order not reproducible);
+                                      default: fixed slot order, bit-reproducible */
+
+typedef struct moe_pool moe_pool; /* opaque handle: one MoE layer's view of the pool */
+
+/*
+ * Shape of one MoE layer and where its weights may live.
+ *   pool_base       device, bf16, num_pages pages of f*d elements each.  Page p
+ *                   starts at element p*f*d.  W1 and W3 pages are [f rows][d]
+ *                   (row n of W1 is output column n; contiguous along d).  A W2
+ *                   page is [d rows][f] (the pages do not fix the down
+ *                   projection's layout; this mirrors W1/W3, contiguous along f).
+ *   num_pages       >= 1.
+ *   d, f            hidden and intermediate size; each a positive multiple of 64.
+ *   num_experts     routed experts E, 1..1024.
+ *   top_k           1..min(E, 32).
+ *   num_shared      0 or 1.  A shared expert is id E, always chosen with
+ *                   weight 1, appended after the k routed picks.
+ *   loadbuf_slots   slots per load buffer (0 = no load buffer).  A slot holds
+ *                   one expert as 3*f*d bf16: W1, W3, W2 back to back.
+ *   loadbuf_base[b] device base of load buffer b (b = 0, 1); may be NULL when
+ *                   loadbuf_slots == 0.  The two buffers alternate: one feeds
+ *                   this layer while the other receives the next layer's experts.
+ */
+typedef struct {
+    void *pool_base;
+    int64_t num_pages;
+    int32_t d, f;
+    int32_t num_experts;
+    int32_t top_k;
+    int32_t num_shared;
+    int32_t loadbuf_slots;
+    void *loadbuf_base[2];
+} moe_pool_desc;
+
+/* One location-table entry (16 bytes).  See MOE_LOC_*. */
+typedef struct {
+    int32_t kind;
+    int32_t idx[3];
+} moe_expert_loc;
+
+/*
+ * Create a layer handle.  Validates desc (MOE_ERR_INVALID_ARG /
+ * MOE_ERR_UNSUPPORTED / MOE_ERR_ALIGN), then allocates the handle's own small
+ * state on the current device: the device copy of the location table
+ * (E + S entries), a pinned staging copy, and four hipEvents (filled and
+ * consumed, per load buffer).  The table starts with every expert unset; a
+ * forward before moe_set_expert_locs fails with MOE_ERR_STATE.
+ * *out receives the handle; destroy it with moe_pool_destroy.
+ */
+int moe_pool_create(const moe_pool_desc *desc, moe_pool **out);
+
+/* Release the handle's state.  Waits for the handle's own pending work. NULL is a no-op. */
+int moe_pool_destroy(moe_pool *pool);
+
+/*
+ * Host-only check of a location table against desc; touches no GPU.
+ * locs: host array of n = num_experts + num_shared entries.  Errors:
+ * MOE_ERR_INVALID_ARG (n or a kind wrong), MOE_ERR_PAGE_RANGE, MOE_ERR_PAGE_ALIAS
+ * (a page used twice by any two matrices), MOE_ERR_SLOT_RANGE (slot out of
+ * range, or one slot given to two experts).
+ */
+int moe_validate_locs(const moe_pool_desc *desc, const moe_expert_loc *locs, int32_t n);
+
+/*
+ * Point the layer's page table at new locations (the page-table update on the
+ * GPU side in the digest's scheduling-round pipeline).  locs: host, n = E + S entries, validated as by
+ * moe_validate_locs.  The upload is ordered on `stream`: forwards enqueued on
+ * `stream` afterwards see the new table, forwards enqueued before it see the
+ * old one.  The caller must order forwards on other streams itself.  The host
+ * array may be reused as soon as the call returns.
+ */
+int moe_set_expert_locs(moe_pool *pool, const moe_expert_loc *locs, int32_t n, void *stream);
+
+/*
+ * Capacities the routing outputs need for T tokens and tile height block_m:
+ *   *sorted_cap = T*(k+S) + (E+S)*(block_m-1)  entries of sorted_ids
+ *   *blocks_cap = ceil(sorted_cap / block_m)   entries of block_expert
+ * block_m must be one of 16, 32, 64, 128, 256.
+ */
+int moe_route_capacity(const moe_pool *pool, int64_t T, int32_t block_m,
+                       int64_t *sorted_cap, int64_t *blocks_cap);
+
+/* Bytes of device workspace moe_route and the forwards need for (T, block_m, flags). */
+int moe_workspace_bytes(const moe_pool *pool, int64_t T, int32_t block_m, uint32_t flags,
+                        size_t *bytes);
+
+/*
+ * Routing and token alignment, all on the device, no host synchronisation.
+ *   logits       device fp32 [T][E] router logits (finite values).
+ *   topk_ids     device int32 [T][k+S] out: per token the k experts with the
+ *                largest logits, largest first, equal logits to the lower id;
+ *                then the shared expert id E when S = 1.
+ *   topk_w       device fp32 [T][k+S] out: softmax of the chosen logits
+ *                renormalised over the k picks; 1.0 for the shared expert.
+ *   sorted_ids   device int32 [sorted_cap] out: flat indices i = t*(k+S)+j
+ *                grouped by expert (ascending id), ascending i within an
+ *                expert, each expert's segment padded with the sentinel T*(k+S)
+ *                to a multiple of block_m.  Entries past *num_padded are
+ *                unspecified.
+ *   block_expert device int32 [blocks_cap] out: expert of each block_m-row block.
+ *   num_padded   device int32 [1] out: total rows in sorted_ids (a multiple of block_m).
+ *   workspace    device, >= moe_workspace_bytes(pool, T, block_m, 0) bytes.
+ */
+int moe_route(moe_pool *pool, const float *logits, int64_t T, int32_t block_m,
+              int32_t *topk_ids, float *topk_w, int32_t *sorted_ids, int32_t *block_expert,
+              int32_t *num_padded, void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * The layer output from the routing above, reading the weights in place.
+ *   x            device bf16 [T][d] hidden states.
+ *   topk_ids ... num_padded: as produced by moe_route with the same block_m.
+ *   active_buf   0 or 1: the load buffer the MOE_LOC_LOADBUF experts are read
+ *                from.  The forward waits (on `stream`, via an event) for the
+ *                last moe_loadbuf_fill of that buffer, and marks the buffer
+ *                consumed when its last read is done; it fails with
+ *                MOE_ERR_STATE if the table names load-buffer experts and that
+ *                buffer was never filled.
+ *   y            device bf16 [T][d] out.
+ *   workspace    device, >= moe_workspace_bytes(pool, T, block_m, flags) bytes;
+ *                holds the SiLU-gated activations [sorted_cap][f] (bf16) and the
+ *                combine buffer (fp32).  Not kept between calls.
+ *   flags        0 or MOE_FLAG_ATOMIC_COMBINE.
+ * Gate/up GEMM: each output tile resolves its W1 and W3 page bases once and
+ * fuses silu(gate) * up into its epilogue; down GEMM: each tile resolves its
+ * W2 page once and scales by the routing weight; the k+S partial rows of a
+ * token are summed in fp32 in slot order and rounded to bf16 once.
+ */
+int moe_paged_forward(moe_pool *pool, const void *x, int64_t T, int32_t block_m,
+                      const int32_t *topk_ids, const float *topk_w, const int32_t *sorted_ids,
+                      const int32_t *block_expert, const int32_t *num_padded, int32_t active_buf,
+                      void *y, void *workspace, size_t ws_bytes, uint32_t flags, void *stream);
+
+/*
+ * The same layer with the weights in two dense arrays (the contiguous
+ * baseline the paged kernel is measured against; same kernels and tile
+ * schedule, only the per-tile base address differs, so results are
+ * bit-identical to moe_paged_forward for the same weights).
+ *   w13  device bf16 [E+S][2f][d]: rows [0,f) W1, rows [f,2f) W3 of each expert.
+ *   w2   device bf16 [E+S][d][f].
+ * The pool handle supplies the shape only; its page table is not read.
+ */
+int moe_contiguous_forward(const moe_pool *pool, const void *w13, const void *w2, const void *x,
+                           int64_t T, int32_t block_m, const int32_t *topk_ids,
+                           const float *topk_w, const int32_t *sorted_ids,
+                           const int32_t *block_expert, const int32_t *num_padded, void *y,
+                           void *workspace, size_t ws_bytes, uint32_t flags, void *stream);
+
+/*
+ * Fill slots of load buffer `buf` from pinned host memory on `copy_stream`
+ * (the digest's double-buffered loading: this layer computes from one buffer
+ * while the other receives the next layer's experts).
+ *   slots[i]     slot to fill (host int32, n entries, distinct).
+ *   host_src[i]  pinned host, 3*f*d bf16 (W1, W3, W2 back to back).
+ * The copies wait for the last forward that read `buf` (write-after-read) and
+ * for earlier fills of `buf`; the buffer's "filled" event is recorded after
+ * them, and the next forward reading `buf` waits for it (read-after-write).
+ */
+int moe_loadbuf_fill(moe_pool *pool, int32_t buf, int32_t n, const int32_t *slots,
+                     const void *const *host_src, void *copy_stream);
+
+/*
+ * Resolve weight addresses on the device with the same per-tile resolver the
+ * GEMM kernels use, for checking against the address formula.
+ *   e, which, row, col  device int32/int32/int64/int64 [n] queries:
+ *       which 0: gate/up operand, row = output column n in [0, 2f), col = t in [0, d)
+ *       which 1: down projection, row in [0, d), col in [0, f)
+ *   off   device int64 [n] out: element offset from the base below
+ *   base  device int32 [n] out: 0 = pool_base, 1 + b = loadbuf_base[b]; -1 for
+ *         a query out of range (off = -1)
+ *   active_buf selects the load buffer for MOE_LOC_LOADBUF experts.
+ */
+int moe_resolve_addrs(moe_pool *pool, int32_t active_buf, int64_t n, const int32_t *e,
+                      const int32_t *which, const int64_t *row, const int64_t *col,
+                      int64_t *off, int32_t *base, void *stream);
+
+/*
+ * A block_m for T tokens: the tile height that covers the expected rows per
+ * active expert ((T*(k+S)) / min(T*(k+S), E+S)) in few tiles without mostly
+ * padding.  Any of 16, 32, 64, 128, 256 is valid for every entry point.
+ */
+int32_t moe_suggest_block_m(const moe_pool *pool, int64_t T);
+
+/*
+ * Stage timing of paged forwards, for measurement.  With enable != 0 every
+ * moe_paged_forward of this handle records four hipEvents on its stream:
+ * before the gate/up GEMM, after it, after the down GEMM and after the
+ * combine (at most 1024 forwards are recorded; later ones run untimed).
+ * moe_stage_times waits for the recorded forwards, writes the summed
+ * milliseconds of the three stages to ms[0..2] (gate/up, down, combine) and
+ * their number to *count, and starts a new recording.  enable = 0 stops
+ * recording.  The events add a marker between kernels; time the whole
+ * forward with recording off.
+ */
+int moe_stage_timing(moe_pool *pool, int32_t enable);
+int moe_stage_times(moe_pool *pool, float *ms, int32_t *count);
+
+/* Message for the last non-zero return on this thread ("" if none). */
+const char *moe_last_error(void);
+
+/* ABI version (major*100 + minor). */
+int moe_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PMOE_MOE_H */

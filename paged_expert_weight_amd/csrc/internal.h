@@ -1,0 +1,75 @@
+// Internal declarations shared by the host runtime and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pmoe {
+
+// Device copy of one location-table entry; same 16-byte layout as moe_expert_loc.
+struct DevLoc {
+    int32_t kind;   // 0 pool page, 1 load-buffer slot
+    int32_t idx[3]; // pool: W1, W3, W2 page; load buffer: slot in idx[0]
+};
+
+constexpr int kMaxExpertsTotal = 1024; // E + S
+constexpr int kMaxTopK = 32;
+
+struct RouteArgs {
+    const float *logits;
+    int64_t T;
+    int E, k, S, keff, E_tot, BM;
+    int32_t *topk_ids;
+    float *topk_w;
+    int32_t *sorted_ids;
+    int32_t *block_expert;
+    int32_t *num_padded;
+    int64_t sorted_cap, blocks_cap;
+    int32_t *counts; // workspace: [nchunks][E_tot] (large path only)
+};
+
+// Route + align.  Picks the fused one-workgroup path for small T, otherwise
+// route / histogram / scan / scatter.
+hipError_t launch_route_align(const RouteArgs &a, hipStream_t s);
+int64_t route_workspace_bytes(int64_t T, int keff, int E_tot);
+
+struct FwdArgs {
+    // weights: paged (locs != nullptr) or contiguous
+    const DevLoc *locs;
+    const uint16_t *pool;
+    const uint16_t *loadbuf; // active load buffer (may be null)
+    const uint16_t *w13;     // contiguous only
+    const uint16_t *w2;      // contiguous only
+    const uint16_t *x;
+    int64_t T;
+    int d, f, keff, E_tot, BM;
+    const int32_t *topk_ids;
+    const float *topk_w;
+    const int32_t *sorted_ids;
+    const int32_t *block_expert;
+    const int32_t *num_padded;
+    int64_t sorted_cap, blocks_cap;
+    uint16_t *y;
+    uint16_t *h;  // workspace [sorted_cap][f] bf16
+    float *comb;  // workspace: [T*keff][d] (ordered) or [T][d] (atomic) fp32
+    bool atomic;
+    hipEvent_t ev[4]; // optional: recorded before gate/up, after gate/up, after down, after combine
+};
+
+hipError_t launch_forward(const FwdArgs &a, hipStream_t s);
+
+struct ResolveArgs {
+    const DevLoc *locs;
+    const uint16_t *pool;
+    const uint16_t *loadbuf0, *loadbuf1;
+    int active_buf;
+    int d, f, E_tot;
+    int64_t n;
+    const int32_t *e, *which;
+    const int64_t *row, *col;
+    int64_t *off;
+    int32_t *base;
+};
+hipError_t launch_resolve(const ResolveArgs &a, hipStream_t s);
+
+} // namespace pmoe

@@ -1,0 +1,394 @@
+// Top-k softmax routing and token alignment (gfx950, wave64).
+//
+// Routing: one wave per token.  Lane L holds logits L, L+64, ...; each of the k
+// rounds takes a lane-local best, then a butterfly max over the wave with a
+// strict total order (larger logit first, equal logits to the lower id), so all
+// lanes agree on the winner.  Lane j keeps pick j; the weights are the softmax
+// of the k picks renormalised over them, exp(l_j - l_0) / sum_i exp(l_i - l_0),
+// in fp32.  A shared expert (id E, weight 1) is appended as pick k.  The pages
+// do not print a routing rule; this is the top-k softmax router of the MoE layer
+// whose fused kernel the Rimuru digest's kernel section rewrites.
+//
+// Alignment: a stable counting sort of the flat picks i = t*(k+S) + j by expert
+// with each expert's run padded to the GEMM tile height BM, so that every
+// BM-row block of the grouped GEMMs belongs to one expert:
+//   histogram (per chunk of flat entries, LDS atomics: counts are order free)
+//   -> exclusive scan of the padded counts over experts, and of the raw counts
+//      over chunks (the start of every (chunk, expert) run)
+//   -> in-order scatter: inside a chunk each wave owns a contiguous range and
+//      walks it 64 entries at a time; the lanes holding one expert are found
+//      with a ballot, ranked by popcount of the lower lanes, and the run's
+//      cursor advances by the ballot's popcount, so the order is the flat order.
+// Small batches run all of it in one workgroup (one launch); large batches use
+// route, histogram, scan and scatter kernels.
+#include "internal.h"
+
+namespace pmoe {
+namespace {
+
+constexpr int kAlignWaves = 8;
+constexpr int kAlignThreads = 64 * kAlignWaves;
+constexpr int kChunkElems = 2048; // flat entries per alignment chunk
+constexpr int kSmallTokens = 64;  // one-workgroup route + align when T <= this and T*keff <= kChunkElems
+
+__device__ __forceinline__ bool beats(float va, int ia, float vb, int ib)
+{
+    if (ia < 0)
+        return false;
+    if (ib < 0)
+        return true;
+    return va > vb || (va == vb && ia < ib);
+}
+
+// Route one token with one wave.  Writes ids/w[0 .. k+S) and, when lds_ids is
+// not null, the ids into LDS as well.
+template <int NV>
+__device__ void route_token(const float *row, int E, int k, int S, int lane, int32_t *ids, float *w,
+                            int32_t *lds_ids)
+{
+    float v[NV];
+    uint32_t taken = 0;
+#pragma unroll
+    for (int i = 0; i < NV; i++) {
+        const int e = lane + 64 * i;
+        v[i] = e < E ? row[e] : 0.f;
+        if (e >= E)
+            taken |= 1u << i;
+    }
+    float my_v = 0.f;
+    int my_id = 0;
+    for (int j = 0; j < k; j++) {
+        float bv = 0.f;
+        int bi = -1;
+#pragma unroll
+        for (int i = 0; i < NV; i++) {
+            if (!((taken >> i) & 1u) && beats(v[i], lane + 64 * i, bv, bi)) {
+                bv = v[i];
+                bi = lane + 64 * i;
+            }
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+            const float ov = __shfl_xor(bv, off);
+            const int oi = __shfl_xor(bi, off);
+            if (beats(ov, oi, bv, bi)) {
+                bv = ov;
+                bi = oi;
+            }
+        }
+        if (bi >= 0 && (bi & 63) == lane)
+            taken |= 1u << (bi >> 6);
+        if (lane == j) {
+            my_v = bv;
+            my_id = bi;
+        }
+    }
+    const float lmax = __shfl(my_v, 0);
+    const float ex = lane < k ? expf(my_v - lmax) : 0.f;
+    float sum = ex;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1)
+        sum += __shfl_xor(sum, off); // commutative pairs: every lane ends with the same sum
+    if (lane < k) {
+        ids[lane] = my_id;
+        w[lane] = ex / sum;
+        if (lds_ids)
+            lds_ids[lane] = my_id;
+    }
+    if (S && lane == k) {
+        ids[k] = E;
+        w[k] = 1.f;
+        if (lds_ids)
+            lds_ids[k] = E;
+    }
+}
+
+template <int NV>
+__global__ __launch_bounds__(256) void k_route(const RouteArgs a)
+{
+    const int lane = threadIdx.x & 63;
+    const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= a.T)
+        return;
+    route_token<NV>(a.logits + t * a.E, a.E, a.k, a.S, lane, a.topk_ids + t * a.keff,
+                    a.topk_w + t * a.keff, nullptr);
+}
+
+__device__ __forceinline__ void wave_range(int n, int w, int &lo, int &hi)
+{
+    int per = (n + kAlignWaves - 1) / kAlignWaves;
+    per = (per + 63) & ~63;
+    lo = min(n, w * per);
+    hi = min(n, lo + per);
+}
+
+// Per-wave histogram of the chunk held in s_ids[0..n).  s_cnt[w*E_tot + e] must be zero.
+__device__ void chunk_hist(const int32_t *s_ids, int n, int E_tot, int *s_cnt)
+{
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    int lo, hi;
+    wave_range(n, w, lo, hi);
+    for (int i = lo + lane; i < hi; i += 64)
+        atomicAdd(&s_cnt[w * E_tot + s_ids[i]], 1);
+}
+
+// Exclusive scan across the workgroup of one int per thread; *total gets the sum.
+__device__ int wg_exclusive_scan(int v, int *s_tmp, int *total)
+{
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    int x = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(x, off);
+        if (lane >= off)
+            x += y;
+    }
+    if (lane == 63)
+        s_tmp[w] = x;
+    __syncthreads();
+    int before = 0, all = 0;
+    for (int i = 0; i < kAlignWaves; i++) {
+        const int s = s_tmp[i];
+        before += i < w ? s : 0;
+        all += s;
+    }
+    __syncthreads();
+    *total = all;
+    return before + x - v;
+}
+
+// Given per-expert token counts cnt(e), write each expert's padded segment start
+// into seg_start[e], the block->expert map, the sentinel padding and num_padded.
+// Each thread owns experts 2*tid and 2*tid+1 (E_tot <= 2*kAlignThreads).
+template <class CountFn>
+__device__ void scan_experts(CountFn cnt, int E_tot, int BM, int n, int *seg_start, int *s_tmp,
+                             const RouteArgs &a)
+{
+    const int e0 = 2 * threadIdx.x, e1 = e0 + 1;
+    const int c0 = e0 < E_tot ? cnt(e0) : 0;
+    const int c1 = e1 < E_tot ? cnt(e1) : 0;
+    const int p0 = (c0 + BM - 1) / BM * BM;
+    const int p1 = (c1 + BM - 1) / BM * BM;
+    int total;
+    const int o0 = wg_exclusive_scan(p0 + p1, s_tmp, &total);
+    const int o1 = o0 + p0;
+    if (e0 < E_tot)
+        seg_start[e0] = o0;
+    if (e1 < E_tot)
+        seg_start[e1] = o1;
+    for (int pass = 0; pass < 2; pass++) {
+        const int e = pass ? e1 : e0, c = pass ? c1 : c0, p = pass ? p1 : p0, o = pass ? o1 : o0;
+        if (e >= E_tot)
+            continue;
+        for (int b = o / BM; b < (o + p) / BM; b++)
+            a.block_expert[b] = e;
+        for (int pos = o + c; pos < o + p; pos++)
+            a.sorted_ids[pos] = n;
+    }
+    if (threadIdx.x == 0)
+        *a.num_padded = total;
+}
+
+// In-order scatter of the chunk s_ids[0..n) whose first flat index is elem0.
+// s_cur[w*E_tot + e] = position in sorted_ids of wave w's first entry of expert e.
+__device__ void chunk_scatter(const int32_t *s_ids, int n, int elem0, int E_tot, int *s_cur,
+                              int32_t *sorted_ids)
+{
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    int lo, hi;
+    wave_range(n, w, lo, hi);
+    for (int g = lo; g < hi; g += 64) {
+        const int i = g + lane;
+        const bool valid = i < hi;
+        const int e = valid ? s_ids[i] : -1;
+        uint64_t left = __ballot(valid);
+        while (left) {
+            const int leader = __ffsll((unsigned long long)left) - 1;
+            const int le = __shfl(e, leader);
+            const uint64_t mask = __ballot(e == le) & left;
+            const int base = s_cur[w * E_tot + le];
+            if (e == le)
+                sorted_ids[base + __popcll(mask & below)] = elem0 + i;
+            if (lane == leader)
+                s_cur[w * E_tot + le] = base + __popcll(mask);
+            left &= ~mask;
+        }
+    }
+}
+
+// Turn per-wave counts s_cnt[w][e] into per-wave cursors starting at start(e).
+template <class StartFn>
+__device__ void wave_cursors(StartFn start, int E_tot, int *s_cnt)
+{
+    for (int e = threadIdx.x; e < E_tot; e += kAlignThreads) {
+        int run = start(e);
+        for (int w = 0; w < kAlignWaves; w++) {
+            const int c = s_cnt[w * E_tot + e];
+            s_cnt[w * E_tot + e] = run;
+            run += c;
+        }
+    }
+}
+
+struct AlignSmem {
+    int32_t ids[kChunkElems];
+    int cnt[kAlignWaves * kMaxExpertsTotal];
+    int seg[kMaxExpertsTotal];
+    int tmp[kAlignWaves];
+};
+
+// Alignment of a whole batch in one workgroup (n <= kChunkElems); s_ids already filled.
+__device__ void align_in_one_wg(AlignSmem &sm, int n, const RouteArgs &a)
+{
+    chunk_hist(sm.ids, n, a.E_tot, sm.cnt);
+    __syncthreads();
+    auto count = [&](int e) {
+        int c = 0;
+        for (int w = 0; w < kAlignWaves; w++)
+            c += sm.cnt[w * a.E_tot + e];
+        return c;
+    };
+    scan_experts(count, a.E_tot, a.BM, n, sm.seg, sm.tmp, a);
+    __syncthreads();
+    wave_cursors([&](int e) { return sm.seg[e]; }, a.E_tot, sm.cnt);
+    __syncthreads();
+    chunk_scatter(sm.ids, n, 0, a.E_tot, sm.cnt, a.sorted_ids);
+}
+
+__device__ void zero_counts(AlignSmem &sm, int E_tot)
+{
+    for (int i = threadIdx.x; i < kAlignWaves * E_tot; i += kAlignThreads)
+        sm.cnt[i] = 0;
+}
+
+template <int NV>
+__global__ __launch_bounds__(kAlignThreads) void k_route_align_small(const RouteArgs a)
+{
+    __shared__ AlignSmem sm;
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    zero_counts(sm, a.E_tot);
+    for (int t = w; t < (int)a.T; t += kAlignWaves)
+        route_token<NV>(a.logits + (int64_t)t * a.E, a.E, a.k, a.S, lane, a.topk_ids + (int64_t)t * a.keff,
+                        a.topk_w + (int64_t)t * a.keff, sm.ids + t * a.keff);
+    __syncthreads();
+    align_in_one_wg(sm, (int)a.T * a.keff, a);
+}
+
+__global__ __launch_bounds__(kAlignThreads) void k_align_single(const RouteArgs a)
+{
+    __shared__ AlignSmem sm;
+    const int n = (int)a.T * a.keff;
+    zero_counts(sm, a.E_tot);
+    for (int i = threadIdx.x; i < n; i += kAlignThreads)
+        sm.ids[i] = a.topk_ids[i];
+    __syncthreads();
+    align_in_one_wg(sm, n, a);
+}
+
+__global__ __launch_bounds__(kAlignThreads) void k_align_hist(const RouteArgs a)
+{
+    __shared__ int hist[kMaxExpertsTotal];
+    const int64_t n = a.T * a.keff;
+    const int64_t lo = (int64_t)blockIdx.x * kChunkElems;
+    const int cn = (int)min((int64_t)kChunkElems, n - lo);
+    for (int e = threadIdx.x; e < a.E_tot; e += kAlignThreads)
+        hist[e] = 0;
+    __syncthreads();
+    for (int i = threadIdx.x; i < cn; i += kAlignThreads)
+        atomicAdd(&hist[a.topk_ids[lo + i]], 1);
+    __syncthreads();
+    for (int e = threadIdx.x; e < a.E_tot; e += kAlignThreads)
+        a.counts[(int64_t)blockIdx.x * a.E_tot + e] = hist[e];
+}
+
+// One workgroup: segment starts, block map, padding; then counts[ch][e] is
+// replaced in place by the start of chunk ch's run of expert e.
+__global__ __launch_bounds__(kAlignThreads) void k_align_scan(const RouteArgs a, int nch)
+{
+    __shared__ int seg[kMaxExpertsTotal];
+    __shared__ int tmp[kAlignWaves];
+    const int n = (int)(a.T * a.keff);
+    auto count = [&](int e) {
+        int c = 0;
+        for (int ch = 0; ch < nch; ch++)
+            c += a.counts[(int64_t)ch * a.E_tot + e];
+        return c;
+    };
+    scan_experts(count, a.E_tot, a.BM, n, seg, tmp, a);
+    __syncthreads();
+    for (int e = threadIdx.x; e < a.E_tot; e += kAlignThreads) {
+        int run = seg[e];
+        for (int ch = 0; ch < nch; ch++) {
+            const int c = a.counts[(int64_t)ch * a.E_tot + e];
+            a.counts[(int64_t)ch * a.E_tot + e] = run;
+            run += c;
+        }
+    }
+}
+
+__global__ __launch_bounds__(kAlignThreads) void k_align_scatter(const RouteArgs a)
+{
+    __shared__ AlignSmem sm;
+    const int64_t n = a.T * a.keff;
+    const int64_t lo = (int64_t)blockIdx.x * kChunkElems;
+    const int cn = (int)min((int64_t)kChunkElems, n - lo);
+    zero_counts(sm, a.E_tot);
+    for (int i = threadIdx.x; i < cn; i += kAlignThreads)
+        sm.ids[i] = a.topk_ids[lo + i];
+    __syncthreads();
+    chunk_hist(sm.ids, cn, a.E_tot, sm.cnt);
+    __syncthreads();
+    const int32_t *starts = a.counts + (int64_t)blockIdx.x * a.E_tot;
+    wave_cursors([&](int e) { return starts[e]; }, a.E_tot, sm.cnt);
+    __syncthreads();
+    chunk_scatter(sm.ids, cn, (int)lo, a.E_tot, sm.cnt, a.sorted_ids);
+}
+
+template <int NV>
+hipError_t launch_nv(const RouteArgs &a, hipStream_t s)
+{
+    const int64_t n = a.T * a.keff;
+    if (a.T <= kSmallTokens && n <= kChunkElems) {
+        k_route_align_small<NV><<<1, kAlignThreads, 0, s>>>(a);
+        return hipGetLastError();
+    }
+    k_route<NV><<<(unsigned)((a.T + 3) / 4), 256, 0, s>>>(a);
+    if (n <= kChunkElems) {
+        k_align_single<<<1, kAlignThreads, 0, s>>>(a);
+    } else {
+        const int nch = (int)((n + kChunkElems - 1) / kChunkElems);
+        k_align_hist<<<nch, kAlignThreads, 0, s>>>(a);
+        k_align_scan<<<1, kAlignThreads, 0, s>>>(a, nch);
+        k_align_scatter<<<nch, kAlignThreads, 0, s>>>(a);
+    }
+    return hipGetLastError();
+}
+
+} // namespace
+
+int64_t route_workspace_bytes(int64_t T, int keff, int E_tot)
+{
+    const int64_t n = T * keff;
+    if (n <= kChunkElems)
+        return 0;
+    const int64_t nch = (n + kChunkElems - 1) / kChunkElems;
+    return nch * E_tot * (int64_t)sizeof(int32_t);
+}
+
+hipError_t launch_route_align(const RouteArgs &a, hipStream_t s)
+{
+    if (a.T <= 0)
+        return hipSuccess;
+    if (a.E <= 64)
+        return launch_nv<1>(a, s);
+    if (a.E <= 128)
+        return launch_nv<2>(a, s);
+    if (a.E <= 256)
+        return launch_nv<4>(a, s);
+    if (a.E <= 512)
+        return launch_nv<8>(a, s);
+    return launch_nv<16>(a, s);
+}
+
+} // namespace pmoe

@@ -1,0 +1,591 @@
+// Host runtime of the paged fused-MoE C ABI: argument validation, the layer's
+// location table (page table), the double-buffer event protocol and the
+// workspace layout.  All compute is in the HIP kernels (route_align.hip,
+// moe_gemm.hip); this file only validates and enqueues.
+#include "moe.h"
+#include "internal.h"
+
+#include <array>
+#include <cstring>
+#include <string>
+#include <vector>
+
+using pmoe::DevLoc;
+
+struct moe_pool {
+    moe_pool_desc desc;
+    int E_tot = 0, keff = 0;
+    int device = 0;
+    DevLoc *d_locs = nullptr;           // device copy of the location table
+    moe_expert_loc *h_stage = nullptr;  // pinned staging of the last upload
+    hipEvent_t upload_done = nullptr;   // staging may be rewritten once this fired
+    bool upload_pending = false;
+    bool locs_set = false;
+    bool uses_loadbuf = false;          // the table names at least one load-buffer expert
+    hipEvent_t filled[2] = {nullptr, nullptr};   // last fill of buffer b done (read-after-write)
+    hipEvent_t consumed[2] = {nullptr, nullptr}; // last forward reading buffer b done (write-after-read)
+    bool ever_filled[2] = {false, false};
+    bool consumed_rec[2] = {false, false};
+    // stage timing (measurement only): one set of 4 events per recorded forward
+    bool timing = false;
+    std::vector<std::array<hipEvent_t, 4>> tev;
+    size_t tev_used = 0;
+};
+
+constexpr size_t kMaxTimedForwards = 1024;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const std::string &msg)
+{
+    g_err = msg;
+    return code;
+}
+
+int hip_fail(hipError_t e, const char *what)
+{
+    return fail(MOE_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+#define HIP_TRY(call)                                                                              \
+    do {                                                                                           \
+        hipError_t e_ = (call);                                                                    \
+        if (e_ != hipSuccess)                                                                      \
+            return hip_fail(e_, #call);                                                            \
+    } while (0)
+
+constexpr int64_t kMaxBuf = (int64_t)1 << 31; // every buffer read through a descriptor stays < 2 GiB
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool valid_block_m(int bm) { return bm == 16 || bm == 32 || bm == 64 || bm == 128 || bm == 256; }
+
+int check_desc(const moe_pool_desc *d)
+{
+    if (!d)
+        return fail(MOE_ERR_INVALID_ARG, "desc is null");
+    if (!d->pool_base)
+        return fail(MOE_ERR_INVALID_ARG, "pool_base is null");
+    if (!aligned(d->pool_base, 16))
+        return fail(MOE_ERR_ALIGN, "pool_base not 16-byte aligned");
+    if (d->num_pages < 1)
+        return fail(MOE_ERR_INVALID_ARG, "num_pages < 1");
+    if (d->d <= 0 || d->f <= 0)
+        return fail(MOE_ERR_INVALID_ARG, "d and f must be positive");
+    if (d->d % 64 || d->f % 64)
+        return fail(MOE_ERR_UNSUPPORTED, "d and f must be multiples of 64");
+    if ((int64_t)d->f * d->d * 2 >= kMaxBuf)
+        return fail(MOE_ERR_UNSUPPORTED, "one page (f*d bf16) must be < 2 GiB");
+    if (d->num_shared < 0 || d->num_shared > 1)
+        return fail(MOE_ERR_INVALID_ARG, "num_shared must be 0 or 1");
+    if (d->num_experts < 1 || d->num_experts + d->num_shared > pmoe::kMaxExpertsTotal)
+        return fail(MOE_ERR_UNSUPPORTED, "num_experts + num_shared must be in [1, 1024]");
+    if (d->top_k < 1 || d->top_k > d->num_experts || d->top_k > pmoe::kMaxTopK)
+        return fail(MOE_ERR_INVALID_ARG, "top_k must be in [1, min(num_experts, 32)]");
+    if (d->loadbuf_slots < 0)
+        return fail(MOE_ERR_INVALID_ARG, "loadbuf_slots < 0");
+    if (d->loadbuf_slots > 0) {
+        for (int b = 0; b < 2; b++) {
+            if (!d->loadbuf_base[b])
+                return fail(MOE_ERR_INVALID_ARG, "loadbuf_base is null while loadbuf_slots > 0");
+            if (!aligned(d->loadbuf_base[b], 16))
+                return fail(MOE_ERR_ALIGN, "loadbuf_base not 16-byte aligned");
+        }
+    }
+    return MOE_OK;
+}
+
+struct Sizes {
+    int64_t n, sorted_cap, blocks_cap;
+    size_t off_counts, off_h, off_comb, total;
+};
+
+size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+Sizes sizes_for(const moe_pool *p, int64_t T, int bm, uint32_t flags)
+{
+    Sizes s{};
+    s.n = T * p->keff;
+    s.sorted_cap = s.n + (int64_t)p->E_tot * (bm - 1);
+    s.blocks_cap = (s.sorted_cap + bm - 1) / bm;
+    const size_t counts = (size_t)pmoe::route_workspace_bytes(T, p->keff, p->E_tot);
+    const size_t h = (size_t)s.sorted_cap * p->desc.f * 2;
+    const size_t comb = (flags & MOE_FLAG_ATOMIC_COMBINE) ? (size_t)T * p->desc.d * 4
+                                                          : (size_t)s.n * p->desc.d * 4;
+    s.off_counts = 0;
+    s.off_h = up256(counts);
+    s.off_comb = s.off_h + up256(h);
+    s.total = s.off_comb + up256(comb);
+    return s;
+}
+
+// Shared checks of moe_route / the forwards: T range and buffer-size limits.
+int check_tokens(const moe_pool *p, int64_t T, int bm)
+{
+    if (T < 0)
+        return fail(MOE_ERR_INVALID_ARG, "T < 0");
+    if (!valid_block_m(bm))
+        return fail(MOE_ERR_INVALID_ARG, "block_m must be 16, 32, 64, 128 or 256");
+    const int64_t n = T * p->keff;
+    if (n + (int64_t)p->E_tot * bm >= ((int64_t)1 << 31))
+        return fail(MOE_ERR_UNSUPPORTED, "T*(k+S) too large for int32 indices");
+    if (T * p->desc.d * 2 >= kMaxBuf)
+        return fail(MOE_ERR_UNSUPPORTED, "x (T*d bf16) must be < 2 GiB");
+    const int64_t sorted_cap = n + (int64_t)p->E_tot * (bm - 1);
+    if (sorted_cap * p->desc.f * 2 >= kMaxBuf)
+        return fail(MOE_ERR_UNSUPPORTED, "activation buffer (sorted_cap*f bf16) must be < 2 GiB");
+    return MOE_OK;
+}
+
+int check_dev(const void *ptr, size_t align, const char *name)
+{
+    if (!ptr)
+        return fail(MOE_ERR_INVALID_ARG, std::string(name) + " is null");
+    if (!aligned(ptr, align))
+        return fail(MOE_ERR_ALIGN, std::string(name) + " misaligned");
+    return MOE_OK;
+}
+
+#define CHECK(expr)                                                                                \
+    do {                                                                                           \
+        int rc_ = (expr);                                                                          \
+        if (rc_ != MOE_OK)                                                                         \
+            return rc_;                                                                            \
+    } while (0)
+
+int forward_common(const moe_pool *p, const void *w13, const void *w2, bool paged, const void *x,
+                   int64_t T, int32_t bm, const int32_t *ids, const float *w, const int32_t *sorted,
+                   const int32_t *blk, const int32_t *npad, int32_t active_buf, void *y, void *ws,
+                   size_t ws_bytes, uint32_t flags, hipStream_t s, hipEvent_t *ev)
+{
+    if (flags & ~MOE_FLAG_ATOMIC_COMBINE)
+        return fail(MOE_ERR_INVALID_ARG, "unknown flag bits");
+    CHECK(check_tokens(p, T, bm));
+    if (T == 0)
+        return MOE_OK;
+    CHECK(check_dev(x, 16, "x"));
+    CHECK(check_dev(y, 16, "y"));
+    CHECK(check_dev(ids, 4, "topk_ids"));
+    CHECK(check_dev(w, 4, "topk_w"));
+    CHECK(check_dev(sorted, 4, "sorted_ids"));
+    CHECK(check_dev(blk, 4, "block_expert"));
+    CHECK(check_dev(npad, 4, "num_padded"));
+    CHECK(check_dev(ws, 256, "workspace"));
+    const Sizes sz = sizes_for(p, T, bm, flags);
+    if (ws_bytes < sz.total)
+        return fail(MOE_ERR_WORKSPACE, "workspace too small: need " + std::to_string(sz.total) + " bytes");
+    pmoe::FwdArgs a{};
+    if (paged) {
+        a.locs = p->d_locs;
+        a.pool = (const uint16_t *)p->desc.pool_base;
+        a.loadbuf = p->desc.loadbuf_slots > 0 ? (const uint16_t *)p->desc.loadbuf_base[active_buf] : nullptr;
+    } else {
+        a.w13 = (const uint16_t *)w13;
+        a.w2 = (const uint16_t *)w2;
+    }
+    a.x = (const uint16_t *)x;
+    a.T = T;
+    a.d = p->desc.d;
+    a.f = p->desc.f;
+    a.keff = p->keff;
+    a.E_tot = p->E_tot;
+    a.BM = bm;
+    a.topk_ids = ids;
+    a.topk_w = w;
+    a.sorted_ids = sorted;
+    a.block_expert = blk;
+    a.num_padded = npad;
+    a.sorted_cap = sz.sorted_cap;
+    a.blocks_cap = sz.blocks_cap;
+    a.y = (uint16_t *)y;
+    a.h = (uint16_t *)((char *)ws + sz.off_h);
+    a.comb = (float *)((char *)ws + sz.off_comb);
+    a.atomic = (flags & MOE_FLAG_ATOMIC_COMBINE) != 0;
+    if (ev)
+        for (int i = 0; i < 4; i++)
+            a.ev[i] = ev[i];
+    HIP_TRY(pmoe::launch_forward(a, s));
+    return MOE_OK;
+}
+
+// Events for the next timed forward of p, or nullptr when timing is off or full.
+hipEvent_t *next_timing_events(moe_pool *p)
+{
+    if (!p->timing || p->tev_used >= kMaxTimedForwards)
+        return nullptr;
+    if (p->tev_used == p->tev.size()) {
+        std::array<hipEvent_t, 4> ev{};
+        for (auto &e : ev)
+            if (hipEventCreate(&e) != hipSuccess)
+                return nullptr;
+        p->tev.push_back(ev);
+    }
+    return p->tev[p->tev_used++].data();
+}
+
+} // namespace
+
+extern "C" {
+
+const char *moe_last_error(void) { return g_err.c_str(); }
+
+int moe_version(void) { return 100; }
+
+int moe_validate_locs(const moe_pool_desc *desc, const moe_expert_loc *locs, int32_t n)
+{
+    CHECK(check_desc(desc));
+    const int E_tot = desc->num_experts + desc->num_shared;
+    if (!locs)
+        return fail(MOE_ERR_INVALID_ARG, "locs is null");
+    if (n != E_tot)
+        return fail(MOE_ERR_INVALID_ARG, "locs must have num_experts + num_shared entries");
+    std::vector<int32_t> page_owner(desc->num_pages, -1);
+    std::vector<int32_t> slot_owner(desc->loadbuf_slots > 0 ? desc->loadbuf_slots : 0, -1);
+    for (int e = 0; e < n; e++) {
+        const moe_expert_loc &L = locs[e];
+        if (L.kind == MOE_LOC_POOL) {
+            for (int m = 0; m < 3; m++) {
+                const int64_t pg = L.idx[m];
+                if (pg < 0 || pg >= desc->num_pages)
+                    return fail(MOE_ERR_PAGE_RANGE, "expert " + std::to_string(e) + ": page " +
+                                                        std::to_string(pg) + " out of range");
+                if (page_owner[pg] >= 0)
+                    return fail(MOE_ERR_PAGE_ALIAS, "page " + std::to_string(pg) + " used twice (experts " +
+                                                        std::to_string(page_owner[pg]) + ", " +
+                                                        std::to_string(e) + ")");
+                page_owner[pg] = e;
+            }
+        } else if (L.kind == MOE_LOC_LOADBUF) {
+            const int s = L.idx[0];
+            if (s < 0 || s >= desc->loadbuf_slots)
+                return fail(MOE_ERR_SLOT_RANGE, "expert " + std::to_string(e) + ": slot " +
+                                                    std::to_string(s) + " out of range");
+            if (slot_owner[s] >= 0)
+                return fail(MOE_ERR_SLOT_RANGE, "slot " + std::to_string(s) + " given to two experts");
+            slot_owner[s] = e;
+        } else {
+            return fail(MOE_ERR_INVALID_ARG, "expert " + std::to_string(e) + ": unknown kind");
+        }
+    }
+    return MOE_OK;
+}
+
+int moe_pool_create(const moe_pool_desc *desc, moe_pool **out)
+{
+    if (!out)
+        return fail(MOE_ERR_INVALID_ARG, "out is null");
+    *out = nullptr;
+    CHECK(check_desc(desc));
+    moe_pool *p = new moe_pool();
+    p->desc = *desc;
+    p->E_tot = desc->num_experts + desc->num_shared;
+    p->keff = desc->top_k + desc->num_shared;
+    auto cleanup = [&](int rc) {
+        moe_pool_destroy(p);
+        return rc;
+    };
+    hipError_t e;
+    if ((e = hipGetDevice(&p->device)) != hipSuccess)
+        return cleanup(hip_fail(e, "hipGetDevice"));
+    if ((e = hipMalloc((void **)&p->d_locs, sizeof(DevLoc) * p->E_tot)) != hipSuccess)
+        return cleanup(hip_fail(e, "hipMalloc(location table)"));
+    if ((e = hipHostMalloc((void **)&p->h_stage, sizeof(moe_expert_loc) * p->E_tot, hipHostMallocDefault)) !=
+        hipSuccess)
+        return cleanup(hip_fail(e, "hipHostMalloc(staging)"));
+    if ((e = hipEventCreateWithFlags(&p->upload_done, hipEventDisableTiming)) != hipSuccess)
+        return cleanup(hip_fail(e, "hipEventCreate"));
+    for (int b = 0; b < 2; b++) {
+        if ((e = hipEventCreateWithFlags(&p->filled[b], hipEventDisableTiming)) != hipSuccess)
+            return cleanup(hip_fail(e, "hipEventCreate"));
+        if ((e = hipEventCreateWithFlags(&p->consumed[b], hipEventDisableTiming)) != hipSuccess)
+            return cleanup(hip_fail(e, "hipEventCreate"));
+    }
+    *out = p;
+    return MOE_OK;
+}
+
+int moe_pool_destroy(moe_pool *p)
+{
+    if (!p)
+        return MOE_OK;
+    if (p->upload_pending && p->upload_done)
+        (void)hipEventSynchronize(p->upload_done);
+    for (int b = 0; b < 2; b++) {
+        if (p->filled[b]) {
+            if (p->ever_filled[b])
+                (void)hipEventSynchronize(p->filled[b]);
+            (void)hipEventDestroy(p->filled[b]);
+        }
+        if (p->consumed[b]) {
+            if (p->consumed_rec[b])
+                (void)hipEventSynchronize(p->consumed[b]);
+            (void)hipEventDestroy(p->consumed[b]);
+        }
+    }
+    if (p->upload_done)
+        (void)hipEventDestroy(p->upload_done);
+    for (auto &ev : p->tev)
+        for (auto e : ev)
+            if (e)
+                (void)hipEventDestroy(e);
+    if (p->d_locs)
+        (void)hipFree(p->d_locs);
+    if (p->h_stage)
+        (void)hipHostFree(p->h_stage);
+    delete p;
+    return MOE_OK;
+}
+
+int moe_set_expert_locs(moe_pool *p, const moe_expert_loc *locs, int32_t n, void *stream)
+{
+    if (!p)
+        return fail(MOE_ERR_INVALID_ARG, "pool is null");
+    CHECK(moe_validate_locs(&p->desc, locs, n));
+    if (p->upload_pending)
+        HIP_TRY(hipEventSynchronize(p->upload_done));
+    std::memcpy(p->h_stage, locs, sizeof(moe_expert_loc) * n);
+    hipStream_t s = (hipStream_t)stream;
+    HIP_TRY(hipMemcpyAsync(p->d_locs, p->h_stage, sizeof(moe_expert_loc) * n, hipMemcpyHostToDevice, s));
+    HIP_TRY(hipEventRecord(p->upload_done, s));
+    p->upload_pending = true;
+    p->locs_set = true;
+    p->uses_loadbuf = false;
+    for (int e = 0; e < n; e++)
+        p->uses_loadbuf |= locs[e].kind == MOE_LOC_LOADBUF;
+    return MOE_OK;
+}
+
+int moe_route_capacity(const moe_pool *p, int64_t T, int32_t block_m, int64_t *sorted_cap, int64_t *blocks_cap)
+{
+    if (!p || !sorted_cap || !blocks_cap)
+        return fail(MOE_ERR_INVALID_ARG, "null argument");
+    CHECK(check_tokens(p, T, block_m));
+    const Sizes s = sizes_for(p, T, block_m, 0);
+    *sorted_cap = s.sorted_cap;
+    *blocks_cap = s.blocks_cap;
+    return MOE_OK;
+}
+
+int moe_workspace_bytes(const moe_pool *p, int64_t T, int32_t block_m, uint32_t flags, size_t *bytes)
+{
+    if (!p || !bytes)
+        return fail(MOE_ERR_INVALID_ARG, "null argument");
+    if (flags & ~MOE_FLAG_ATOMIC_COMBINE)
+        return fail(MOE_ERR_INVALID_ARG, "unknown flag bits");
+    CHECK(check_tokens(p, T, block_m));
+    *bytes = sizes_for(p, T, block_m, flags).total;
+    return MOE_OK;
+}
+
+int moe_route(moe_pool *p, const float *logits, int64_t T, int32_t block_m, int32_t *topk_ids, float *topk_w,
+              int32_t *sorted_ids, int32_t *block_expert, int32_t *num_padded, void *ws, size_t ws_bytes,
+              void *stream)
+{
+    if (!p)
+        return fail(MOE_ERR_INVALID_ARG, "pool is null");
+    CHECK(check_tokens(p, T, block_m));
+    if (T == 0)
+        return MOE_OK;
+    CHECK(check_dev(logits, 4, "logits"));
+    CHECK(check_dev(topk_ids, 4, "topk_ids"));
+    CHECK(check_dev(topk_w, 4, "topk_w"));
+    CHECK(check_dev(sorted_ids, 4, "sorted_ids"));
+    CHECK(check_dev(block_expert, 4, "block_expert"));
+    CHECK(check_dev(num_padded, 4, "num_padded"));
+    const Sizes sz = sizes_for(p, T, block_m, 0);
+    if (sz.off_h > 0) {
+        CHECK(check_dev(ws, 256, "workspace"));
+        if (ws_bytes < sz.off_h)
+            return fail(MOE_ERR_WORKSPACE, "workspace too small for routing");
+    }
+    pmoe::RouteArgs a{};
+    a.logits = logits;
+    a.T = T;
+    a.E = p->desc.num_experts;
+    a.k = p->desc.top_k;
+    a.S = p->desc.num_shared;
+    a.keff = p->keff;
+    a.E_tot = p->E_tot;
+    a.BM = block_m;
+    a.topk_ids = topk_ids;
+    a.topk_w = topk_w;
+    a.sorted_ids = sorted_ids;
+    a.block_expert = block_expert;
+    a.num_padded = num_padded;
+    a.sorted_cap = sz.sorted_cap;
+    a.blocks_cap = sz.blocks_cap;
+    a.counts = (int32_t *)((char *)ws + sz.off_counts);
+    HIP_TRY(pmoe::launch_route_align(a, (hipStream_t)stream));
+    return MOE_OK;
+}
+
+int moe_paged_forward(moe_pool *p, const void *x, int64_t T, int32_t block_m, const int32_t *topk_ids,
+                      const float *topk_w, const int32_t *sorted_ids, const int32_t *block_expert,
+                      const int32_t *num_padded, int32_t active_buf, void *y, void *ws, size_t ws_bytes,
+                      uint32_t flags, void *stream)
+{
+    if (!p)
+        return fail(MOE_ERR_INVALID_ARG, "pool is null");
+    if (active_buf < 0 || active_buf > 1)
+        return fail(MOE_ERR_INVALID_ARG, "active_buf must be 0 or 1");
+    if (!p->locs_set)
+        return fail(MOE_ERR_STATE, "no location table: call moe_set_expert_locs first");
+    if (p->uses_loadbuf && !p->ever_filled[active_buf])
+        return fail(MOE_ERR_STATE, "load buffer " + std::to_string(active_buf) +
+                                       " was never filled but the table reads from it");
+    hipStream_t s = (hipStream_t)stream;
+    if (T > 0 && p->uses_loadbuf)
+        HIP_TRY(hipStreamWaitEvent(s, p->filled[active_buf], 0));
+    CHECK(forward_common(p, nullptr, nullptr, true, x, T, block_m, topk_ids, topk_w, sorted_ids, block_expert,
+                         num_padded, active_buf, y, ws, ws_bytes, flags, s, T > 0 ? next_timing_events(p) : nullptr));
+    if (T > 0 && p->uses_loadbuf) {
+        HIP_TRY(hipEventRecord(p->consumed[active_buf], s));
+        p->consumed_rec[active_buf] = true;
+    }
+    return MOE_OK;
+}
+
+int moe_contiguous_forward(const moe_pool *p, const void *w13, const void *w2, const void *x, int64_t T,
+                           int32_t block_m, const int32_t *topk_ids, const float *topk_w,
+                           const int32_t *sorted_ids, const int32_t *block_expert, const int32_t *num_padded,
+                           void *y, void *ws, size_t ws_bytes, uint32_t flags, void *stream)
+{
+    if (!p)
+        return fail(MOE_ERR_INVALID_ARG, "pool is null");
+    CHECK(check_dev(w13, 16, "w13"));
+    CHECK(check_dev(w2, 16, "w2"));
+    return forward_common(p, w13, w2, false, x, T, block_m, topk_ids, topk_w, sorted_ids, block_expert,
+                          num_padded, 0, y, ws, ws_bytes, flags, (hipStream_t)stream, nullptr);
+}
+
+int moe_loadbuf_fill(moe_pool *p, int32_t buf, int32_t n, const int32_t *slots, const void *const *host_src,
+                     void *copy_stream)
+{
+    if (!p)
+        return fail(MOE_ERR_INVALID_ARG, "pool is null");
+    if (buf < 0 || buf > 1)
+        return fail(MOE_ERR_INVALID_ARG, "buf must be 0 or 1");
+    if (p->desc.loadbuf_slots <= 0)
+        return fail(MOE_ERR_STATE, "this layer has no load buffers");
+    if (n < 0 || n > p->desc.loadbuf_slots)
+        return fail(MOE_ERR_INVALID_ARG, "n out of range");
+    if (n > 0 && (!slots || !host_src))
+        return fail(MOE_ERR_INVALID_ARG, "slots / host_src is null");
+    std::vector<char> seen(p->desc.loadbuf_slots, 0);
+    for (int i = 0; i < n; i++) {
+        if (slots[i] < 0 || slots[i] >= p->desc.loadbuf_slots)
+            return fail(MOE_ERR_SLOT_RANGE, "slot " + std::to_string(slots[i]) + " out of range");
+        if (seen[slots[i]])
+            return fail(MOE_ERR_SLOT_RANGE, "slot " + std::to_string(slots[i]) + " listed twice");
+        seen[slots[i]] = 1;
+        if (!host_src[i])
+            return fail(MOE_ERR_INVALID_ARG, "host_src entry is null");
+        hipPointerAttribute_t attr;
+        hipError_t e = hipPointerGetAttributes(&attr, host_src[i]);
+        if (e != hipSuccess || attr.type != hipMemoryTypeHost) {
+            (void)hipGetLastError();
+            return fail(MOE_ERR_INVALID_ARG, "host_src must be pinned host memory");
+        }
+    }
+    hipStream_t s = (hipStream_t)copy_stream;
+    if (p->consumed_rec[buf])
+        HIP_TRY(hipStreamWaitEvent(s, p->consumed[buf], 0));
+    if (p->ever_filled[buf])
+        HIP_TRY(hipStreamWaitEvent(s, p->filled[buf], 0));
+    const size_t bytes = (size_t)3 * p->desc.f * p->desc.d * 2;
+    char *dst0 = (char *)p->desc.loadbuf_base[buf];
+    for (int i = 0; i < n; i++)
+        HIP_TRY(hipMemcpyAsync(dst0 + (size_t)slots[i] * bytes, host_src[i], bytes, hipMemcpyHostToDevice, s));
+    HIP_TRY(hipEventRecord(p->filled[buf], s));
+    p->ever_filled[buf] = true;
+    return MOE_OK;
+}
+
+int moe_resolve_addrs(moe_pool *p, int32_t active_buf, int64_t n, const int32_t *e, const int32_t *which,
+                      const int64_t *row, const int64_t *col, int64_t *off, int32_t *base, void *stream)
+{
+    if (!p)
+        return fail(MOE_ERR_INVALID_ARG, "pool is null");
+    if (active_buf < 0 || active_buf > 1)
+        return fail(MOE_ERR_INVALID_ARG, "active_buf must be 0 or 1");
+    if (!p->locs_set)
+        return fail(MOE_ERR_STATE, "no location table: call moe_set_expert_locs first");
+    if (n < 0)
+        return fail(MOE_ERR_INVALID_ARG, "n < 0");
+    if (n == 0)
+        return MOE_OK;
+    CHECK(check_dev(e, 4, "e"));
+    CHECK(check_dev(which, 4, "which"));
+    CHECK(check_dev(row, 8, "row"));
+    CHECK(check_dev(col, 8, "col"));
+    CHECK(check_dev(off, 8, "off"));
+    CHECK(check_dev(base, 4, "base"));
+    pmoe::ResolveArgs r{};
+    r.locs = p->d_locs;
+    r.pool = (const uint16_t *)p->desc.pool_base;
+    r.loadbuf0 = (const uint16_t *)p->desc.loadbuf_base[0];
+    r.loadbuf1 = (const uint16_t *)p->desc.loadbuf_base[1];
+    r.active_buf = active_buf;
+    r.d = p->desc.d;
+    r.f = p->desc.f;
+    r.E_tot = p->E_tot;
+    r.n = n;
+    r.e = e;
+    r.which = which;
+    r.row = row;
+    r.col = col;
+    r.off = off;
+    r.base = base;
+    HIP_TRY(pmoe::launch_resolve(r, (hipStream_t)stream));
+    return MOE_OK;
+}
+
+int moe_stage_timing(moe_pool *p, int32_t enable)
+{
+    if (!p)
+        return fail(MOE_ERR_INVALID_ARG, "pool is null");
+    p->timing = enable != 0;
+    p->tev_used = 0;
+    return MOE_OK;
+}
+
+int moe_stage_times(moe_pool *p, float *ms, int32_t *count)
+{
+    if (!p || !ms || !count)
+        return fail(MOE_ERR_INVALID_ARG, "null argument");
+    ms[0] = ms[1] = ms[2] = 0.f;
+    for (size_t i = 0; i < p->tev_used; i++) {
+        auto &ev = p->tev[i];
+        HIP_TRY(hipEventSynchronize(ev[3]));
+        for (int k = 0; k < 3; k++) {
+            float t = 0.f;
+            HIP_TRY(hipEventElapsedTime(&t, ev[k], ev[k + 1]));
+            ms[k] += t;
+        }
+    }
+    *count = (int32_t)p->tev_used;
+    p->tev_used = 0;
+    return MOE_OK;
+}
+
+int32_t moe_suggest_block_m(const moe_pool *p, int64_t T)
+{
+    if (!p || T <= 0)
+        return 16;
+    // expected rows per active expert; a block should cover an expert's rows
+    // in as few tiles as possible without mostly padding
+    const int64_t n = T * p->keff;
+    const int64_t active = n < p->E_tot ? n : p->E_tot;
+    const int64_t per = n / active;
+    if (per <= 16)
+        return 16;
+    if (per <= 32)
+        return 32;
+    if (per <= 96)
+        return 64;
+    return 128;
+}
+
+} // extern "C"
