@@ -1,0 +1,304 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged fused-MoE layer on one MI355X.
+
+One step = one pass of the layer over one batch of resident inputs: top-k
+routing + alignment (moe_route), the gate/up GEMM with SiLU*mul, the down GEMM
+with the weighted combine (moe_paged_forward), reading every expert in place
+from pool pages or from the active load buffer.  The load-buffer fill of the
+next layer (pinned host -> device over PCIe on a side stream) is measured in
+the same run and reported under "loadbuf": its bound is the host link, not HBM.
+
+Consecutive steps rotate over R copies of the layer's pool and load buffers
+(R large enough that R working sets exceed the 256 MB Infinity Cache), as the
+layers of a model would, so each step streams its weights from HBM.
+
+Prints ONE JSON line.  Default workload: the Qwen1.5-MoE-shaped layer
+(T=1024, d=2048, f=1408, E=60, top-4; 48 experts in a 256-page pool, 12 in the
+load buffer).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "paged fused-MoE TFLOP/s & HBM GB/s (%roofline) + overhead vs contiguous"
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+MALL_BYTES = 256 << 20
+
+WORKLOAD_TEXT = {
+    "tiny": "tiny MoE layer T=16 d=128 f=64 E=8 top-2; 6 experts paged in a 32-page pool, 2 via load buffer",
+    "qwen15": "Qwen1.5-MoE-14B-shaped MoE layer T=1024 d=2048 f=1408 E=60 top-4; 48 experts paged in a "
+              "256-page pool (random order), 12 via double-buffered load buffer",
+    "decode": "Qwen1.5-MoE-shaped decode layer d=2048 f=1408 E=60 top-4; 30 experts paged, 30 via load buffer",
+    "mixtral": "Mixtral-8x7B-shaped MoE layer T=4096 d=4096 f=14336 E=8 top-2, Zipf(1.2) routing; all experts "
+               "paged in a 32-page pool with 8 pages carved into KV pages",
+    "qwen3n": "Qwen3-Next-80B-A3B-shaped MoE layer T=8192 d=2048 f=512 E=512 top-10 + 1 shared expert, "
+              "Zipf(1.1) routing; pool of 2 MiB pages interleaved with 16-token KV pages; 64 experts via load buffer",
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="qwen15", choices=sorted(WORKLOAD_TEXT))
+    ap.add_argument("--T", type=int, default=None, help="tokens (default: the workload's own; decode: 1)")
+    ap.add_argument("--block-m", type=int, default=0, help="GEMM tile height (default: moe_suggest_block_m)")
+    ap.add_argument("--atomic", action="store_true", help="fp32-atomic combine instead of the ordered one")
+    ap.add_argument("--rotate", type=int, default=0, help="layer copies to rotate over (default: automatic)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-contig", action="store_true")
+    ap.add_argument("--no-fill", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target seconds of oracle work")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the layer's hot path runs on a single MI355X and this build "
+              "has no multi-GPU path (see DESIGN.md for how it would shard). Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import paged_expert_weight_amd as pm
+    from workloads import device as wdev
+    from workloads import synth
+
+    pm.lib()  # fails loudly without the HIP library
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+
+    name = args.workload
+    s = synth.SPECS[name]
+    T = args.T if args.T is not None else (1 if name == "decode" else s.T)
+    t0 = time.time()
+    layer = synth.make_layer(s, T)
+    dev = wdev.to_device(layer)
+    print(f"# layer {name} T={T} generated and placed in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+
+    fd = s.f * s.d
+    # working set of one step (weights of touched experts are at most all experts)
+    ws_bytes_est = min(s.E_tot, T * s.k_eff) * 3 * fd * 2
+    R = args.rotate or max(2, min(16, math.ceil(1.0 * MALL_BYTES / max(1, ws_bytes_est)) + 1))
+
+    slots = sorted(dev.host_blobs)
+    copies = []
+    for r in range(R):
+        pool = dev.pool if r == 0 else dev.pool.clone()
+        lbs = tuple(dev.loadbuf) if r == 0 else tuple(b.clone() for b in dev.loadbuf)
+        h = pm.moe_pool_create(pool, s.pool_pages, s.d, s.f, s.E, s.k, s.S, s.loadbuf_slots, lbs)
+        pm.moe_set_expert_locs(h, layer.placement.locs)
+        if s.loadbuf_slots:
+            pm.moe_loadbuf_fill(h, 0, slots, [dev.host_blobs[k] for k in slots])
+        w13 = dev.w13 if r == 0 else dev.w13.clone()
+        w2 = dev.w2 if r == 0 else dev.w2.clone()
+        copies.append(dict(h=h, pool=pool, lbs=lbs, w13=w13, w2=w2))
+    torch.cuda.synchronize()
+
+    h0 = copies[0]["h"]
+    bm = args.block_m or pm.moe_suggest_block_m(h0, T)
+    flags = pm.MOE_FLAG_ATOMIC_COMBINE if args.atomic else 0
+    ws = pm.workspace(h0, T, bm, flags)
+    rt = pm.RouteOut(h0, T, bm)
+    y = torch.empty_like(dev.x)
+    stream = torch.cuda.current_stream()
+
+    def step(i, contiguous=False):
+        c = copies[i % R]
+        pm.moe_route(c["h"], dev.logits, bm, rt.topk_ids, rt.topk_w, rt.sorted_ids, rt.block_expert,
+                     rt.num_padded, ws, stream)
+        if contiguous:
+            pm.moe_contiguous_forward(c["h"], c["w13"], c["w2"], dev.x, bm, rt.topk_ids, rt.topk_w, rt.sorted_ids,
+                                      rt.block_expert, rt.num_padded, y, ws, flags, stream)
+        else:
+            pm.moe_paged_forward(c["h"], dev.x, bm, rt.topk_ids, rt.topk_w, rt.sorted_ids, rt.block_expert,
+                                 rt.num_padded, 0, y, ws, flags, stream)
+
+    def timed(K, W, contiguous=False):
+        for i in range(W):
+            step(i, contiguous)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(K):
+            step(i, contiguous)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / K
+
+    # ---- the timed region (paged)
+    ms = timed(args.steps, args.warmup)
+    print(f"# paged: {ms * 1e3:.1f} us/step", file=sys.stderr, flush=True)
+
+    ids = rt.topk_ids.cpu().numpy()
+    n = T * s.k_eff
+    touched = int(np.unique(ids).size)
+    flops = 6.0 * s.d * s.f * n
+    bytes_alg = touched * 3 * fd * 2 + T * s.d * 2 + 2 * n * s.f * 2 + T * s.d * 2
+    tflops = flops / (ms * 1e-3) / 1e12
+    gbs = bytes_alg / (ms * 1e-3) / 1e9
+
+    # ---- contiguous twin (same kernels, dense weight arrays), same inputs and routing
+    contig_ms = None
+    if not args.no_contig:
+        contig_ms = timed(args.steps, args.warmup, contiguous=True)
+        print(f"# contiguous: {contig_ms * 1e3:.1f} us/step", file=sys.stderr, flush=True)
+
+    # ---- per-stage times from HIP events on the launch stream
+    for c in copies:
+        pm.moe_stage_timing(c["h"], True)
+    ra0, ra1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    route_ms = 0.0
+    for i in range(args.steps):
+        c = copies[i % R]
+        ra0.record(stream)
+        pm.moe_route(c["h"], dev.logits, bm, rt.topk_ids, rt.topk_w, rt.sorted_ids, rt.block_expert,
+                     rt.num_padded, ws, stream)
+        ra1.record(stream)
+        pm.moe_paged_forward(c["h"], dev.x, bm, rt.topk_ids, rt.topk_w, rt.sorted_ids, rt.block_expert,
+                             rt.num_padded, 0, y, ws, flags, stream)
+        ra1.synchronize()
+        route_ms += ra0.elapsed_time(ra1)
+    torch.cuda.synchronize()
+    stage = [0.0, 0.0, 0.0]
+    cnt = 0
+    for c in copies:
+        msv, k = pm.moe_stage_times(c["h"])
+        pm.moe_stage_timing(c["h"], False)
+        stage = [a + b for a, b in zip(stage, msv)]
+        cnt += k
+    stage_us = [v / max(1, cnt) * 1e3 for v in stage]
+    route_us = route_ms / args.steps * 1e3
+
+    g1_flops = 4.0 * n * s.f * s.d
+    g1_bytes = touched * 2 * fd * 2 + T * s.d * 2 + n * s.f * 2
+    g1_ai = g1_flops / g1_bytes
+    ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    g1_s = stage_us[0] * 1e-6
+    if g1_ai < ridge:
+        roof = {"bound": "hbm", "achieved": round(g1_bytes / g1_s / 1e9, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": round(g1_flops / g1_s / 1e12, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["traffic"] = None
+    roof["kernel"] = "k_gemm1 (paged gate/up GEMM + SiLU*mul)"
+    roof["avg_launch_us"] = round(stage_us[0], 2)
+    roof["algorithmic_bytes_per_launch"] = int(g1_bytes)
+    roof["algorithmic_flops_per_launch"] = int(g1_flops)
+
+    # ---- load-buffer fill (host link) and its effect on compute
+    loadbuf = None
+    if s.loadbuf_slots and not args.no_fill:
+        copy = torch.cuda.Stream()
+        hc = copies[0]["h"]
+        blobs = [dev.host_blobs[k] for k in slots]
+        nbytes = len(slots) * 3 * fd * 2
+        f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 5
+        pm.moe_loadbuf_fill(hc, 1, slots, blobs, copy)
+        copy.synchronize()
+        f0.record(copy)
+        for _ in range(reps):
+            pm.moe_loadbuf_fill(hc, 1, slots, blobs, copy)
+        f1.record(copy)
+        copy.synchronize()
+        fill_ms = f0.elapsed_time(f1) / reps
+        # compute on buffer 0 while buffer 1 keeps filling
+        for _ in range(max(1, int(args.steps * ms / fill_ms) + 1)):
+            pm.moe_loadbuf_fill(hc, 1, slots, blobs, copy)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(args.steps):
+            step(0)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        busy_ms = e0.elapsed_time(e1) / args.steps
+        loadbuf = {"experts_per_fill": len(slots), "bytes_per_fill": nbytes, "fill_ms": round(fill_ms, 3),
+                   "h2d_gbs": round(nbytes / (fill_ms * 1e-3) / 1e9, 2),
+                   "step_us_with_concurrent_fill": round(busy_ms * 1e3, 2),
+                   "step_slowdown_pct": round((busy_ms / ms - 1) * 100, 2),
+                   "fill_hidden_behind_one_step": fill_ms <= ms}
+
+    line = {
+        "metric": METRIC,
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD_TEXT[name], "name": name, "T": T, "block_m": bm,
+                   "combine": "atomic" if args.atomic else "ordered", "layer_copies_rotated": R},
+        "hbm_gbs": round(gbs, 1),
+        "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "mfma_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+        "algorithmic": {"flops": int(flops), "bytes": int(bytes_alg), "experts_touched": touched},
+        "contig_ms_per_step": round(contig_ms, 5) if contig_ms else None,
+        "overhead_vs_contiguous_pct": round((ms / contig_ms - 1) * 100, 3) if contig_ms else None,
+        "stages_us": {"route_align": round(route_us, 2), "gate_up": round(stage_us[0], 2),
+                      "down": round(stage_us[1], 2), "combine": round(stage_us[2], 2)},
+        "roofline": roof,
+        "loadbuf": loadbuf,
+    }
+
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(layer, args.cpu_seconds)
+
+    print(json.dumps(line), flush=True)
+    for c in copies:
+        c["h"].close()
+
+
+def cpu_baseline(layer, seconds: float):
+    """The oracle, as it stands, on a bounded sample of the same workload."""
+    import numpy as np
+    import oracle
+
+    s = layer.spec
+    T = layer.T
+    per_tok = 6.0 * s.d * s.f * s.k_eff
+    t = time.time()
+    ids, w = oracle.route(layer.logits, s.k, s.S)
+    oracle.align(ids, s.E_tot, 64)
+    route_s = time.time() - t
+    # probe the rate on a few tokens, then size the sample to ~`seconds`
+    probe = list(range(min(T, 8)))
+    t = time.time()
+    oracle.moe(layer.x, layer.w13, layer.w2, ids, w, tokens=probe)
+    rate = len(probe) * per_tok / max(1e-6, time.time() - t)
+    ntok = int(max(1, min(T, seconds * rate / per_tok)))
+    toks = np.linspace(0, T - 1, ntok).astype(np.int64)
+    done, flops, t = 0, 0.0, time.time()
+    while True:
+        oracle.moe(layer.x, layer.w13, layer.w2, ids, w, tokens=toks)
+        done += 1
+        flops += ntok * per_tok
+        if time.time() - t >= seconds * 0.8 or done >= 50:
+            break
+    el = time.time() - t + route_s
+    return {"value": round(flops / el / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.threads(), "kind": "oracle",
+            "sample": f"routing + alignment of all {T} tokens, then the per-token expert sum for {ntok} of "
+                      f"the {T} tokens (evenly spaced) x{done}; {el:.1f} s of CPU work in fp64"}
+
+
+if __name__ == "__main__":
+    main()
