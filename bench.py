@@ -59,11 +59,28 @@ def parse():
     ap.add_argument("--no-contig", action="store_true")
     ap.add_argument("--no-fill", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target seconds of oracle work")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB fp32 read + 1 GiB write elementwise kernel (scales HBM counters)")
     return ap.parse_args()
+
+
+def copy_calibration():
+    """A plain elementwise kernel of known traffic: reads 1 GiB, writes 1 GiB."""
+    import torch
+    src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": {"read_bytes": src.numel() * 4, "write_bytes": dst.numel() * 4,
+                                           "launches": 3}}))
 
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the layer's hot path runs on a single MI355X and this build "
               "has no multi-GPU path (see DESIGN.md for how it would shard). Use --gpus 1.", file=sys.stderr)

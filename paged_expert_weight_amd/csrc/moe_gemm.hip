@@ -21,10 +21,11 @@
 //   combine:  y[t] = bf16( sum_j comb[t*(k+S)+j] ), j ascending.
 //
 // Operands are K-contiguous on both sides (x rows and weight rows run along d;
-// h rows and W2 rows run along f), so each stage moves 128-byte row segments
-// from HBM to LDS with 16-byte loads and feeds v_mfma_f32_16x16x32_bf16 from
-// LDS with one 16-byte read per lane.  Two LDS stages: the global loads of
-// stage k+1 are in flight while stage k is multiplied.
+// h rows and W2 rows run along f).  Each K-step of 32 moves 64-byte row
+// segments from HBM straight into LDS (buffer_load_dwordx4 ... lds, no VGPR
+// round trip), into one of S LDS stages, so S-1 K-steps are in flight while one
+// is multiplied; v_mfma_f32_16x16x32_bf16 reads its operands from LDS with one
+// 16-byte read per lane, XOR-swizzled so 8 rows never share a bank group.
 #include "internal.h"
 
 namespace pmoe {
@@ -34,8 +35,6 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int BK = 64;         // K elements per stage
-constexpr int BKP = BK + 8;    // LDS row pitch in elements (144 bytes)
 constexpr uint32_t kOOB = 0x80000000u; // byte offset past every buffer (all are < 2 GiB): loads return 0
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint32_t bytes)
@@ -90,273 +89,303 @@ __device__ __forceinline__ const uint16_t *down_base(const FwdArgs &a, int e)
     }
 }
 
-// Validity of block b; returns its expert or -1.
-__device__ __forceinline__ int block_owner(const FwdArgs &a, int BM, int b)
+// ---------------------------------------------------------------------------- tile order
+// Workgroups are dispatched round-robin over the 8 XCDs (workgroup i runs on
+// XCD i mod 8, each XCD with its own L2).  The grid is sized for the most
+// blocks the routing can produce, but only num_padded / BM blocks exist, so
+// the logical tiles u of the existing blocks are dealt out first: XCD x walks
+// the contiguous range u in [x*per_xcd, (x+1)*per_xcd) and surplus workgroups
+// exit.  Tiles are grouped GM blocks at a time, column-tile major inside a
+// group: the GM blocks of a group reuse each weight tile from L2, and each
+// block's activation rows are reused across the group's column tiles.
+template <int GM>
+__device__ __forceinline__ bool tile_of(const FwdArgs &a, int BM, int ntiles, int &b, int &nt)
 {
-    const int npad = *a.num_padded;
-    if ((int64_t)(b + 1) * BM > a.sorted_cap || b * BM >= npad)
-        return -1;
+    int blocks = *a.num_padded / BM;
+    const int cap = (int)(a.sorted_cap / BM);
+    blocks = blocks < cap ? blocks : cap;
+    const int total = blocks * ntiles;
+    const int per_xcd = (total + 7) / 8;
+    const int u = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
+    if ((int)(blockIdx.x / 8) >= per_xcd || u >= total)
+        return false;
+    const int g = u / (GM * ntiles), r = u % (GM * ntiles);
+    const int gm = min(GM, blocks - g * GM);
+    nt = r / gm;
+    b = g * GM + r % gm;
+    return true;
+}
+
+// Expert of block b (b < num_padded / BM), or -1 for a corrupt map entry.
+__device__ __forceinline__ int block_owner(const FwdArgs &a, int b)
+{
     const int e = a.block_expert[b];
     return (e >= 0 && e < a.E_tot) ? e : -1;
 }
 
-// ---------------------------------------------------------------------------- gate/up + SiLU*mul
-template <int BM, int BN, int WAVES_M, bool PAGED>
-__global__ __launch_bounds__(256) void k_gemm1(const FwdArgs a)
+// ---------------------------------------------------------------------------- LDS stages
+// A stage holds the K-slice [k0, k0+BK) of the A rows (BM) and of the B rows
+// (2*BN gate|up, or BN) as rows of BK bf16 (BK*2 bytes), filled by
+// buffer_load_dwordx4 ... lds: one instruction moves 64 x 16 bytes into 1 KB of
+// LDS, lane L at byte 16*L.  A lane therefore picks which global 16-byte chunk
+// lands in its LDS slot; chunk c of row r is stored at position
+// c ^ swz(r) of that row, so that the 16-byte MFMA operand reads of 8
+// consecutive rows at one chunk index hit 8 different 16-byte bank groups.
+template <int BK>
+struct StageGeom {
+    static constexpr int ROWB = BK * 2;          // bytes per row
+    static constexpr int CH = BK / 8;            // 16-byte chunks per row
+    static constexpr int ROWS_PER_LD = 64 / CH;  // rows one DMA instruction covers
+    __device__ static __forceinline__ int swz(int r) { return CH == 8 ? (r & 7) : ((r >> 1) & 3); }
+};
+
+template <int N>
+struct Int {
+    static constexpr int value = N;
+};
+
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm0(Int<N>)
 {
-    constexpr int WAVES_N = 4 / WAVES_M;
-    constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
-    constexpr int FM = WM / 16, FN = WN / 16;
-    static_assert(FM >= 1 && FN >= 1 && WM % 16 == 0 && WN % 16 == 0, "tile");
-    constexpr int A_ROWS = BM, B_ROWS = 2 * BN;
-    constexpr int A_LD = (A_ROWS * 8 + 255) / 256;
-    constexpr int B_LD = B_ROWS * 8 / 256;
-    constexpr int B_GATE_LD = BN * 8 / 256; // loads q < this fetch W1 rows
-    static_assert(B_ROWS * 8 % 256 == 0 && BN * 8 % 256 == 0, "B tile");
-    __shared__ __attribute__((aligned(16))) uint16_t As[2][A_ROWS * BKP];
-    __shared__ __attribute__((aligned(16))) uint16_t Bs[2][B_ROWS * BKP];
+    static_assert(N < 64, "vmcnt");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0x0 << 8));
+}
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave / WAVES_N, wn = wave % WAVES_N;
-    const int b = blockIdx.y;
-    const int e = block_owner(a, BM, b);
-    if (e < 0)
-        return;
-    const uint16_t *w1, *w3;
-    gate_up_bases<PAGED>(a, e, w1, w3);
-    const int d = a.d, f = a.f, keff = a.keff;
-    const int j0 = blockIdx.x * BN;
-    const uint32_t page_bytes = (uint32_t)((int64_t)f * d * 2);
-    const auto rx = make_rsrc(a.x, (uint32_t)(a.T * d * 2));
-    const auto r1 = make_rsrc(w1, page_bytes);
-    const auto r3 = make_rsrc(w3, page_bytes);
-    const int64_t nflat = a.T * keff;
+// ---------------------------------------------------------------------------- grouped GEMM
+// G1 (gate/up): A = x rows gathered by token, B = W1 rows n0..n0+BN and W3 rows
+//     n0..n0+BN, K = d; epilogue h = bf16(silu(gate) * up).
+// G2 (down):    A = h rows of the block, B = W2 rows n0..n0+BN, K = f;
+//     epilogue: x routing weight -> combine buffer (ordered) or y32 (atomic).
+// The K order of the accumulation (32-wide MFMA steps, lane group g holding k
+// 8g..8g+7 of each step) is the same for every tile shape, so the result of an
+// output element does not depend on BM, BN or the weight layout.
+template <int BM, int BN, int WAVES_M, int WAVES_N, int BK, int S, bool G1>
+struct Gemm {
+    using Geo = StageGeom<BK>;
+    static constexpr int NW = WAVES_M * WAVES_N;
+    static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
+    static constexpr int FM = WM / 16, FN = WN / 16;
+    static_assert(FM >= 1 && FN >= 1 && WM % 16 == 0 && WN % 16 == 0, "wave tile");
+    static constexpr int B_ROWS = G1 ? 2 * BN : BN;
+    static constexpr int ROWS = BM + B_ROWS;
+    static_assert(ROWS % (Geo::ROWS_PER_LD * NW) == 0, "DMA instructions must split evenly over the waves");
+    static constexpr int IPW = ROWS / Geo::ROWS_PER_LD / NW; // DMA instructions per wave per stage
+    static_assert(BM % Geo::ROWS_PER_LD == 0 && BN % Geo::ROWS_PER_LD == 0, "sections");
+    static constexpr int STAGE_BYTES = ROWS * Geo::ROWB;
+    static_assert(S >= 2 && S <= 8 && (S - 2) * IPW < 64, "stages");
 
-    uint32_t aoff[A_LD], boff[B_LD];
-#pragma unroll
-    for (int q = 0; q < A_LD; q++) {
-        const int L = tid + 256 * q, row = L >> 3, ch = L & 7;
-        aoff[q] = kOOB;
-        if (L < A_ROWS * 8) {
-            const int flat = a.sorted_ids[b * BM + row];
-            if (flat >= 0 && flat < nflat)
-                aoff[q] = (uint32_t)(flat / keff) * (uint32_t)d * 2u + ch * 16u;
-        }
-    }
-#pragma unroll
-    for (int q = 0; q < B_LD; q++) {
-        const int L = tid + 256 * q, row = L >> 3, ch = L & 7;
-        boff[q] = (uint32_t)(j0 + row % BN) * (uint32_t)d * 2u + ch * 16u;
+    __amdgpu_buffer_rsrc_t ra, rb0, rb1;
+    uint32_t voff[IPW];
+    int wave, wm, wn, l16, lg;
+    uint8_t *lds; // S stages of STAGE_BYTES, one workgroup-scope array
+    f32x4 acc0[FM][FN], acc1[FM][FN];
+
+    // Stage J at a constant offset: the waits on the DMA into one stage then
+    // never cover the LDS reads of another.
+    template <int J>
+    __device__ __forceinline__ uint8_t *stage() const
+    {
+        static_assert(J < S, "stage");
+        return lds + J * STAGE_BYTES;
     }
 
-    i32x4 ra[A_LD], rb[B_LD];
-    auto gload = [&](int kt) {
+    // DMA of K-step kt into stage J: instruction i of this wave reads section
+    // 0 (A), 1 (B gate / W2) or 2 (B up).
+    template <int J>
+    __device__ __forceinline__ void issue(int kt)
+    {
+        uint8_t *slot = stage<J>();
         const int soff = kt * BK * 2;
 #pragma unroll
-        for (int q = 0; q < A_LD; q++)
-            ra[q] = bload(rx, aoff[q], soff);
-#pragma unroll
-        for (int q = 0; q < B_LD; q++)
-            rb[q] = bload(q < B_GATE_LD ? r1 : r3, boff[q], soff);
-    };
-    auto sstore = [&](int buf) {
-#pragma unroll
-        for (int q = 0; q < A_LD; q++) {
-            const int L = tid + 256 * q;
-            if (L < A_ROWS * 8)
-                *(i32x4 *)&As[buf][(L >> 3) * BKP + (L & 7) * 8] = ra[q];
+        for (int i = 0; i < IPW; i++) {
+            const int q = wave + NW * i;
+            const int row0 = q * Geo::ROWS_PER_LD;
+            auto *dst = (__attribute__((address_space(3))) void *)(slot + q * 1024);
+            if (row0 < BM)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, dst, 16, voff[i], soff, 0, 0);
+            else if (!G1 || row0 - BM < BN)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rb0, dst, 16, voff[i], soff, 0, 0);
+            else
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rb1, dst, 16, voff[i], soff, 0, 0);
         }
-#pragma unroll
-        for (int q = 0; q < B_LD; q++) {
-            const int L = tid + 256 * q;
-            *(i32x4 *)&Bs[buf][(L >> 3) * BKP + (L & 7) * 8] = rb[q];
-        }
-    };
+    }
 
-    f32x4 accg[FM][FN], accu[FM][FN];
+    template <int J>
+    __device__ __forceinline__ void compute()
+    {
+        const uint8_t *sp = stage<J>();
 #pragma unroll
-    for (int i = 0; i < FM; i++)
+        for (int sub = 0; sub < BK / 32; sub++) {
+            const int chunk = 4 * sub + lg;
+            bf16x8 af[FM], b0[FN], b1[FN];
 #pragma unroll
-        for (int j = 0; j < FN; j++) {
-            accg[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-            accu[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-
-    const int KT = d / BK;
-    gload(0);
-    sstore(0);
-    __syncthreads();
-    const int lrow = lane & 15, lk = 8 * (lane >> 4);
-    for (int kt = 0; kt < KT; kt++) {
-        const int cur = kt & 1;
-        if (kt + 1 < KT)
-            gload(kt + 1);
-#pragma unroll
-        for (int kk = 0; kk < BK; kk += 32) {
-            bf16x8 af[FM], bg[FN], bu[FN];
-#pragma unroll
-            for (int i = 0; i < FM; i++)
-                af[i] = *(const bf16x8 *)&As[cur][(wm * WM + i * 16 + lrow) * BKP + kk + lk];
+            for (int i = 0; i < FM; i++) {
+                const int row = wm * WM + 16 * i + l16;
+                af[i] = *(const bf16x8 *)(sp + row * Geo::ROWB + ((chunk ^ Geo::swz(row)) * 16));
+            }
 #pragma unroll
             for (int j = 0; j < FN; j++) {
-                const int r = wn * WN + j * 16 + lrow;
-                bg[j] = *(const bf16x8 *)&Bs[cur][r * BKP + kk + lk];
-                bu[j] = *(const bf16x8 *)&Bs[cur][(BN + r) * BKP + kk + lk];
+                const int row = BM + wn * WN + 16 * j + l16;
+                b0[j] = *(const bf16x8 *)(sp + row * Geo::ROWB + ((chunk ^ Geo::swz(row)) * 16));
+                if constexpr (G1) {
+                    const int row1 = row + BN;
+                    b1[j] = *(const bf16x8 *)(sp + row1 * Geo::ROWB + ((chunk ^ Geo::swz(row1)) * 16));
+                }
             }
 #pragma unroll
             for (int i = 0; i < FM; i++)
 #pragma unroll
                 for (int j = 0; j < FN; j++) {
-                    accg[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bg[j], accg[i][j], 0, 0, 0);
-                    accu[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bu[j], accu[i][j], 0, 0, 0);
+                    acc0[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], b0[j], acc0[i][j], 0, 0, 0);
+                    if constexpr (G1)
+                        acc1[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], b1[j], acc1[i][j], 0, 0, 0);
                 }
         }
-        if (kt + 1 < KT)
-            sstore(cur ^ 1);
-        __syncthreads();
     }
 
-    uint16_t *hb = a.h + (int64_t)b * BM * f + j0;
-#pragma unroll
-    for (int i = 0; i < FM; i++)
-#pragma unroll
-        for (int j = 0; j < FN; j++)
-#pragma unroll
-            for (int r = 0; r < 4; r++) {
-                const int row = wm * WM + i * 16 + 4 * (lane >> 4) + r;
-                const int col = wn * WN + j * 16 + lrow;
-                const float g = accg[i][j][r], u = accu[i][j][r];
-                hb[(int64_t)row * f + col] = f32_to_bf16(g / (1.f + __expf(-g)) * u);
-            }
-}
-
-// ---------------------------------------------------------------------------- down + weighted combine
-template <int BM, int BN, int WAVES_M, bool PAGED, bool ATOMIC>
-__global__ __launch_bounds__(256) void k_gemm2(const FwdArgs a)
-{
-    constexpr int WAVES_N = 4 / WAVES_M;
-    constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
-    constexpr int FM = WM / 16, FN = WN / 16;
-    static_assert(FM >= 1 && FN >= 1 && WM % 16 == 0 && WN % 16 == 0, "tile");
-    constexpr int A_LD = (BM * 8 + 255) / 256;
-    constexpr int B_LD = BN * 8 / 256;
-    static_assert(BN * 8 % 256 == 0, "B tile");
-    __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * BKP];
-    __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * BKP];
-    __shared__ int s_flat[BM];
-    __shared__ float s_w[BM];
-
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave / WAVES_N, wn = wave % WAVES_N;
-    const int b = blockIdx.y;
-    const int e = block_owner(a, BM, b);
-    if (e < 0)
-        return;
-    const uint16_t *w2 = down_base<PAGED>(a, e);
-    const int d = a.d, f = a.f;
-    const int r0 = blockIdx.x * BN;
-    const int64_t nflat = a.T * a.keff;
-    const auto rh = make_rsrc(a.h, (uint32_t)(a.sorted_cap * f * 2));
-    const auto rw = make_rsrc(w2, (uint32_t)((int64_t)f * d * 2));
-
-    if (tid < BM) {
-        const int flat = a.sorted_ids[b * BM + tid];
-        const bool ok = flat >= 0 && flat < nflat;
-        s_flat[tid] = ok ? flat : -1;
-        s_w[tid] = ok ? a.topk_w[flat] : 0.f;
-    }
-
-    uint32_t aoff[A_LD], boff[B_LD];
-#pragma unroll
-    for (int q = 0; q < A_LD; q++) {
-        const int L = tid + 256 * q, row = L >> 3, ch = L & 7;
-        aoff[q] = L < BM * 8 ? (uint32_t)(b * BM + row) * (uint32_t)f * 2u + ch * 16u : kOOB;
-    }
-#pragma unroll
-    for (int q = 0; q < B_LD; q++) {
-        const int L = tid + 256 * q, row = L >> 3, ch = L & 7;
-        boff[q] = (uint32_t)(r0 + row) * (uint32_t)f * 2u + ch * 16u;
-    }
-
-    i32x4 ra[A_LD], rb[B_LD];
-    auto gload = [&](int kt) {
-        const int soff = kt * BK * 2;
-#pragma unroll
-        for (int q = 0; q < A_LD; q++)
-            ra[q] = bload(rh, aoff[q], soff);
-#pragma unroll
-        for (int q = 0; q < B_LD; q++)
-            rb[q] = bload(rw, boff[q], soff);
-    };
-    auto sstore = [&](int buf) {
-#pragma unroll
-        for (int q = 0; q < A_LD; q++) {
-            const int L = tid + 256 * q;
-            if (L < BM * 8)
-                *(i32x4 *)&As[buf][(L >> 3) * BKP + (L & 7) * 8] = ra[q];
+    template <int J>
+    __device__ __forceinline__ void prologue()
+    {
+        if constexpr (J < S - 1) {
+            this->template issue<J>(J);
+            this->template prologue<J + 1>();
         }
-#pragma unroll
-        for (int q = 0; q < B_LD; q++) {
-            const int L = tid + 256 * q;
-            *(i32x4 *)&Bs[buf][(L >> 3) * BKP + (L & 7) * 8] = rb[q];
-        }
-    };
-
-    f32x4 acc[FM][FN];
-#pragma unroll
-    for (int i = 0; i < FM; i++)
-#pragma unroll
-        for (int j = 0; j < FN; j++)
-            acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    const int KT = f / BK;
-    gload(0);
-    sstore(0);
-    __syncthreads();
-    const int lrow = lane & 15, lk = 8 * (lane >> 4);
-    for (int kt = 0; kt < KT; kt++) {
-        const int cur = kt & 1;
-        if (kt + 1 < KT)
-            gload(kt + 1);
-#pragma unroll
-        for (int kk = 0; kk < BK; kk += 32) {
-            bf16x8 af[FM], bf[FN];
-#pragma unroll
-            for (int i = 0; i < FM; i++)
-                af[i] = *(const bf16x8 *)&As[cur][(wm * WM + i * 16 + lrow) * BKP + kk + lk];
-#pragma unroll
-            for (int j = 0; j < FN; j++)
-                bf[j] = *(const bf16x8 *)&Bs[cur][(wn * WN + j * 16 + lrow) * BKP + kk + lk];
-#pragma unroll
-            for (int i = 0; i < FM; i++)
-#pragma unroll
-                for (int j = 0; j < FN; j++)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
-        }
-        if (kt + 1 < KT)
-            sstore(cur ^ 1);
-        __syncthreads();
     }
 
+    // one pass over the S stages: K-steps kt0 .. kt0+S-1
+    template <int J>
+    __device__ __forceinline__ void steps(int kt0, int KT)
+    {
+        if constexpr (J < S) {
+            const int kt = kt0 + J;
+            // stage kt has landed for this wave and this wave's reads of the
+            // stage about to be refilled are done; then the same for every wave
+            wait_vm_lgkm0(Int<(S - 2) * IPW>{});
+            __builtin_amdgcn_s_barrier();
+            constexpr int NEXT = (J + S - 1) % S;
+            this->template issue<NEXT>(kt + S - 1);
+            if (kt < KT)
+                this->template compute<J>();
+            this->template steps<J + 1>(kt0, KT);
+        }
+    }
+
+    __device__ __forceinline__ void run(int KT)
+    {
 #pragma unroll
-    for (int i = 0; i < FM; i++)
-#pragma unroll
-        for (int r = 0; r < 4; r++) {
-            const int row = wm * WM + i * 16 + 4 * (lane >> 4) + r;
-            const int flat = s_flat[row];
-            if (flat < 0)
-                continue;
-            const float wt = s_w[row];
+        for (int i = 0; i < FM; i++)
 #pragma unroll
             for (int j = 0; j < FN; j++) {
-                const int col = r0 + wn * WN + j * 16 + lrow;
-                const float v = acc[i][j][r] * wt;
-                if constexpr (ATOMIC)
-                    unsafeAtomicAdd(&a.comb[(int64_t)(flat / a.keff) * d + col], v);
-                else
-                    a.comb[(int64_t)flat * d + col] = v;
+                acc0[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+                acc1[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
             }
+        prologue<0>();
+        for (int kt0 = 0; kt0 < KT; kt0 += S)
+            steps<0>(kt0, KT);
+        wait_vm_lgkm0(Int<0>{}); // no DMA may still be writing this workgroup's LDS when it exits
+    }
+};
+
+template <int BM, int BN, int WAVES_M, int WAVES_N, int BK, int S, int GM, bool G1, bool PAGED, bool ATOMIC>
+__global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm(const FwdArgs a)
+{
+    // The host pass only needs this kernel's signature (for its launch stub);
+    // the pipeline's gfx950 builtins are compiled in the device pass.
+#if defined(__HIP_DEVICE_COMPILE__)
+    using G = Gemm<BM, BN, WAVES_M, WAVES_N, BK, S, G1>;
+    using Geo = typename G::Geo;
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[S * G::STAGE_BYTES];
+    G g;
+    g.lds = lds;
+    const int tid = threadIdx.x, lane = tid & 63;
+    g.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    g.wm = g.wave / WAVES_N;
+    g.wn = g.wave % WAVES_N;
+    g.l16 = lane & 15;
+    g.lg = lane >> 4;
+    const int ntiles = (G1 ? a.f : a.d) / BN;
+    int b, nt;
+    if (!tile_of<GM>(a, BM, ntiles, b, nt))
+        return;
+    const int e = block_owner(a, b);
+    if (e < 0)
+        return;
+    const int d = a.d, f = a.f, K = G1 ? d : f;
+    const int n0 = nt * BN;
+    const int64_t nflat = a.T * a.keff;
+    const uint32_t page_bytes = (uint32_t)((int64_t)f * d * 2);
+
+    if constexpr (G1) {
+        const uint16_t *w1, *w3;
+        gate_up_bases<PAGED>(a, e, w1, w3);
+        g.ra = make_rsrc(a.x, (uint32_t)(a.T * d * 2));
+        g.rb0 = make_rsrc(w1, page_bytes);
+        g.rb1 = make_rsrc(w3, page_bytes);
+    } else {
+        g.ra = make_rsrc(a.h, (uint32_t)(a.sorted_cap * f * 2));
+        g.rb0 = g.rb1 = make_rsrc(down_base<PAGED>(a, e), page_bytes);
+    }
+
+    // per-lane source offset of each DMA instruction this wave issues
+    const int lrow = lane / Geo::CH, lpos = lane % Geo::CH;
+#pragma unroll
+    for (int i = 0; i < G::IPW; i++) {
+        const int q = g.wave + G::NW * i;              // instruction index within the stage
+        const int row = q * Geo::ROWS_PER_LD + lrow;  // row within the stage
+        const int chunk = lpos ^ Geo::swz(row);
+        uint32_t off;
+        if (row < BM) {
+            if constexpr (G1) {
+                const int flat = a.sorted_ids[b * BM + row];
+                off = (flat >= 0 && flat < nflat) ? (uint32_t)(flat / a.keff) * (uint32_t)d * 2u : kOOB;
+            } else {
+                off = (uint32_t)(b * BM + row) * (uint32_t)f * 2u;
+            }
+        } else {
+            const int br = (row - BM) % BN;
+            off = (uint32_t)(n0 + br) * (uint32_t)K * 2u;
         }
+        g.voff[i] = off + chunk * 16u;
+    }
+
+    g.run(K / BK);
+
+    const int lg = g.lg, l16 = g.l16;
+    if constexpr (G1) {
+        uint16_t *hb = a.h + (int64_t)b * BM * f + n0;
+#pragma unroll
+        for (int i = 0; i < G::FM; i++)
+#pragma unroll
+            for (int j = 0; j < G::FN; j++)
+#pragma unroll
+                for (int r = 0; r < 4; r++) {
+                    const int row = g.wm * G::WM + i * 16 + 4 * lg + r;
+                    const int col = g.wn * G::WN + j * 16 + l16;
+                    const float gt = g.acc0[i][j][r], up = g.acc1[i][j][r];
+                    hb[(int64_t)row * f + col] = f32_to_bf16(gt / (1.f + __expf(-gt)) * up);
+                }
+    } else {
+#pragma unroll
+        for (int i = 0; i < G::FM; i++)
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                const int row = g.wm * G::WM + i * 16 + 4 * lg + r;
+                const int flat = a.sorted_ids[b * BM + row];
+                if (flat < 0 || flat >= nflat)
+                    continue;
+                const float wt = a.topk_w[flat];
+#pragma unroll
+                for (int j = 0; j < G::FN; j++) {
+                    const int col = n0 + g.wn * G::WN + j * 16 + l16;
+                    const float v = g.acc0[i][j][r] * wt;
+                    if constexpr (ATOMIC)
+                        unsafeAtomicAdd(&a.comb[(int64_t)(flat / a.keff) * d + col], v);
+                    else
+                        a.comb[(int64_t)flat * d + col] = v;
+                }
+            }
+    }
+#endif
 }
 
 // ---------------------------------------------------------------------------- combine / convert
@@ -421,28 +450,54 @@ __global__ __launch_bounds__(256) void k_resolve(const ResolveArgs r, const FwdA
     r.base[q] = in_pool ? 0 : 1 + r.active_buf;
 }
 
-template <int BM, int BN1, int BN2, int WAVES_M, bool PAGED>
+// Tile shapes: block height BM; for each GEMM the column tile BN, the wave
+// grid (M x N), the K-step BK and the number of LDS stages.
+template <int BM_, int BN1_, int WM1_, int WN1_, int BK1_, int S1_, int BN2_, int WM2_, int WN2_, int BK2_, int S2_>
+struct Tiles {
+    static constexpr int BM = BM_;
+    static constexpr int BN1 = BN1_, WM1 = WM1_, WN1 = WN1_, BK1 = BK1_, S1 = S1_;
+    static constexpr int BN2 = BN2_, WM2 = WM2_, WN2 = WN2_, BK2 = BK2_, S2 = S2_;
+};
+// decode-sized blocks: one wave per tile and a deep pipeline (many tiles, many bytes in flight)
+using Tiles16 = Tiles<16, 16, 1, 1, 32, 8, 16, 1, 1, 32, 8>;
+using Tiles32 = Tiles<32, 32, 1, 2, 64, 2, 32, 1, 2, 64, 2>;
+using Tiles64 = Tiles<64, 64, 2, 2, 64, 2, 64, 2, 2, 64, 2>;
+using Tiles128 = Tiles<128, 64, 2, 2, 64, 2, 128, 2, 2, 64, 2>;
+// large blocks: 8 waves, 64x(64+64) wave tiles for the MFMA-bound shapes
+using Tiles256 = Tiles<256, 128, 4, 2, 64, 2, 128, 4, 2, 64, 2>;
+using Tiles256n = Tiles<256, 64, 4, 2, 32, 4, 64, 4, 1, 32, 4>; // when f or d is not a multiple of 128
+
+constexpr int kGroupM = 4;
+
+template <class C, bool PAGED>
 hipError_t launch_tiles(const FwdArgs &a, hipStream_t s)
 {
+    constexpr int BM = C::BM;
     const int64_t n = a.T * a.keff;
     int64_t grid_m = n / BM + (n < a.E_tot ? n : a.E_tot);
     if (grid_m > a.blocks_cap)
         grid_m = a.blocks_cap;
+    if (a.f % C::BN1 || a.d % C::BN2)
+        return hipErrorInvalidValue;
     auto mark = [&](int i) {
         if (a.ev[i])
             (void)hipEventRecord(a.ev[i], s);
     };
+    auto grid = [&](int ntiles) { return (unsigned)((grid_m * ntiles + 7) / 8 * 8); };
     if (a.atomic) {
         const int64_t n4 = a.T * a.d / 4;
         k_zero<<<(unsigned)((n4 + 255) / 256), 256, 0, s>>>((float4 *)a.comb, n4);
     }
     mark(0);
-    k_gemm1<BM, BN1, WAVES_M, PAGED><<<dim3(a.f / BN1, (unsigned)grid_m), 256, 0, s>>>(a);
+    k_gemm<BM, C::BN1, C::WM1, C::WN1, C::BK1, C::S1, kGroupM, true, PAGED, false>
+        <<<grid(a.f / C::BN1), 64 * C::WM1 * C::WN1, 0, s>>>(a);
     mark(1);
     if (a.atomic)
-        k_gemm2<BM, BN2, WAVES_M, PAGED, true><<<dim3(a.d / BN2, (unsigned)grid_m), 256, 0, s>>>(a);
+        k_gemm<BM, C::BN2, C::WM2, C::WN2, C::BK2, C::S2, kGroupM, false, PAGED, true>
+            <<<grid(a.d / C::BN2), 64 * C::WM2 * C::WN2, 0, s>>>(a);
     else
-        k_gemm2<BM, BN2, WAVES_M, PAGED, false><<<dim3(a.d / BN2, (unsigned)grid_m), 256, 0, s>>>(a);
+        k_gemm<BM, C::BN2, C::WM2, C::WN2, C::BK2, C::S2, kGroupM, false, PAGED, false>
+            <<<grid(a.d / C::BN2), 64 * C::WM2 * C::WN2, 0, s>>>(a);
     mark(2);
     const int rows = a.atomic ? 1 : a.keff;
     const int64_t nq = a.T * a.d / 4;
@@ -455,11 +510,14 @@ template <bool PAGED>
 hipError_t launch_paged(const FwdArgs &a, hipStream_t s)
 {
     switch (a.BM) {
-    case 16: return launch_tiles<16, 64, 64, 1, PAGED>(a, s);
-    case 32: return launch_tiles<32, 64, 64, 2, PAGED>(a, s);
-    case 64: return launch_tiles<64, 64, 64, 2, PAGED>(a, s);
-    case 128: return launch_tiles<128, 64, 64, 2, PAGED>(a, s);
-    case 256: return launch_tiles<256, 64, 64, 4, PAGED>(a, s);
+    case 16: return launch_tiles<Tiles16, PAGED>(a, s);
+    case 32: return launch_tiles<Tiles32, PAGED>(a, s);
+    case 64: return launch_tiles<Tiles64, PAGED>(a, s);
+    case 128: return launch_tiles<Tiles128, PAGED>(a, s);
+    case 256:
+        if (a.f % Tiles256::BN1 == 0 && a.d % Tiles256::BN2 == 0)
+            return launch_tiles<Tiles256, PAGED>(a, s);
+        return launch_tiles<Tiles256n, PAGED>(a, s);
     default: return hipErrorInvalidValue;
     }
 }

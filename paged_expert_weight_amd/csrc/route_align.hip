@@ -12,24 +12,29 @@
 // Alignment: a stable counting sort of the flat picks i = t*(k+S) + j by expert
 // with each expert's run padded to the GEMM tile height BM, so that every
 // BM-row block of the grouped GEMMs belongs to one expert:
-//   histogram (per chunk of flat entries, LDS atomics: counts are order free)
+//   histogram (per chunk of flat entries: counts are order free)
 //   -> exclusive scan of the padded counts over experts, and of the raw counts
-//      over chunks (the start of every (chunk, expert) run)
+//      over chunks and waves (the start of every (chunk, wave, expert) run)
 //   -> in-order scatter: inside a chunk each wave owns a contiguous range and
-//      walks it 64 entries at a time; the lanes holding one expert are found
-//      with a ballot, ranked by popcount of the lower lanes, and the run's
-//      cursor advances by the ballot's popcount, so the order is the flat order.
-// Small batches run all of it in one workgroup (one launch); large batches use
-// route, histogram, scan and scatter kernels.
+//      walks it 64 entries at a time.  The lanes that hold the same expert are
+//      found in one pass by slicing the expert id into bits (one ballot per
+//      bit: the lanes agreeing with mine on every bit hold my expert); a lane's
+//      rank is the popcount of the matching lanes below it, and the lowest
+//      matching lane advances the run's cursor by the match count.  Distinct
+//      experts of a group update distinct cursors, so the 64 entries of a group
+//      are placed at once, in flat order.
+// Small batches run routing and alignment in one workgroup (one launch);
+// larger ones route with one wave per token and align in one workgroup up to
+// kChunkElems entries, or with histogram / scan / scatter kernels over chunks.
 #include "internal.h"
 
 namespace pmoe {
 namespace {
 
-constexpr int kAlignWaves = 8;
+constexpr int kAlignWaves = 16;
 constexpr int kAlignThreads = 64 * kAlignWaves;
-constexpr int kChunkElems = 2048; // flat entries per alignment chunk
-constexpr int kSmallTokens = 64;  // one-workgroup route + align when T <= this and T*keff <= kChunkElems
+constexpr int kChunkElems = 8192; // flat entries per alignment workgroup
+constexpr int kSmallTokens = 64;  // route + align in one workgroup when T <= this (and T*keff <= kChunkElems)
 
 __device__ __forceinline__ bool beats(float va, int ia, float vb, int ib)
 {
@@ -122,14 +127,75 @@ __device__ __forceinline__ void wave_range(int n, int w, int &lo, int &hi)
     hi = min(n, lo + per);
 }
 
-// Per-wave histogram of the chunk held in s_ids[0..n).  s_cnt[w*E_tot + e] must be zero.
+// Lanes of the wave whose id equals mine (valid lanes only), from one ballot per id bit.
+__device__ __forceinline__ uint64_t same_id_lanes(int e, bool valid, int nbits)
+{
+    uint64_t m = __ballot(valid);
+    for (int b = 0; b < nbits; b++) {
+        const bool bit = (e >> b) & 1;
+        const uint64_t on = __ballot(bit);
+        m &= bit ? on : ~on;
+    }
+    return m;
+}
+
+__device__ __forceinline__ int id_bits(int E_tot)
+{
+    int b = 0;
+    while ((1 << b) < E_tot)
+        b++;
+    return b;
+}
+
+__device__ __forceinline__ uint64_t lanes_below()
+{
+    const int lane = threadIdx.x & 63;
+    return lane == 0 ? 0ull : (~0ull >> (64 - lane));
+}
+
+// Per-wave histogram of the chunk s_ids[0..n): s_cnt[w*E_tot + e] (must start at zero).
 __device__ void chunk_hist(const int32_t *s_ids, int n, int E_tot, int *s_cnt)
 {
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int nbits = id_bits(E_tot);
+    const uint64_t below = lanes_below();
     int lo, hi;
     wave_range(n, w, lo, hi);
-    for (int i = lo + lane; i < hi; i += 64)
-        atomicAdd(&s_cnt[w * E_tot + s_ids[i]], 1);
+    for (int g = lo; g < hi; g += 64) {
+        const int i = g + lane;
+        const bool valid = i < hi;
+        const int e = valid ? s_ids[i] : 0;
+        const uint64_t m = same_id_lanes(e, valid, nbits);
+        if (valid && (m & below) == 0)
+            s_cnt[w * E_tot + e] += __popcll(m);
+    }
+}
+
+// In-order scatter of the chunk s_ids[0..n) whose first flat index is elem0.
+// s_cur[w*E_tot + e] = position in sorted_ids of wave w's next entry of expert e.
+__device__ void chunk_scatter(const int32_t *s_ids, int n, int elem0, int E_tot, int *s_cur,
+                              int32_t *sorted_ids)
+{
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int nbits = id_bits(E_tot);
+    const uint64_t below = lanes_below();
+    int lo, hi;
+    wave_range(n, w, lo, hi);
+    for (int g = lo; g < hi; g += 64) {
+        const int i = g + lane;
+        const bool valid = i < hi;
+        const int e = valid ? s_ids[i] : 0;
+        const uint64_t m = same_id_lanes(e, valid, nbits);
+        if (valid) {
+            const int base = s_cur[w * E_tot + e];
+            sorted_ids[base + __popcll(m & below)] = elem0 + i;
+        }
+        // every lane has read its cursor before any leader moves one
+        __builtin_amdgcn_wave_barrier();
+        if (valid && (m & below) == 0)
+            s_cur[w * E_tot + e] += __popcll(m);
+        __builtin_amdgcn_wave_barrier();
+    }
 }
 
 // Exclusive scan across the workgroup of one int per thread; *total gets the sum.
@@ -159,27 +225,18 @@ __device__ int wg_exclusive_scan(int v, int *s_tmp, int *total)
 
 // Given per-expert token counts cnt(e), write each expert's padded segment start
 // into seg_start[e], the block->expert map, the sentinel padding and num_padded.
-// Each thread owns experts 2*tid and 2*tid+1 (E_tot <= 2*kAlignThreads).
+// Thread t owns expert t (E_tot <= kAlignThreads).
 template <class CountFn>
 __device__ void scan_experts(CountFn cnt, int E_tot, int BM, int n, int *seg_start, int *s_tmp,
                              const RouteArgs &a)
 {
-    const int e0 = 2 * threadIdx.x, e1 = e0 + 1;
-    const int c0 = e0 < E_tot ? cnt(e0) : 0;
-    const int c1 = e1 < E_tot ? cnt(e1) : 0;
-    const int p0 = (c0 + BM - 1) / BM * BM;
-    const int p1 = (c1 + BM - 1) / BM * BM;
+    const int e = threadIdx.x;
+    const int c = e < E_tot ? cnt(e) : 0;
+    const int p = (c + BM - 1) / BM * BM;
     int total;
-    const int o0 = wg_exclusive_scan(p0 + p1, s_tmp, &total);
-    const int o1 = o0 + p0;
-    if (e0 < E_tot)
-        seg_start[e0] = o0;
-    if (e1 < E_tot)
-        seg_start[e1] = o1;
-    for (int pass = 0; pass < 2; pass++) {
-        const int e = pass ? e1 : e0, c = pass ? c1 : c0, p = pass ? p1 : p0, o = pass ? o1 : o0;
-        if (e >= E_tot)
-            continue;
+    const int o = wg_exclusive_scan(p, s_tmp, &total);
+    if (e < E_tot) {
+        seg_start[e] = o;
         for (int b = o / BM; b < (o + p) / BM; b++)
             a.block_expert[b] = e;
         for (int pos = o + c; pos < o + p; pos++)
@@ -187,34 +244,6 @@ __device__ void scan_experts(CountFn cnt, int E_tot, int BM, int n, int *seg_sta
     }
     if (threadIdx.x == 0)
         *a.num_padded = total;
-}
-
-// In-order scatter of the chunk s_ids[0..n) whose first flat index is elem0.
-// s_cur[w*E_tot + e] = position in sorted_ids of wave w's first entry of expert e.
-__device__ void chunk_scatter(const int32_t *s_ids, int n, int elem0, int E_tot, int *s_cur,
-                              int32_t *sorted_ids)
-{
-    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    int lo, hi;
-    wave_range(n, w, lo, hi);
-    for (int g = lo; g < hi; g += 64) {
-        const int i = g + lane;
-        const bool valid = i < hi;
-        const int e = valid ? s_ids[i] : -1;
-        uint64_t left = __ballot(valid);
-        while (left) {
-            const int leader = __ffsll((unsigned long long)left) - 1;
-            const int le = __shfl(e, leader);
-            const uint64_t mask = __ballot(e == le) & left;
-            const int base = s_cur[w * E_tot + le];
-            if (e == le)
-                sorted_ids[base + __popcll(mask & below)] = elem0 + i;
-            if (lane == leader)
-                s_cur[w * E_tot + le] = base + __popcll(mask);
-            left &= ~mask;
-        }
-    }
 }
 
 // Turn per-wave counts s_cnt[w][e] into per-wave cursors starting at start(e).
@@ -238,7 +267,13 @@ struct AlignSmem {
     int tmp[kAlignWaves];
 };
 
-// Alignment of a whole batch in one workgroup (n <= kChunkElems); s_ids already filled.
+__device__ void zero_counts(AlignSmem &sm, int E_tot)
+{
+    for (int i = threadIdx.x; i < kAlignWaves * E_tot; i += kAlignThreads)
+        sm.cnt[i] = 0;
+}
+
+// Alignment of a whole batch in one workgroup (n <= kChunkElems); sm.ids filled, sm.cnt zero.
 __device__ void align_in_one_wg(AlignSmem &sm, int n, const RouteArgs &a)
 {
     chunk_hist(sm.ids, n, a.E_tot, sm.cnt);
@@ -254,12 +289,6 @@ __device__ void align_in_one_wg(AlignSmem &sm, int n, const RouteArgs &a)
     wave_cursors([&](int e) { return sm.seg[e]; }, a.E_tot, sm.cnt);
     __syncthreads();
     chunk_scatter(sm.ids, n, 0, a.E_tot, sm.cnt, a.sorted_ids);
-}
-
-__device__ void zero_counts(AlignSmem &sm, int E_tot)
-{
-    for (int i = threadIdx.x; i < kAlignWaves * E_tot; i += kAlignThreads)
-        sm.cnt[i] = 0;
 }
 
 template <int NV>

@@ -574,8 +574,9 @@ int32_t moe_suggest_block_m(const moe_pool *p, int64_t T)
 {
     if (!p || T <= 0)
         return 16;
-    // expected rows per active expert; a block should cover an expert's rows
-    // in as few tiles as possible without mostly padding
+    // expected rows per active expert; cover them with one block when that
+    // costs no more MFMA work than two smaller blocks (the weights of an
+    // expert's column tile are then streamed once)
     const int64_t n = T * p->keff;
     const int64_t active = n < p->E_tot ? n : p->E_tot;
     const int64_t per = n / active;
@@ -583,7 +584,7 @@ int32_t moe_suggest_block_m(const moe_pool *p, int64_t T)
         return 16;
     if (per <= 32)
         return 32;
-    if (per <= 96)
+    if (per <= 64)
         return 64;
     return 128;
 }
