@@ -159,25 +159,31 @@ __device__ __forceinline__ void wait_vm_lgkm0(Int<N>)
 // The K order of the accumulation (32-wide MFMA steps, lane group g holding k
 // 8g..8g+7 of each step) is the same for every tile shape, so the result of an
 // output element does not depend on BM, BN or the weight layout.
-template <int BM, int BN, int WAVES_M, int WAVES_N, int BK, int S, bool G1>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int WK, int BK, int S, bool G1>
 struct Gemm {
     using Geo = StageGeom<BK>;
-    static constexpr int NW = WAVES_M * WAVES_N;
+    // WAVES_M x WAVES_N waves share one tile; with WK > 1 (one wave per tile)
+    // WK waves split K into contiguous ranges, each with private LDS stages and
+    // no barriers, and their partial sums are added in wave order at the end.
+    static constexpr int NT = WAVES_M * WAVES_N;
+    static constexpr int NW = NT * WK;
+    static_assert(WK == 1 || NT == 1, "split-K tiles have one wave per K range");
     static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
     static constexpr int FM = WM / 16, FN = WN / 16;
     static_assert(FM >= 1 && FN >= 1 && WM % 16 == 0 && WN % 16 == 0, "wave tile");
     static constexpr int B_ROWS = G1 ? 2 * BN : BN;
     static constexpr int ROWS = BM + B_ROWS;
-    static_assert(ROWS % (Geo::ROWS_PER_LD * NW) == 0, "DMA instructions must split evenly over the waves");
-    static constexpr int IPW = ROWS / Geo::ROWS_PER_LD / NW; // DMA instructions per wave per stage
+    static_assert(ROWS % (Geo::ROWS_PER_LD * NT) == 0, "DMA instructions must split evenly over the waves");
+    static constexpr int IPW = ROWS / Geo::ROWS_PER_LD / NT; // DMA instructions per wave per stage
     static_assert(BM % Geo::ROWS_PER_LD == 0 && BN % Geo::ROWS_PER_LD == 0, "sections");
     static constexpr int STAGE_BYTES = ROWS * Geo::ROWB;
+    static constexpr int LDS_BYTES = WK * S * STAGE_BYTES;
     static_assert(S >= 2 && S <= 8 && (S - 2) * IPW < 64, "stages");
 
     __amdgpu_buffer_rsrc_t ra, rb0, rb1;
     uint32_t voff[IPW];
-    int wave, wm, wn, l16, lg;
-    uint8_t *lds; // S stages of STAGE_BYTES, one workgroup-scope array
+    int wave, wt, kg, wm, wn, l16, lg;
+    uint8_t *lds; // WK x S stages of STAGE_BYTES, one workgroup-scope array
     f32x4 acc0[FM][FN], acc1[FM][FN];
 
     // Stage J at a constant offset: the waits on the DMA into one stage then
@@ -186,7 +192,7 @@ struct Gemm {
     __device__ __forceinline__ uint8_t *stage() const
     {
         static_assert(J < S, "stage");
-        return lds + J * STAGE_BYTES;
+        return lds + (kg * S + J) * STAGE_BYTES;
     }
 
     // DMA of K-step kt into stage J: instruction i of this wave reads section
@@ -198,7 +204,7 @@ struct Gemm {
         const int soff = kt * BK * 2;
 #pragma unroll
         for (int i = 0; i < IPW; i++) {
-            const int q = wave + NW * i;
+            const int q = wt + NT * i;
             const int row0 = q * Geo::ROWS_PER_LD;
             auto *dst = (__attribute__((address_space(3))) void *)(slot + q * 1024);
             if (row0 < BM)
@@ -244,33 +250,36 @@ struct Gemm {
     }
 
     template <int J>
-    __device__ __forceinline__ void prologue()
+    __device__ __forceinline__ void prologue(int kb)
     {
         if constexpr (J < S - 1) {
-            this->template issue<J>(J);
-            this->template prologue<J + 1>();
+            this->template issue<J>(kb + J);
+            this->template prologue<J + 1>(kb);
         }
     }
 
-    // one pass over the S stages: K-steps kt0 .. kt0+S-1
+    // one pass over the S stages: K-steps kt0 .. kt0+S-1 (of the range ending at ke)
     template <int J>
-    __device__ __forceinline__ void steps(int kt0, int KT)
+    __device__ __forceinline__ void steps(int kt0, int ke)
     {
         if constexpr (J < S) {
             const int kt = kt0 + J;
             // stage kt has landed for this wave and this wave's reads of the
-            // stage about to be refilled are done; then the same for every wave
+            // stage about to be refilled are done; then the same for every
+            // wave that shares the stages
             wait_vm_lgkm0(Int<(S - 2) * IPW>{});
-            __builtin_amdgcn_s_barrier();
+            if constexpr (NT > 1)
+                __builtin_amdgcn_s_barrier();
             constexpr int NEXT = (J + S - 1) % S;
             this->template issue<NEXT>(kt + S - 1);
-            if (kt < KT)
+            if (kt < ke)
                 this->template compute<J>();
-            this->template steps<J + 1>(kt0, KT);
+            this->template steps<J + 1>(kt0, ke);
         }
     }
 
-    __device__ __forceinline__ void run(int KT)
+    // K-steps [kb, ke)
+    __device__ __forceinline__ void run(int kb, int ke)
     {
 #pragma unroll
         for (int i = 0; i < FM; i++)
@@ -279,28 +288,72 @@ struct Gemm {
                 acc0[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
                 acc1[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
             }
-        prologue<0>();
-        for (int kt0 = 0; kt0 < KT; kt0 += S)
-            steps<0>(kt0, KT);
+        this->template prologue<0>(kb);
+        for (int kt0 = kb; kt0 < ke; kt0 += S)
+            this->template steps<0>(kt0, ke);
         wait_vm_lgkm0(Int<0>{}); // no DMA may still be writing this workgroup's LDS when it exits
+    }
+
+    // Split-K: add the partial sums of waves 1..WK-1 into wave 0's, in wave order.
+    // Returns false for the waves that are done.
+    __device__ __forceinline__ bool reduce_k()
+    {
+        if constexpr (WK == 1) {
+            return true;
+        } else {
+            constexpr int PER = FM * FN * 8; // floats per lane
+            __syncthreads();
+            float *red = (float *)lds;
+            const int lane = threadIdx.x & 63;
+            if (kg > 0) {
+                float *dst = red + ((kg - 1) * PER) * 64;
+#pragma unroll
+                for (int i = 0; i < FM; i++)
+#pragma unroll
+                    for (int j = 0; j < FN; j++)
+#pragma unroll
+                        for (int r = 0; r < 4; r++) {
+                            dst[((i * FN + j) * 8 + r) * 64 + lane] = acc0[i][j][r];
+                            dst[((i * FN + j) * 8 + 4 + r) * 64 + lane] = acc1[i][j][r];
+                        }
+            }
+            __syncthreads();
+            if (kg > 0)
+                return false;
+            for (int w = 1; w < WK; w++) {
+                const float *src = red + ((w - 1) * PER) * 64;
+#pragma unroll
+                for (int i = 0; i < FM; i++)
+#pragma unroll
+                    for (int j = 0; j < FN; j++)
+#pragma unroll
+                        for (int r = 0; r < 4; r++) {
+                            acc0[i][j][r] += src[((i * FN + j) * 8 + r) * 64 + lane];
+                            acc1[i][j][r] += src[((i * FN + j) * 8 + 4 + r) * 64 + lane];
+                        }
+            }
+            return true;
+        }
     }
 };
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int BK, int S, int GM, bool G1, bool PAGED, bool ATOMIC>
-__global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm(const FwdArgs a)
+template <int BM, int BN, int WAVES_M, int WAVES_N, int WK, int BK, int S, int GM, bool G1, bool PAGED, bool ATOMIC>
+__global__ __launch_bounds__(64 * WAVES_M * WAVES_N * WK) void k_gemm(const FwdArgs a)
 {
     // The host pass only needs this kernel's signature (for its launch stub);
     // the pipeline's gfx950 builtins are compiled in the device pass.
 #if defined(__HIP_DEVICE_COMPILE__)
-    using G = Gemm<BM, BN, WAVES_M, WAVES_N, BK, S, G1>;
+    using G = Gemm<BM, BN, WAVES_M, WAVES_N, WK, BK, S, G1>;
     using Geo = typename G::Geo;
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[S * G::STAGE_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[G::LDS_BYTES];
     G g;
     g.lds = lds;
     const int tid = threadIdx.x, lane = tid & 63;
     g.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    g.wm = g.wave / WAVES_N;
-    g.wn = g.wave % WAVES_N;
+    g.wt = g.wave % G::NT;  // wave within the tile
+    g.kg = g.wave / G::NT;  // K range of this wave
+    g.wm = g.wt / WAVES_N;
+    g.wn = g.wt % WAVES_N;
     g.l16 = lane & 15;
     g.lg = lane >> 4;
     const int ntiles = (G1 ? a.f : a.d) / BN;
@@ -330,7 +383,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm(const FwdArgs a
     const int lrow = lane / Geo::CH, lpos = lane % Geo::CH;
 #pragma unroll
     for (int i = 0; i < G::IPW; i++) {
-        const int q = g.wave + G::NW * i;              // instruction index within the stage
+        const int q = g.wt + G::NT * i;                // instruction index within the stage
         const int row = q * Geo::ROWS_PER_LD + lrow;  // row within the stage
         const int chunk = lpos ^ Geo::swz(row);
         uint32_t off;
@@ -348,7 +401,10 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm(const FwdArgs a
         g.voff[i] = off + chunk * 16u;
     }
 
-    g.run(K / BK);
+    const int KT = K / BK;
+    g.run(g.kg * KT / WK, (g.kg + 1) * KT / WK);
+    if (!g.reduce_k())
+        return;
 
     const int lg = g.lg, l16 = g.l16;
     if constexpr (G1) {
@@ -451,21 +507,22 @@ __global__ __launch_bounds__(256) void k_resolve(const ResolveArgs r, const FwdA
 }
 
 // Tile shapes: block height BM; for each GEMM the column tile BN, the wave
-// grid (M x N), the K-step BK and the number of LDS stages.
-template <int BM_, int BN1_, int WM1_, int WN1_, int BK1_, int S1_, int BN2_, int WM2_, int WN2_, int BK2_, int S2_>
+// grid (M x N), the split-K wave count WK, the K-step BK and the LDS stages.
+template <int BM_, int BN1_, int WM1_, int WN1_, int WK1_, int BK1_, int S1_, int BN2_, int WM2_, int WN2_, int WK2_,
+          int BK2_, int S2_>
 struct Tiles {
     static constexpr int BM = BM_;
-    static constexpr int BN1 = BN1_, WM1 = WM1_, WN1 = WN1_, BK1 = BK1_, S1 = S1_;
-    static constexpr int BN2 = BN2_, WM2 = WM2_, WN2 = WN2_, BK2 = BK2_, S2 = S2_;
+    static constexpr int BN1 = BN1_, WM1 = WM1_, WN1 = WN1_, WK1 = WK1_, BK1 = BK1_, S1 = S1_;
+    static constexpr int BN2 = BN2_, WM2 = WM2_, WN2 = WN2_, WK2 = WK2_, BK2 = BK2_, S2 = S2_;
 };
-// decode-sized blocks: one wave per tile and a deep pipeline (many tiles, many bytes in flight)
-using Tiles16 = Tiles<16, 16, 1, 1, 32, 8, 16, 1, 1, 32, 8>;
-using Tiles32 = Tiles<32, 32, 1, 2, 64, 2, 32, 1, 2, 64, 2>;
-using Tiles64 = Tiles<64, 64, 2, 2, 64, 2, 64, 2, 2, 64, 2>;
-using Tiles128 = Tiles<128, 64, 2, 2, 64, 2, 128, 2, 2, 64, 2>;
+// decode-sized blocks: one wave per 16x16 tile, four waves splitting K (many bytes in flight)
+using Tiles16 = Tiles<16, 16, 1, 1, 4, 64, 3, 16, 1, 1, 4, 64, 3>;
+using Tiles32 = Tiles<32, 32, 1, 2, 1, 64, 2, 32, 1, 2, 1, 64, 2>;
+using Tiles64 = Tiles<64, 64, 2, 2, 1, 64, 2, 64, 2, 2, 1, 64, 2>;
+using Tiles128 = Tiles<128, 64, 2, 2, 1, 64, 2, 128, 2, 2, 1, 64, 2>;
 // large blocks: 8 waves, 64x(64+64) wave tiles for the MFMA-bound shapes
-using Tiles256 = Tiles<256, 128, 4, 2, 64, 2, 128, 4, 2, 64, 2>;
-using Tiles256n = Tiles<256, 64, 4, 2, 32, 4, 64, 4, 1, 32, 4>; // when f or d is not a multiple of 128
+using Tiles256 = Tiles<256, 128, 4, 2, 1, 64, 2, 128, 4, 2, 1, 64, 2>;
+using Tiles256n = Tiles<256, 64, 4, 2, 1, 32, 4, 64, 4, 1, 1, 32, 4>; // when f or d is not a multiple of 128
 
 constexpr int kGroupM = 4;
 
@@ -489,15 +546,15 @@ hipError_t launch_tiles(const FwdArgs &a, hipStream_t s)
         k_zero<<<(unsigned)((n4 + 255) / 256), 256, 0, s>>>((float4 *)a.comb, n4);
     }
     mark(0);
-    k_gemm<BM, C::BN1, C::WM1, C::WN1, C::BK1, C::S1, kGroupM, true, PAGED, false>
-        <<<grid(a.f / C::BN1), 64 * C::WM1 * C::WN1, 0, s>>>(a);
+    k_gemm<BM, C::BN1, C::WM1, C::WN1, C::WK1, C::BK1, C::S1, kGroupM, true, PAGED, false>
+        <<<grid(a.f / C::BN1), 64 * C::WM1 * C::WN1 * C::WK1, 0, s>>>(a);
     mark(1);
     if (a.atomic)
-        k_gemm<BM, C::BN2, C::WM2, C::WN2, C::BK2, C::S2, kGroupM, false, PAGED, true>
-            <<<grid(a.d / C::BN2), 64 * C::WM2 * C::WN2, 0, s>>>(a);
+        k_gemm<BM, C::BN2, C::WM2, C::WN2, C::WK2, C::BK2, C::S2, kGroupM, false, PAGED, true>
+            <<<grid(a.d / C::BN2), 64 * C::WM2 * C::WN2 * C::WK2, 0, s>>>(a);
     else
-        k_gemm<BM, C::BN2, C::WM2, C::WN2, C::BK2, C::S2, kGroupM, false, PAGED, false>
-            <<<grid(a.d / C::BN2), 64 * C::WM2 * C::WN2, 0, s>>>(a);
+        k_gemm<BM, C::BN2, C::WM2, C::WN2, C::WK2, C::BK2, C::S2, kGroupM, false, PAGED, false>
+            <<<grid(a.d / C::BN2), 64 * C::WM2 * C::WN2 * C::WK2, 0, s>>>(a);
     mark(2);
     const int rows = a.atomic ? 1 : a.keff;
     const int64_t nq = a.T * a.d / 4;

@@ -223,11 +223,14 @@ __device__ int wg_exclusive_scan(int v, int *s_tmp, int *total)
     return before + x - v;
 }
 
-// Given per-expert token counts cnt(e), write each expert's padded segment start
-// into seg_start[e], the block->expert map, the sentinel padding and num_padded.
-// Thread t owns expert t (E_tot <= kAlignThreads).
+// Given per-expert token counts cnt(e): each expert's padded segment start in
+// seg_start[e] (and its count in seg_cnt[e]), num_padded, then the block->expert
+// map and the sentinel padding.  The map and the padding are written by all
+// threads position by position (coalesced); a position finds its expert by a
+// binary search over the segment starts.  Thread t owns expert t for the scan
+// (E_tot <= kAlignThreads).
 template <class CountFn>
-__device__ void scan_experts(CountFn cnt, int E_tot, int BM, int n, int *seg_start, int *s_tmp,
+__device__ void scan_experts(CountFn cnt, int E_tot, int BM, int n, int *seg_start, int *seg_cnt, int *s_tmp,
                              const RouteArgs &a)
 {
     const int e = threadIdx.x;
@@ -237,13 +240,30 @@ __device__ void scan_experts(CountFn cnt, int E_tot, int BM, int n, int *seg_sta
     const int o = wg_exclusive_scan(p, s_tmp, &total);
     if (e < E_tot) {
         seg_start[e] = o;
-        for (int b = o / BM; b < (o + p) / BM; b++)
-            a.block_expert[b] = e;
-        for (int pos = o + c; pos < o + p; pos++)
-            a.sorted_ids[pos] = n;
+        seg_cnt[e] = c;
     }
     if (threadIdx.x == 0)
         *a.num_padded = total;
+    __syncthreads();
+    // last expert whose segment starts at or before pos (segments of empty experts have length 0)
+    auto owner = [&](int pos) {
+        int lo = 0, hi = E_tot - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (seg_start[mid] <= pos)
+                lo = mid;
+            else
+                hi = mid - 1;
+        }
+        return lo;
+    };
+    for (int b = threadIdx.x; b < total / BM; b += kAlignThreads)
+        a.block_expert[b] = owner(b * BM);
+    for (int pos = threadIdx.x; pos < total; pos += kAlignThreads) {
+        const int x = owner(pos);
+        if (pos - seg_start[x] >= seg_cnt[x])
+            a.sorted_ids[pos] = n;
+    }
 }
 
 // Turn per-wave counts s_cnt[w][e] into per-wave cursors starting at start(e).
@@ -264,6 +284,7 @@ struct AlignSmem {
     int32_t ids[kChunkElems];
     int cnt[kAlignWaves * kMaxExpertsTotal];
     int seg[kMaxExpertsTotal];
+    int segc[kMaxExpertsTotal];
     int tmp[kAlignWaves];
 };
 
@@ -284,7 +305,7 @@ __device__ void align_in_one_wg(AlignSmem &sm, int n, const RouteArgs &a)
             c += sm.cnt[w * a.E_tot + e];
         return c;
     };
-    scan_experts(count, a.E_tot, a.BM, n, sm.seg, sm.tmp, a);
+    scan_experts(count, a.E_tot, a.BM, n, sm.seg, sm.segc, sm.tmp, a);
     __syncthreads();
     wave_cursors([&](int e) { return sm.seg[e]; }, a.E_tot, sm.cnt);
     __syncthreads();
@@ -336,6 +357,7 @@ __global__ __launch_bounds__(kAlignThreads) void k_align_hist(const RouteArgs a)
 __global__ __launch_bounds__(kAlignThreads) void k_align_scan(const RouteArgs a, int nch)
 {
     __shared__ int seg[kMaxExpertsTotal];
+    __shared__ int segc[kMaxExpertsTotal];
     __shared__ int tmp[kAlignWaves];
     const int n = (int)(a.T * a.keff);
     auto count = [&](int e) {
@@ -344,7 +366,7 @@ __global__ __launch_bounds__(kAlignThreads) void k_align_scan(const RouteArgs a,
             c += a.counts[(int64_t)ch * a.E_tot + e];
         return c;
     };
-    scan_experts(count, a.E_tot, a.BM, n, seg, tmp, a);
+    scan_experts(count, a.E_tot, a.BM, n, seg, segc, tmp, a);
     __syncthreads();
     for (int e = threadIdx.x; e < a.E_tot; e += kAlignThreads) {
         int run = seg[e];

@@ -189,13 +189,27 @@ def test_paged_equals_contiguous_bitwise(name):
         assert torch.equal(y.view(torch.int16), yc.view(torch.int16)), f"block_m={bm}"
 
 
+# Tile heights 32..256 share one K summation order (32-wide MFMA steps in K
+# order); the 16-row decode tile splits K over four waves and adds the partial
+# sums in wave order, so it is held to the oracle tolerance instead.
+SAME_K_ORDER = (32, 64, 128, 256)
+
+
 @pytest.mark.parametrize("name", ["tiny", "qwen15"])
 def test_tile_height_does_not_change_y(name):
     c = case(name)
-    ys = [c.forward(bm)[0] for bm in BLOCK_MS]
+    ys = [c.forward(bm)[0] for bm in SAME_K_ORDER]
     torch.cuda.synchronize()
-    for bm, y in zip(BLOCK_MS[1:], ys[1:]):
+    for bm, y in zip(SAME_K_ORDER[1:], ys[1:]):
         assert torch.equal(ys[0].view(torch.int16), y.view(torch.int16)), f"block_m={bm}"
+
+
+@pytest.mark.parametrize("name,T", [("tiny", None), ("qwen15", None), ("decode", 8)])
+def test_every_tile_height_matches_oracle(name, T):
+    c = case(name, T)
+    for bm in BLOCK_MS:
+        y, _ = c.forward(bm)
+        _check_y(c, y)
 
 
 @pytest.mark.parametrize("name", ["tiny", "qwen15"])
