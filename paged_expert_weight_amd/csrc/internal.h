@@ -51,7 +51,7 @@ struct FwdArgs {
     int64_t sorted_cap, blocks_cap;
     uint16_t *y;
     uint16_t *h;  // workspace [sorted_cap][f] bf16
-    float *comb;  // workspace: [T*keff][d] (ordered) or [T][d] (atomic) fp32
+    void *comb;   // workspace: bf16 [T*keff][d] weighted partials (ordered) or fp32 [T][d] (atomic)
     bool atomic;
     hipEvent_t ev[4]; // optional: recorded before gate/up, after gate/up, after down, after combine
 };

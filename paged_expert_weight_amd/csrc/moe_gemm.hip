@@ -401,6 +401,26 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N * WK) void k_gemm(const FwdA
         g.voff[i] = off + chunk * 16u;
     }
 
+    // G2: the flat pick and routing weight of every output row this lane
+    // stores, fetched before the K loop so their latency overlaps it
+    int eflat[G::FM][4];
+    float ewt[G::FM][4];
+    if constexpr (!G1) {
+#pragma unroll
+        for (int i = 0; i < G::FM; i++)
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                const int row = g.wm * G::WM + i * 16 + 4 * g.lg + r;
+                const int flat = a.sorted_ids[b * BM + row];
+                eflat[i][r] = (flat >= 0 && flat < nflat) ? flat : -1;
+            }
+#pragma unroll
+        for (int i = 0; i < G::FM; i++)
+#pragma unroll
+            for (int r = 0; r < 4; r++)
+                ewt[i][r] = eflat[i][r] >= 0 ? a.topk_w[eflat[i][r]] : 0.f;
+    }
+
     const int KT = K / BK;
     g.run(g.kg * KT / WK, (g.kg + 1) * KT / WK);
     if (!g.reduce_k())
@@ -425,19 +445,18 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N * WK) void k_gemm(const FwdA
         for (int i = 0; i < G::FM; i++)
 #pragma unroll
             for (int r = 0; r < 4; r++) {
-                const int row = g.wm * G::WM + i * 16 + 4 * lg + r;
-                const int flat = a.sorted_ids[b * BM + row];
-                if (flat < 0 || flat >= nflat)
+                const int flat = eflat[i][r];
+                if (flat < 0)
                     continue;
-                const float wt = a.topk_w[flat];
+                const float wt = ewt[i][r];
 #pragma unroll
                 for (int j = 0; j < G::FN; j++) {
                     const int col = n0 + g.wn * G::WN + j * 16 + l16;
                     const float v = g.acc0[i][j][r] * wt;
                     if constexpr (ATOMIC)
-                        unsafeAtomicAdd(&a.comb[(int64_t)(flat / a.keff) * d + col], v);
+                        unsafeAtomicAdd(&((float *)a.comb)[(int64_t)(flat / a.keff) * d + col], v);
                     else
-                        a.comb[(int64_t)flat * d + col] = v;
+                        ((uint16_t *)a.comb)[(int64_t)flat * d + col] = f32_to_bf16(v);
                 }
             }
     }
@@ -445,8 +464,12 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N * WK) void k_gemm(const FwdA
 }
 
 // ---------------------------------------------------------------------------- combine / convert
-// y[t][c] = bf16( sum_{j < rows} comb[t*rows + j][c] ), four columns per thread.
-__global__ __launch_bounds__(256) void k_combine(const float *comb, int64_t T, int d, int rows, uint16_t *y)
+// Ordered: y[t][c] = bf16( sum_{j < keff} part[t*keff + j][c] ), the weighted
+// bf16 partial rows added in fp32 in slot order.  Atomic: y = bf16(y32).
+// Four columns per thread.
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+__global__ __launch_bounds__(256) void k_combine(const uint16_t *part, int64_t T, int d, int keff, uint16_t *y)
 {
     const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const int q = d / 4;
@@ -454,18 +477,37 @@ __global__ __launch_bounds__(256) void k_combine(const float *comb, int64_t T, i
         return;
     const int64_t t = idx / q;
     const int c = (int)(idx % q) * 4;
-    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int j = 0; j < rows; j++) {
-        const float4 v = *(const float4 *)&comb[(t * rows + j) * d + c];
-        s.x += v.x;
-        s.y += v.y;
-        s.z += v.z;
-        s.w += v.w;
+    float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+    for (int j0 = 0; j0 < keff; j0 += 4) {
+        uint2 v[4];
+#pragma unroll
+        for (int r = 0; r < 4; r++)
+            v[r] = j0 + r < keff ? *(const uint2 *)&part[(t * keff + j0 + r) * d + c] : make_uint2(0u, 0u);
+#pragma unroll
+        for (int r = 0; r < 4; r++) { // slot order; a missing slot adds +0
+            s0 += bf16_to_f32(v[r].x & 0xffffu);
+            s1 += bf16_to_f32(v[r].x >> 16);
+            s2 += bf16_to_f32(v[r].y & 0xffffu);
+            s3 += bf16_to_f32(v[r].y >> 16);
+        }
     }
     uint2 o;
-    o.x = (uint32_t)f32_to_bf16(s.x) | ((uint32_t)f32_to_bf16(s.y) << 16);
-    o.y = (uint32_t)f32_to_bf16(s.z) | ((uint32_t)f32_to_bf16(s.w) << 16);
+    o.x = (uint32_t)f32_to_bf16(s0) | ((uint32_t)f32_to_bf16(s1) << 16);
+    o.y = (uint32_t)f32_to_bf16(s2) | ((uint32_t)f32_to_bf16(s3) << 16);
     *(uint2 *)&y[t * d + c] = o;
+}
+
+__global__ __launch_bounds__(256) void k_convert(const float *y32, int64_t T, int d, uint16_t *y)
+{
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int q = d / 4;
+    if (idx >= T * q)
+        return;
+    const float4 v = *(const float4 *)&y32[idx * 4];
+    uint2 o;
+    o.x = (uint32_t)f32_to_bf16(v.x) | ((uint32_t)f32_to_bf16(v.y) << 16);
+    o.y = (uint32_t)f32_to_bf16(v.z) | ((uint32_t)f32_to_bf16(v.w) << 16);
+    *(uint2 *)&y[idx * 4] = o;
 }
 
 __global__ __launch_bounds__(256) void k_zero(float4 *p, int64_t n4)
@@ -556,9 +598,11 @@ hipError_t launch_tiles(const FwdArgs &a, hipStream_t s)
         k_gemm<BM, C::BN2, C::WM2, C::WN2, C::WK2, C::BK2, C::S2, kGroupM, false, PAGED, false>
             <<<grid(a.d / C::BN2), 64 * C::WM2 * C::WN2 * C::WK2, 0, s>>>(a);
     mark(2);
-    const int rows = a.atomic ? 1 : a.keff;
     const int64_t nq = a.T * a.d / 4;
-    k_combine<<<(unsigned)((nq + 255) / 256), 256, 0, s>>>(a.comb, a.T, a.d, rows, a.y);
+    if (a.atomic)
+        k_convert<<<(unsigned)((nq + 255) / 256), 256, 0, s>>>((const float *)a.comb, a.T, a.d, a.y);
+    else
+        k_combine<<<(unsigned)((nq + 255) / 256), 256, 0, s>>>((const uint16_t *)a.comb, a.T, a.d, a.keff, a.y);
     mark(3);
     return hipGetLastError();
 }

@@ -45,21 +45,28 @@ __device__ __forceinline__ bool beats(float va, int ia, float vb, int ib)
     return va > vb || (va == vb && ia < ib);
 }
 
-// Route one token with one wave.  Writes ids/w[0 .. k+S) and, when lds_ids is
-// not null, the ids into LDS as well.
+// Lane L's logits L, L+64, ... of one token row.
 template <int NV>
-__device__ void route_token(const float *row, int E, int k, int S, int lane, int32_t *ids, float *w,
-                            int32_t *lds_ids)
+__device__ __forceinline__ void load_logits(const float *row, int E, int lane, float (&v)[NV])
 {
-    float v[NV];
-    uint32_t taken = 0;
 #pragma unroll
     for (int i = 0; i < NV; i++) {
         const int e = lane + 64 * i;
         v[i] = e < E ? row[e] : 0.f;
-        if (e >= E)
-            taken |= 1u << i;
     }
+}
+
+// Route one token with one wave from its loaded logits.  Writes ids/w[0 .. k+S)
+// and, when lds_ids is not null, the ids into LDS as well.
+template <int NV>
+__device__ void route_token(const float (&v)[NV], int E, int k, int S, int lane, int32_t *ids, float *w,
+                            int32_t *lds_ids)
+{
+    uint32_t taken = 0;
+#pragma unroll
+    for (int i = 0; i < NV; i++)
+        if (lane + 64 * i >= E)
+            taken |= 1u << i;
     float my_v = 0.f;
     int my_id = 0;
     for (int j = 0; j < k; j++) {
@@ -115,8 +122,28 @@ __global__ __launch_bounds__(256) void k_route(const RouteArgs a)
     const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= a.T)
         return;
-    route_token<NV>(a.logits + t * a.E, a.E, a.k, a.S, lane, a.topk_ids + t * a.keff,
-                    a.topk_w + t * a.keff, nullptr);
+    float v[NV];
+    load_logits<NV>(a.logits + t * a.E, a.E, lane, v);
+    route_token<NV>(v, a.E, a.k, a.S, lane, a.topk_ids + t * a.keff, a.topk_w + t * a.keff, nullptr);
+}
+
+// dst[i] = src[i] for i < n (n <= kChunkElems): all loads of a thread are
+// issued before any of them is waited for.
+__device__ __forceinline__ void stage_ids(int32_t *dst, const int32_t *src, int n)
+{
+    constexpr int R = kChunkElems / kAlignThreads;
+    int32_t v[R];
+#pragma unroll
+    for (int r = 0; r < R; r++) {
+        const int i = threadIdx.x + r * kAlignThreads;
+        v[r] = i < n ? src[i] : 0;
+    }
+#pragma unroll
+    for (int r = 0; r < R; r++) {
+        const int i = threadIdx.x + r * kAlignThreads;
+        if (i < n)
+            dst[i] = v[r];
+    }
 }
 
 __device__ __forceinline__ void wave_range(int n, int w, int &lo, int &hi)
@@ -225,9 +252,8 @@ __device__ int wg_exclusive_scan(int v, int *s_tmp, int *total)
 
 // Given per-expert token counts cnt(e): each expert's padded segment start in
 // seg_start[e] (and its count in seg_cnt[e]), num_padded, then the block->expert
-// map and the sentinel padding.  The map and the padding are written by all
-// threads position by position (coalesced); a position finds its expert by a
-// binary search over the segment starts.  Thread t owns expert t for the scan
+// map and the sentinel padding, one wave per expert run with its lanes on
+// consecutive positions.  Thread t owns expert t for the scan
 // (E_tot <= kAlignThreads).
 template <class CountFn>
 __device__ void scan_experts(CountFn cnt, int E_tot, int BM, int n, int *seg_start, int *seg_cnt, int *s_tmp,
@@ -245,24 +271,15 @@ __device__ void scan_experts(CountFn cnt, int E_tot, int BM, int n, int *seg_sta
     if (threadIdx.x == 0)
         *a.num_padded = total;
     __syncthreads();
-    // last expert whose segment starts at or before pos (segments of empty experts have length 0)
-    auto owner = [&](int pos) {
-        int lo = 0, hi = E_tot - 1;
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (seg_start[mid] <= pos)
-                lo = mid;
-            else
-                hi = mid - 1;
-        }
-        return lo;
-    };
-    for (int b = threadIdx.x; b < total / BM; b += kAlignThreads)
-        a.block_expert[b] = owner(b * BM);
-    for (int pos = threadIdx.x; pos < total; pos += kAlignThreads) {
-        const int x = owner(pos);
-        if (pos - seg_start[x] >= seg_cnt[x])
-            a.sorted_ids[pos] = n;
+    // each wave takes whole experts; its lanes write consecutive positions
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    for (int x = w; x < E_tot; x += kAlignWaves) {
+        const int ox = seg_start[x], cx = seg_cnt[x];
+        const int px = (cx + BM - 1) / BM * BM;
+        for (int i = lane; i < px - cx; i += 64)
+            a.sorted_ids[ox + cx + i] = n;
+        for (int i = lane; i < px / BM; i += 64)
+            a.block_expert[ox / BM + i] = x;
     }
 }
 
@@ -318,9 +335,23 @@ __global__ __launch_bounds__(kAlignThreads) void k_route_align_small(const Route
     __shared__ AlignSmem sm;
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
     zero_counts(sm, a.E_tot);
-    for (int t = w; t < (int)a.T; t += kAlignWaves)
-        route_token<NV>(a.logits + (int64_t)t * a.E, a.E, a.k, a.S, lane, a.topk_ids + (int64_t)t * a.keff,
-                        a.topk_w + (int64_t)t * a.keff, sm.ids + t * a.keff);
+    // this wave's tokens w, w+16, ... (at most kSmallTokens/kAlignWaves): load
+    // all their logits first, then route them
+    constexpr int TPW = kSmallTokens / kAlignWaves;
+    float v[TPW][NV];
+#pragma unroll
+    for (int r = 0; r < TPW; r++) {
+        const int t = w + r * kAlignWaves;
+        if (t < (int)a.T)
+            load_logits<NV>(a.logits + (int64_t)t * a.E, a.E, lane, v[r]);
+    }
+#pragma unroll
+    for (int r = 0; r < TPW; r++) {
+        const int t = w + r * kAlignWaves;
+        if (t < (int)a.T)
+            route_token<NV>(v[r], a.E, a.k, a.S, lane, a.topk_ids + (int64_t)t * a.keff,
+                            a.topk_w + (int64_t)t * a.keff, sm.ids + t * a.keff);
+    }
     __syncthreads();
     align_in_one_wg(sm, (int)a.T * a.keff, a);
 }
@@ -330,8 +361,7 @@ __global__ __launch_bounds__(kAlignThreads) void k_align_single(const RouteArgs 
     __shared__ AlignSmem sm;
     const int n = (int)a.T * a.keff;
     zero_counts(sm, a.E_tot);
-    for (int i = threadIdx.x; i < n; i += kAlignThreads)
-        sm.ids[i] = a.topk_ids[i];
+    stage_ids(sm.ids, a.topk_ids, n);
     __syncthreads();
     align_in_one_wg(sm, n, a);
 }
@@ -344,9 +374,18 @@ __global__ __launch_bounds__(kAlignThreads) void k_align_hist(const RouteArgs a)
     const int cn = (int)min((int64_t)kChunkElems, n - lo);
     for (int e = threadIdx.x; e < a.E_tot; e += kAlignThreads)
         hist[e] = 0;
+    constexpr int R = kChunkElems / kAlignThreads;
+    int32_t v[R];
+#pragma unroll
+    for (int r = 0; r < R; r++) {
+        const int i = threadIdx.x + r * kAlignThreads;
+        v[r] = i < cn ? a.topk_ids[lo + i] : -1;
+    }
     __syncthreads();
-    for (int i = threadIdx.x; i < cn; i += kAlignThreads)
-        atomicAdd(&hist[a.topk_ids[lo + i]], 1);
+#pragma unroll
+    for (int r = 0; r < R; r++)
+        if (v[r] >= 0)
+            atomicAdd(&hist[v[r]], 1);
     __syncthreads();
     for (int e = threadIdx.x; e < a.E_tot; e += kAlignThreads)
         a.counts[(int64_t)blockIdx.x * a.E_tot + e] = hist[e];
@@ -360,20 +399,35 @@ __global__ __launch_bounds__(kAlignThreads) void k_align_scan(const RouteArgs a,
     __shared__ int segc[kMaxExpertsTotal];
     __shared__ int tmp[kAlignWaves];
     const int n = (int)(a.T * a.keff);
+    // column e of counts[nch][E_tot], 8 loads in flight at a time
     auto count = [&](int e) {
         int c = 0;
-        for (int ch = 0; ch < nch; ch++)
-            c += a.counts[(int64_t)ch * a.E_tot + e];
+        for (int ch0 = 0; ch0 < nch; ch0 += 8) {
+            int v[8];
+#pragma unroll
+            for (int r = 0; r < 8; r++)
+                v[r] = ch0 + r < nch ? a.counts[(int64_t)(ch0 + r) * a.E_tot + e] : 0;
+#pragma unroll
+            for (int r = 0; r < 8; r++)
+                c += v[r];
+        }
         return c;
     };
     scan_experts(count, a.E_tot, a.BM, n, seg, segc, tmp, a);
     __syncthreads();
     for (int e = threadIdx.x; e < a.E_tot; e += kAlignThreads) {
         int run = seg[e];
-        for (int ch = 0; ch < nch; ch++) {
-            const int c = a.counts[(int64_t)ch * a.E_tot + e];
-            a.counts[(int64_t)ch * a.E_tot + e] = run;
-            run += c;
+        for (int ch0 = 0; ch0 < nch; ch0 += 8) {
+            int v[8];
+#pragma unroll
+            for (int r = 0; r < 8; r++)
+                v[r] = ch0 + r < nch ? a.counts[(int64_t)(ch0 + r) * a.E_tot + e] : 0;
+#pragma unroll
+            for (int r = 0; r < 8; r++) {
+                if (ch0 + r < nch)
+                    a.counts[(int64_t)(ch0 + r) * a.E_tot + e] = run;
+                run += v[r];
+            }
         }
     }
 }
@@ -385,8 +439,7 @@ __global__ __launch_bounds__(kAlignThreads) void k_align_scatter(const RouteArgs
     const int64_t lo = (int64_t)blockIdx.x * kChunkElems;
     const int cn = (int)min((int64_t)kChunkElems, n - lo);
     zero_counts(sm, a.E_tot);
-    for (int i = threadIdx.x; i < cn; i += kAlignThreads)
-        sm.ids[i] = a.topk_ids[lo + i];
+    stage_ids(sm.ids, a.topk_ids + lo, cn);
     __syncthreads();
     chunk_hist(sm.ids, cn, a.E_tot, sm.cnt);
     __syncthreads();

@@ -113,7 +113,7 @@ Sizes sizes_for(const moe_pool *p, int64_t T, int bm, uint32_t flags)
     const size_t counts = (size_t)pmoe::route_workspace_bytes(T, p->keff, p->E_tot);
     const size_t h = (size_t)s.sorted_cap * p->desc.f * 2;
     const size_t comb = (flags & MOE_FLAG_ATOMIC_COMBINE) ? (size_t)T * p->desc.d * 4
-                                                          : (size_t)s.n * p->desc.d * 4;
+                                                          : (size_t)s.n * p->desc.d * 2;
     s.off_counts = 0;
     s.off_h = up256(counts);
     s.off_comb = s.off_h + up256(h);
@@ -201,7 +201,7 @@ int forward_common(const moe_pool *p, const void *w13, const void *w2, bool page
     a.blocks_cap = sz.blocks_cap;
     a.y = (uint16_t *)y;
     a.h = (uint16_t *)((char *)ws + sz.off_h);
-    a.comb = (float *)((char *)ws + sz.off_comb);
+    a.comb = (char *)ws + sz.off_comb;
     a.atomic = (flags & MOE_FLAG_ATOMIC_COMBINE) != 0;
     if (ev)
         for (int i = 0; i < 4; i++)
