@@ -1,9 +1,9 @@
 // Top-k softmax routing and token alignment (gfx950, wave64).
 //
 // Routing: one wave per token.  Lane L holds logits L, L+64, ...; each of the k
-// rounds takes a lane-local best, then a butterfly max over the wave with a
-// strict total order (larger logit first, equal logits to the lower id), so all
-// lanes agree on the winner.  Lane j keeps pick j; the weights are the softmax
+// rounds takes a lane-local best, then a butterfly max over the wave (DPP and
+// lane-swap steps, no LDS) with a strict total order (larger logit first, equal
+// logits to the lower id), so all lanes agree on the winner.  Lane j keeps pick j; the weights are the softmax
 // of the k picks renormalised over them, exp(l_j - l_0) / sum_i exp(l_i - l_0),
 // in fp32.  A shared expert (id E, weight 1) is appended as pick k.  The pages
 // do not print a routing rule; this is the top-k softmax router of the MoE layer
@@ -45,6 +45,77 @@ __device__ __forceinline__ bool beats(float va, int ia, float vb, int ib)
     return va > vb || (va == vb && ia < ib);
 }
 
+// Cross-lane exchange without the LDS crossbar.  Within a row of 16 lanes:
+// DPP quad_perm [1,0,3,2] (lane ^ 1), quad_perm [2,3,0,1] (lane ^ 2),
+// row_half_mirror (lane i <-> 7-i of its 8) and row_mirror (i <-> 15-i).
+// Across rows: v_permlane16_swap / v_permlane32_swap, which hand every lane the
+// value of lane ^ 16 / lane ^ 32 in one of their two results.  Applied in this
+// order, each step pairs every lane with a lane of the other half of the group
+// the previous steps made uniform, so a commutative, associative combine ends
+// with the same result in all 64 lanes.
+template <int CTRL>
+__device__ __forceinline__ int dpp(int v)
+{
+    return __builtin_amdgcn_update_dpp(v, v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v)
+{
+    return __builtin_bit_cast(float, dpp<CTRL>(__builtin_bit_cast(int, v)));
+}
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+
+__device__ __forceinline__ int xor16(int v, int lane)
+{
+    const auto r = __builtin_amdgcn_permlane16_swap((unsigned)v, (unsigned)v, false, false);
+    return (int)(((lane >> 4) & 1) ? r[0] : r[1]);
+}
+__device__ __forceinline__ int xor32(int v, int lane)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap((unsigned)v, (unsigned)v, false, false);
+    return (int)(lane >= 32 ? r[0] : r[1]);
+}
+__device__ __forceinline__ float xor16(float v, int lane)
+{
+    return __builtin_bit_cast(float, xor16(__builtin_bit_cast(int, v), lane));
+}
+__device__ __forceinline__ float xor32(float v, int lane)
+{
+    return __builtin_bit_cast(float, xor32(__builtin_bit_cast(int, v), lane));
+}
+
+// (value, id) of the best pick over the wave (beats order), in every lane.
+__device__ __forceinline__ void wave_best(float &bv, int &bi, int lane)
+{
+#define PMOE_BEST_STEP(GETV, GETI)                                                                 \
+    {                                                                                              \
+        const float ov = GETV;                                                                     \
+        const int oi = GETI;                                                                       \
+        if (beats(ov, oi, bv, bi)) {                                                               \
+            bv = ov;                                                                               \
+            bi = oi;                                                                               \
+        }                                                                                          \
+    }
+    PMOE_BEST_STEP(dpp<kDppXor1>(bv), dpp<kDppXor1>(bi))
+    PMOE_BEST_STEP(dpp<kDppXor2>(bv), dpp<kDppXor2>(bi))
+    PMOE_BEST_STEP(dpp<kDppHalfMirror>(bv), dpp<kDppHalfMirror>(bi))
+    PMOE_BEST_STEP(dpp<kDppMirror>(bv), dpp<kDppMirror>(bi))
+    PMOE_BEST_STEP(xor16(bv, lane), xor16(bi, lane))
+    PMOE_BEST_STEP(xor32(bv, lane), xor32(bi, lane))
+#undef PMOE_BEST_STEP
+}
+
+__device__ __forceinline__ float wave_sum(float x, int lane)
+{
+    x += dpp<kDppXor1>(x);
+    x += dpp<kDppXor2>(x);
+    x += dpp<kDppHalfMirror>(x);
+    x += dpp<kDppMirror>(x);
+    x += xor16(x, lane);
+    x += xor32(x, lane);
+    return x;
+}
+
 // Lane L's logits L, L+64, ... of one token row.
 template <int NV>
 __device__ __forceinline__ void load_logits(const float *row, int E, int lane, float (&v)[NV])
@@ -79,15 +150,7 @@ __device__ void route_token(const float (&v)[NV], int E, int k, int S, int lane,
                 bi = lane + 64 * i;
             }
         }
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) {
-            const float ov = __shfl_xor(bv, off);
-            const int oi = __shfl_xor(bi, off);
-            if (beats(ov, oi, bv, bi)) {
-                bv = ov;
-                bi = oi;
-            }
-        }
+        wave_best(bv, bi, lane);
         if (bi >= 0 && (bi & 63) == lane)
             taken |= 1u << (bi >> 6);
         if (lane == j) {
@@ -95,12 +158,9 @@ __device__ void route_token(const float (&v)[NV], int E, int k, int S, int lane,
             my_id = bi;
         }
     }
-    const float lmax = __shfl(my_v, 0);
+    const float lmax = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, my_v)));
     const float ex = lane < k ? expf(my_v - lmax) : 0.f;
-    float sum = ex;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1)
-        sum += __shfl_xor(sum, off); // commutative pairs: every lane ends with the same sum
+    const float sum = wave_sum(ex, lane); // commutative pairs: every lane ends with the same sum
     if (lane < k) {
         ids[lane] = my_id;
         w[lane] = ex / sum;
