@@ -30,6 +30,11 @@ sys.path.insert(0, ROOT)
 
 METRIC = "paged fused-MoE TFLOP/s & HBM GB/s (%roofline) + overhead vs contiguous"
 HBM_PEAK_GBS = 8000.0
+# HBM bytes per k_gemm1 launch measured with rocprofv3 (FETCH_SIZE scaled by 2.0, the factor a
+# 1 GiB copy reads back, plus WRITE_SIZE), keyed by workload, T, block_m, atomic combine and a
+# hash of the GEMM sources the counters were taken on.  Reported only while that hash matches.
+MEASURED_TRAFFIC = {("qwen15", 1024, 128, False, "c6359423c8c69943"): 773920425}
+GEMM_SOURCES = ("paged_expert_weight_amd/csrc/moe_gemm.hip", "paged_expert_weight_amd/csrc/internal.h")
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 MALL_BYTES = 256 << 20
 
@@ -43,6 +48,20 @@ WORKLOAD_TEXT = {
     "qwen3n": "Qwen3-Next-80B-A3B-shaped MoE layer T=8192 d=2048 f=512 E=512 top-10 + 1 shared expert, "
               "Zipf(1.1) routing; pool of 2 MiB pages interleaved with 16-token KV pages; 64 experts via load buffer",
 }
+
+
+def gemm_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    root = os.path.dirname(os.path.abspath(__file__))
+    for p in GEMM_SOURCES:
+        with open(os.path.join(root, p), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(name, T, bm, atomic):
+    return MEASURED_TRAFFIC.get((name, T, bm, bool(atomic), gemm_source_hash()))
 
 
 def parse():
@@ -82,8 +101,9 @@ def main():
         copy_calibration()
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: the layer's hot path runs on a single MI355X and this build "
-              "has no multi-GPU path (see DESIGN.md for how it would shard). Use --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU: the layer's hot path runs on a single MI355X and there is no "
+              "multi-GPU path (experts would shard across GPUs with an all-to-all of routed tokens, not "
+              "implemented here). Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
@@ -211,7 +231,7 @@ def main():
         roof = {"bound": "mfma", "achieved": round(g1_flops / g1_s / 1e12, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = None
+    roof["traffic"] = measured_traffic(name, T, bm, args.atomic)
     roof["kernel"] = "k_gemm1 (paged gate/up GEMM + SiLU*mul)"
     roof["avg_launch_us"] = round(stage_us[0], 2)
     roof["algorithmic_bytes_per_launch"] = int(g1_bytes)

@@ -5,8 +5,7 @@ the layer's arithmetic (no routing, no sorting, no address formula, no FFN).
 Both the CPU oracle and the HIP path take their inputs from here.
 
 Workloads (shapes and distributions follow the five layer configurations the
-Rimuru digest's kernel section is evaluated against, see the design doc for the
-recipe):
+Rimuru digest's kernel section is evaluated against):
 
   tiny     T=16,   d=128,  f=64,    E=8,   k=2        uniform logits
   qwen15   T=1024, d=2048, f=1408,  E=60,  k=4        uniform logits
