@@ -130,13 +130,15 @@ __device__ __forceinline__ int block_owner(const FwdArgs &a, int b)
 // LDS, lane L at byte 16*L.  A lane therefore picks which global 16-byte chunk
 // lands in its LDS slot; chunk c of row r is stored at position
 // c ^ swz(r) of that row, so that the 16-byte MFMA operand reads of 8
-// consecutive rows at one chunk index hit 8 different 16-byte bank groups.
+// consecutive rows at one chunk index hit 8 different 16-byte bank groups
+// (rows of 128 or 256 bytes: swz = r mod 8; rows of 64 bytes hold two rows
+// per 128-byte bank line: swz = (r / 2) mod 4).
 template <int BK>
 struct StageGeom {
     static constexpr int ROWB = BK * 2;          // bytes per row
     static constexpr int CH = BK / 8;            // 16-byte chunks per row
     static constexpr int ROWS_PER_LD = 64 / CH;  // rows one DMA instruction covers
-    __device__ static __forceinline__ int swz(int r) { return CH == 8 ? (r & 7) : ((r >> 1) & 3); }
+    __device__ static __forceinline__ int swz(int r) { return CH >= 8 ? (r & 7) : ((r >> 1) & 3); }
 };
 
 template <int N>
@@ -402,10 +404,12 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N * WK) void k_gemm(const FwdA
     }
 
     // G2: the flat pick and routing weight of every output row this lane
-    // stores, fetched before the K loop so their latency overlaps it
+    // stores.  Small wave tiles fetch them before the K loop so their latency
+    // overlaps it; large ones (whose accumulators fill the register file, and
+    // whose K loop is long) fetch them after it.
     int eflat[G::FM][4];
     float ewt[G::FM][4];
-    if constexpr (!G1) {
+    auto epilogue_rows = [&]() {
 #pragma unroll
         for (int i = 0; i < G::FM; i++)
 #pragma unroll
@@ -419,12 +423,17 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N * WK) void k_gemm(const FwdA
 #pragma unroll
             for (int r = 0; r < 4; r++)
                 ewt[i][r] = eflat[i][r] >= 0 ? a.topk_w[eflat[i][r]] : 0.f;
-    }
+    };
+    constexpr bool kPrefetchRows = !G1 && G::FM <= 4;
+    if constexpr (kPrefetchRows)
+        epilogue_rows();
 
     const int KT = K / BK;
     g.run(g.kg * KT / WK, (g.kg + 1) * KT / WK);
     if (!g.reduce_k())
         return;
+    if constexpr (!G1 && !kPrefetchRows)
+        epilogue_rows();
 
     const int lg = g.lg, l16 = g.l16;
     if constexpr (G1) {
@@ -562,8 +571,9 @@ using Tiles16 = Tiles<16, 16, 1, 1, 4, 64, 3, 16, 1, 1, 4, 64, 3>;
 using Tiles32 = Tiles<32, 32, 1, 2, 1, 64, 2, 32, 1, 2, 1, 64, 2>;
 using Tiles64 = Tiles<64, 64, 2, 2, 1, 64, 2, 64, 2, 2, 1, 64, 2>;
 using Tiles128 = Tiles<128, 64, 2, 2, 1, 64, 2, 128, 2, 2, 1, 64, 2>;
-// large blocks: 8 waves, 64x(64+64) wave tiles for the MFMA-bound shapes
-using Tiles256 = Tiles<256, 128, 4, 2, 1, 64, 2, 128, 4, 2, 1, 64, 2>;
+// large blocks (MFMA-bound shapes): 8 waves, two per SIMD, each with a 64x128
+// accumulator tile (gate/up: 64 x (64 gate + 64 up)); 256x256 down tiles
+using Tiles256 = Tiles<256, 128, 4, 2, 1, 32, 4, 256, 4, 2, 1, 32, 4>;
 using Tiles256n = Tiles<256, 64, 4, 2, 1, 32, 4, 64, 4, 1, 1, 32, 4>; // when f or d is not a multiple of 128
 
 constexpr int kGroupM = 4;
