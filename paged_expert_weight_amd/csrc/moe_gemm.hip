@@ -98,21 +98,41 @@ __device__ __forceinline__ const uint16_t *down_base(const FwdArgs &a, int e)
 // exit.  Tiles are grouped GM blocks at a time, column-tile major inside a
 // group: the GM blocks of a group reuse each weight tile from L2, and each
 // block's activation rows are reused across the group's column tiles.
+struct TileSpace {
+    int blocks, total, per_xcd; // blocks of BM rows, (block, column tile) pairs, pairs per XCD range
+};
+
+__device__ __forceinline__ TileSpace tile_space(const FwdArgs &a, int BM, int ntiles)
+{
+    TileSpace t;
+    t.blocks = *a.num_padded / BM;
+    const int cap = (int)(a.sorted_cap / BM);
+    t.blocks = t.blocks < cap ? t.blocks : cap;
+    t.total = t.blocks * ntiles;
+    t.per_xcd = (t.total + 7) / 8;
+    return t;
+}
+
+// Logical tile u -> (block b, column tile nt): groups of GM blocks, column-tile
+// major inside a group.
+template <int GM>
+__device__ __forceinline__ void tile_at(const TileSpace &t, int ntiles, int u, int &b, int &nt)
+{
+    const int g = u / (GM * ntiles), r = u % (GM * ntiles);
+    const int gm = min(GM, t.blocks - g * GM);
+    nt = r / gm;
+    b = g * GM + r % gm;
+}
+
+// One tile per workgroup: workgroup i takes tile (i mod 8) * per_xcd + i / 8.
 template <int GM>
 __device__ __forceinline__ bool tile_of(const FwdArgs &a, int BM, int ntiles, int &b, int &nt)
 {
-    int blocks = *a.num_padded / BM;
-    const int cap = (int)(a.sorted_cap / BM);
-    blocks = blocks < cap ? blocks : cap;
-    const int total = blocks * ntiles;
-    const int per_xcd = (total + 7) / 8;
-    const int u = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
-    if ((int)(blockIdx.x / 8) >= per_xcd || u >= total)
+    const TileSpace t = tile_space(a, BM, ntiles);
+    const int u = (int)(blockIdx.x % 8) * t.per_xcd + (int)(blockIdx.x / 8);
+    if ((int)(blockIdx.x / 8) >= t.per_xcd || u >= t.total)
         return false;
-    const int g = u / (GM * ntiles), r = u % (GM * ntiles);
-    const int gm = min(GM, blocks - g * GM);
-    nt = r / gm;
-    b = g * GM + r % gm;
+    tile_at<GM>(t, ntiles, u, b, nt);
     return true;
 }
 
@@ -252,11 +272,12 @@ struct Gemm {
     }
 
     template <int J>
-    __device__ __forceinline__ void prologue(int kb)
+    __device__ __forceinline__ void prologue(int kb, int ke)
     {
         if constexpr (J < S - 1) {
-            this->template issue<J>(kb + J);
-            this->template prologue<J + 1>(kb);
+            if (kb + J < ke)
+                this->template issue<J>(kb + J);
+            this->template prologue<J + 1>(kb, ke);
         }
     }
 
@@ -268,12 +289,18 @@ struct Gemm {
             const int kt = kt0 + J;
             // stage kt has landed for this wave and this wave's reads of the
             // stage about to be refilled are done; then the same for every
-            // wave that shares the stages
-            wait_vm_lgkm0(Int<(S - 2) * IPW>{});
+            // wave that shares the stages.  Only steps inside [kb, ke) are
+            // loaded, so near the end fewer later stages are in flight and
+            // the wait drains them all.
+            if (kt + S - 2 < ke)
+                wait_vm_lgkm0(Int<(S - 2) * IPW>{});
+            else
+                wait_vm_lgkm0(Int<0>{});
             if constexpr (NT > 1)
                 __builtin_amdgcn_s_barrier();
             constexpr int NEXT = (J + S - 1) % S;
-            this->template issue<NEXT>(kt + S - 1);
+            if (kt + S - 1 < ke)
+                this->template issue<NEXT>(kt + S - 1);
             if (kt < ke)
                 this->template compute<J>();
             this->template steps<J + 1>(kt0, ke);
@@ -290,7 +317,7 @@ struct Gemm {
                 acc0[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
                 acc1[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
             }
-        this->template prologue<0>(kb);
+        this->template prologue<0>(kb, ke);
         for (int kt0 = kb; kt0 < ke; kt0 += S)
             this->template steps<0>(kt0, ke);
         wait_vm_lgkm0(Int<0>{}); // no DMA may still be writing this workgroup's LDS when it exits
@@ -339,29 +366,14 @@ struct Gemm {
     }
 };
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int WK, int BK, int S, int GM, bool G1, bool PAGED, bool ATOMIC>
-__global__ __launch_bounds__(64 * WAVES_M * WAVES_N * WK) void k_gemm(const FwdArgs a)
+// One output tile (block b, column tile nt) of a grouped GEMM.
+template <int BM, int BN, int WAVES_M, int WAVES_N, int WK, int BK, int S, bool G1, bool PAGED, bool ATOMIC>
+__device__ __forceinline__ void gemm_tile(const FwdArgs &a, Gemm<BM, BN, WAVES_M, WAVES_N, WK, BK, S, G1> &g, int b,
+                                          int nt)
 {
-    // The host pass only needs this kernel's signature (for its launch stub);
-    // the pipeline's gfx950 builtins are compiled in the device pass.
-#if defined(__HIP_DEVICE_COMPILE__)
     using G = Gemm<BM, BN, WAVES_M, WAVES_N, WK, BK, S, G1>;
     using Geo = typename G::Geo;
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[G::LDS_BYTES];
-    G g;
-    g.lds = lds;
-    const int tid = threadIdx.x, lane = tid & 63;
-    g.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    g.wt = g.wave % G::NT;  // wave within the tile
-    g.kg = g.wave / G::NT;  // K range of this wave
-    g.wm = g.wt / WAVES_N;
-    g.wn = g.wt % WAVES_N;
-    g.l16 = lane & 15;
-    g.lg = lane >> 4;
-    const int ntiles = (G1 ? a.f : a.d) / BN;
-    int b, nt;
-    if (!tile_of<GM>(a, BM, ntiles, b, nt))
-        return;
+    const int lane = threadIdx.x & 63;
     const int e = block_owner(a, b);
     if (e < 0)
         return;
@@ -469,6 +481,30 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N * WK) void k_gemm(const FwdA
                 }
             }
     }
+}
+
+template <int BM, int BN, int WAVES_M, int WAVES_N, int WK, int BK, int S, int GM, bool G1, bool PAGED, bool ATOMIC>
+__global__ __launch_bounds__(64 * WAVES_M * WAVES_N * WK) void k_gemm(const FwdArgs a)
+{
+    // The host pass only needs this kernel's signature (for its launch stub);
+    // the pipeline's gfx950 builtins are compiled in the device pass.
+#if defined(__HIP_DEVICE_COMPILE__)
+    using G = Gemm<BM, BN, WAVES_M, WAVES_N, WK, BK, S, G1>;
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[G::LDS_BYTES];
+    G g;
+    g.lds = lds;
+    const int tid = threadIdx.x, lane = tid & 63;
+    g.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    g.wt = g.wave % G::NT;  // wave within the tile
+    g.kg = g.wave / G::NT;  // K range of this wave
+    g.wm = g.wt / WAVES_N;
+    g.wn = g.wt % WAVES_N;
+    g.l16 = lane & 15;
+    g.lg = lane >> 4;
+    int b, nt;
+    if (!tile_of<GM>(a, BM, (G1 ? a.f : a.d) / BN, b, nt))
+        return;
+    gemm_tile<BM, BN, WAVES_M, WAVES_N, WK, BK, S, G1, PAGED, ATOMIC>(a, g, b, nt);
 #endif
 }
 
@@ -578,8 +614,8 @@ using Tiles256n = Tiles<256, 64, 4, 2, 1, 32, 4, 64, 4, 1, 1, 32, 4>; // when f 
 
 constexpr int kGroupM = 4;
 
-template <class C, bool PAGED>
-hipError_t launch_tiles(const FwdArgs &a, hipStream_t s)
+template <class C, bool PAGED, bool ATOMIC>
+hipError_t launch_tiles_t(const FwdArgs &a, hipStream_t s)
 {
     constexpr int BM = C::BM;
     const int64_t n = a.T * a.keff;
@@ -593,7 +629,7 @@ hipError_t launch_tiles(const FwdArgs &a, hipStream_t s)
             (void)hipEventRecord(a.ev[i], s);
     };
     auto grid = [&](int ntiles) { return (unsigned)((grid_m * ntiles + 7) / 8 * 8); };
-    if (a.atomic) {
+    if (ATOMIC) {
         const int64_t n4 = a.T * a.d / 4;
         k_zero<<<(unsigned)((n4 + 255) / 256), 256, 0, s>>>((float4 *)a.comb, n4);
     }
@@ -601,20 +637,22 @@ hipError_t launch_tiles(const FwdArgs &a, hipStream_t s)
     k_gemm<BM, C::BN1, C::WM1, C::WN1, C::WK1, C::BK1, C::S1, kGroupM, true, PAGED, false>
         <<<grid(a.f / C::BN1), 64 * C::WM1 * C::WN1 * C::WK1, 0, s>>>(a);
     mark(1);
-    if (a.atomic)
-        k_gemm<BM, C::BN2, C::WM2, C::WN2, C::WK2, C::BK2, C::S2, kGroupM, false, PAGED, true>
-            <<<grid(a.d / C::BN2), 64 * C::WM2 * C::WN2 * C::WK2, 0, s>>>(a);
-    else
-        k_gemm<BM, C::BN2, C::WM2, C::WN2, C::WK2, C::BK2, C::S2, kGroupM, false, PAGED, false>
-            <<<grid(a.d / C::BN2), 64 * C::WM2 * C::WN2 * C::WK2, 0, s>>>(a);
+    k_gemm<BM, C::BN2, C::WM2, C::WN2, C::WK2, C::BK2, C::S2, kGroupM, false, PAGED, ATOMIC>
+        <<<grid(a.d / C::BN2), 64 * C::WM2 * C::WN2 * C::WK2, 0, s>>>(a);
     mark(2);
     const int64_t nq = a.T * a.d / 4;
-    if (a.atomic)
+    if (ATOMIC)
         k_convert<<<(unsigned)((nq + 255) / 256), 256, 0, s>>>((const float *)a.comb, a.T, a.d, a.y);
     else
         k_combine<<<(unsigned)((nq + 255) / 256), 256, 0, s>>>((const uint16_t *)a.comb, a.T, a.d, a.keff, a.y);
     mark(3);
     return hipGetLastError();
+}
+
+template <class C, bool PAGED>
+hipError_t launch_tiles(const FwdArgs &a, hipStream_t s)
+{
+    return a.atomic ? launch_tiles_t<C, PAGED, true>(a, s) : launch_tiles_t<C, PAGED, false>(a, s);
 }
 
 template <bool PAGED>
