@@ -603,7 +603,7 @@ struct Tiles {
     static constexpr int BN2 = BN2_, WM2 = WM2_, WN2 = WN2_, WK2 = WK2_, BK2 = BK2_, S2 = S2_;
 };
 // decode-sized blocks: one wave per 16x16 tile, four waves splitting K (many bytes in flight)
-using Tiles16 = Tiles<16, 16, 1, 1, 4, 64, 3, 16, 1, 1, 4, 64, 3>;
+using Tiles16 = Tiles<16, 16, 1, 1, 4, 64, 3, 32, 1, 1, 2, 64, 4>;
 using Tiles32 = Tiles<32, 32, 1, 2, 1, 64, 2, 32, 1, 2, 1, 64, 2>;
 using Tiles64 = Tiles<64, 64, 2, 2, 1, 64, 2, 64, 2, 2, 1, 64, 2>;
 using Tiles128 = Tiles<128, 64, 2, 2, 1, 64, 2, 128, 2, 2, 1, 64, 2>;

@@ -31,6 +31,17 @@
 namespace pmoe {
 namespace {
 
+// Workgroup barrier that orders LDS only.  Nothing these kernels store to
+// global memory is read back by another thread of the same launch, so the
+// barriers need not wait for global stores to complete (a full __syncthreads
+// would, costing a memory round trip at every phase).
+__device__ __forceinline__ void lds_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 constexpr int kAlignWaves = 16;
 constexpr int kAlignThreads = 64 * kAlignWaves;
 constexpr int kChunkElems = 8192; // flat entries per alignment workgroup
@@ -298,14 +309,14 @@ __device__ int wg_exclusive_scan(int v, int *s_tmp, int *total)
     }
     if (lane == 63)
         s_tmp[w] = x;
-    __syncthreads();
+    lds_sync();
     int before = 0, all = 0;
     for (int i = 0; i < kAlignWaves; i++) {
         const int s = s_tmp[i];
         before += i < w ? s : 0;
         all += s;
     }
-    __syncthreads();
+    lds_sync();
     *total = all;
     return before + x - v;
 }
@@ -330,7 +341,7 @@ __device__ void scan_experts(CountFn cnt, int E_tot, int BM, int n, int *seg_sta
     }
     if (threadIdx.x == 0)
         *a.num_padded = total;
-    __syncthreads();
+    lds_sync();
     // each wave takes whole experts; its lanes write consecutive positions
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
     for (int x = w; x < E_tot; x += kAlignWaves) {
@@ -375,7 +386,7 @@ __device__ void zero_counts(AlignSmem &sm, int E_tot)
 __device__ void align_in_one_wg(AlignSmem &sm, int n, const RouteArgs &a)
 {
     chunk_hist(sm.ids, n, a.E_tot, sm.cnt);
-    __syncthreads();
+    lds_sync();
     auto count = [&](int e) {
         int c = 0;
         for (int w = 0; w < kAlignWaves; w++)
@@ -383,9 +394,9 @@ __device__ void align_in_one_wg(AlignSmem &sm, int n, const RouteArgs &a)
         return c;
     };
     scan_experts(count, a.E_tot, a.BM, n, sm.seg, sm.segc, sm.tmp, a);
-    __syncthreads();
+    lds_sync();
     wave_cursors([&](int e) { return sm.seg[e]; }, a.E_tot, sm.cnt);
-    __syncthreads();
+    lds_sync();
     chunk_scatter(sm.ids, n, 0, a.E_tot, sm.cnt, a.sorted_ids);
 }
 
@@ -412,7 +423,7 @@ __global__ __launch_bounds__(kAlignThreads) void k_route_align_small(const Route
             route_token<NV>(v[r], a.E, a.k, a.S, lane, a.topk_ids + (int64_t)t * a.keff,
                             a.topk_w + (int64_t)t * a.keff, sm.ids + t * a.keff);
     }
-    __syncthreads();
+    lds_sync();
     align_in_one_wg(sm, (int)a.T * a.keff, a);
 }
 
@@ -422,7 +433,7 @@ __global__ __launch_bounds__(kAlignThreads) void k_align_single(const RouteArgs 
     const int n = (int)a.T * a.keff;
     zero_counts(sm, a.E_tot);
     stage_ids(sm.ids, a.topk_ids, n);
-    __syncthreads();
+    lds_sync();
     align_in_one_wg(sm, n, a);
 }
 
@@ -441,12 +452,12 @@ __global__ __launch_bounds__(kAlignThreads) void k_align_hist(const RouteArgs a)
         const int i = threadIdx.x + r * kAlignThreads;
         v[r] = i < cn ? a.topk_ids[lo + i] : -1;
     }
-    __syncthreads();
+    lds_sync();
 #pragma unroll
     for (int r = 0; r < R; r++)
         if (v[r] >= 0)
             atomicAdd(&hist[v[r]], 1);
-    __syncthreads();
+    lds_sync();
     for (int e = threadIdx.x; e < a.E_tot; e += kAlignThreads)
         a.counts[(int64_t)blockIdx.x * a.E_tot + e] = hist[e];
 }
@@ -474,7 +485,7 @@ __global__ __launch_bounds__(kAlignThreads) void k_align_scan(const RouteArgs a,
         return c;
     };
     scan_experts(count, a.E_tot, a.BM, n, seg, segc, tmp, a);
-    __syncthreads();
+    lds_sync();
     for (int e = threadIdx.x; e < a.E_tot; e += kAlignThreads) {
         int run = seg[e];
         for (int ch0 = 0; ch0 < nch; ch0 += 8) {
@@ -500,12 +511,12 @@ __global__ __launch_bounds__(kAlignThreads) void k_align_scatter(const RouteArgs
     const int cn = (int)min((int64_t)kChunkElems, n - lo);
     zero_counts(sm, a.E_tot);
     stage_ids(sm.ids, a.topk_ids + lo, cn);
-    __syncthreads();
+    lds_sync();
     chunk_hist(sm.ids, cn, a.E_tot, sm.cnt);
-    __syncthreads();
+    lds_sync();
     const int32_t *starts = a.counts + (int64_t)blockIdx.x * a.E_tot;
     wave_cursors([&](int e) { return starts[e]; }, a.E_tot, sm.cnt);
-    __syncthreads();
+    lds_sync();
     chunk_scatter(sm.ids, cn, (int)lo, a.E_tot, sm.cnt, a.sorted_ids);
 }
 
