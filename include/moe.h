@@ -248,7 +248,9 @@ int moe_resolve_addrs(moe_pool *pool, int32_t active_buf, int64_t n, const int32
 /*
  * A block_m for T tokens: the tile height that covers the expected rows per
  * active expert ((T*(k+S)) / min(T*(k+S), E+S)) in few tiles without mostly
- * padding.  Any of 16, 32, 64, 128, 256 is valid for every entry point.
+ * padding: 16, 32 or 64 up to that many rows, 256 from 512 rows on (when d is
+ * a multiple of 256 and f of 128), else 128.  Any of 16, 32, 64, 128, 256 is
+ * valid for every entry point.
  */
 int32_t moe_suggest_block_m(const moe_pool *pool, int64_t T);
 

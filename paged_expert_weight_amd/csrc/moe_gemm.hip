@@ -28,6 +28,8 @@
 // 16-byte read per lane, XOR-swizzled so 8 rows never share a bank group.
 #include "internal.h"
 
+#include <mutex>
+
 namespace pmoe {
 namespace {
 
@@ -134,6 +136,31 @@ __device__ __forceinline__ bool tile_of(const FwdArgs &a, int BM, int ntiles, in
         return false;
     tile_at<GM>(t, ntiles, u, b, nt);
     return true;
+}
+
+// Last-wave split.  With P resident workgroups, tiles [0, full) run as
+// floor(total / P) whole waves; if the remaining tail <= P / 2 tiles, each is
+// cut into ks contiguous K ranges (ks = min(4, P / tail)) so that the last
+// wave fills the machine.  Every range writes its fp32 accumulators to a
+// partial tile; a fix-up kernel adds the ks partials of a tile in range order
+// and applies the epilogue.  Long-K, large tiles only (one workgroup per CU).
+constexpr int kMaxSplit = 4;
+struct TailPlan {
+    int full, tail, ks;
+};
+
+__device__ __forceinline__ TailPlan tail_plan(const TileSpace &t, int P)
+{
+    TailPlan p{t.total, 0, 1};
+    if (P > 0) {
+        const int full = t.total / P * P, tail = t.total - full;
+        if (tail > 0 && 2 * tail <= P) {
+            p.full = full;
+            p.tail = tail;
+            p.ks = min(kMaxSplit, P / tail);
+        }
+    }
+    return p;
 }
 
 // Expert of block b (b < num_padded / BM), or -1 for a corrupt map entry.
@@ -369,7 +396,7 @@ struct Gemm {
 // One output tile (block b, column tile nt) of a grouped GEMM.
 template <int BM, int BN, int WAVES_M, int WAVES_N, int WK, int BK, int S, bool G1, bool PAGED, bool ATOMIC>
 __device__ __forceinline__ void gemm_tile(const FwdArgs &a, Gemm<BM, BN, WAVES_M, WAVES_N, WK, BK, S, G1> &g, int b,
-                                          int nt)
+                                          int nt, int ks = 0, int nks = 1, float *part = nullptr)
 {
     using G = Gemm<BM, BN, WAVES_M, WAVES_N, WK, BK, S, G1>;
     using Geo = typename G::Geo;
@@ -440,14 +467,34 @@ __device__ __forceinline__ void gemm_tile(const FwdArgs &a, Gemm<BM, BN, WAVES_M
     if constexpr (kPrefetchRows)
         epilogue_rows();
 
+    // K-steps [kb, ke): range ks of nks (the whole contraction unless the tile
+    // is split), divided again over the WK waves of a split-K tile
     const int KT = K / BK;
-    g.run(g.kg * KT / WK, (g.kg + 1) * KT / WK);
+    const int kb = ks * KT / nks, ke = (ks + 1) * KT / nks;
+    g.run(kb + g.kg * (ke - kb) / WK, kb + (g.kg + 1) * (ke - kb) / WK);
     if (!g.reduce_k())
         return;
+    const int lg = g.lg, l16 = g.l16;
+    if (part) {
+        // partial tile [BM][BNE] fp32 (gate/up: gate columns, then up columns)
+        constexpr int BNE = G1 ? 2 * BN : BN;
+#pragma unroll
+        for (int i = 0; i < G::FM; i++)
+#pragma unroll
+            for (int j = 0; j < G::FN; j++)
+#pragma unroll
+                for (int r = 0; r < 4; r++) {
+                    const int row = g.wm * G::WM + i * 16 + 4 * lg + r;
+                    const int col = g.wn * G::WN + j * 16 + l16;
+                    part[row * BNE + col] = g.acc0[i][j][r];
+                    if constexpr (G1)
+                        part[row * BNE + BN + col] = g.acc1[i][j][r];
+                }
+        return;
+    }
     if constexpr (!G1 && !kPrefetchRows)
         epilogue_rows();
 
-    const int lg = g.lg, l16 = g.l16;
     if constexpr (G1) {
         uint16_t *hb = a.h + (int64_t)b * BM * f + n0;
 #pragma unroll
@@ -483,7 +530,8 @@ __device__ __forceinline__ void gemm_tile(const FwdArgs &a, Gemm<BM, BN, WAVES_M
     }
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int WK, int BK, int S, int GM, bool G1, bool PAGED, bool ATOMIC>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int WK, int BK, int S, int GM, bool G1, bool PAGED, bool ATOMIC,
+          bool TAIL>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N * WK) void k_gemm(const FwdArgs a)
 {
     // The host pass only needs this kernel's signature (for its launch stub);
@@ -501,11 +549,89 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N * WK) void k_gemm(const FwdA
     g.wn = g.wt % WAVES_N;
     g.l16 = lane & 15;
     g.lg = lane >> 4;
+    const int ntiles = (G1 ? a.f : a.d) / BN;
     int b, nt;
-    if (!tile_of<GM>(a, BM, (G1 ? a.f : a.d) / BN, b, nt))
+    if constexpr (TAIL) {
+        const TileSpace ts = tile_space(a, BM, ntiles);
+        const TailPlan tp = tail_plan(ts, a.slots[G1 ? 0 : 1]);
+        if (tp.tail > 0) {
+            const int i = (int)blockIdx.x;
+            if (i < tp.full) { // whole tiles, dealt to the XCDs as in tile_of (full is a multiple of 8)
+                tile_at<GM>(ts, ntiles, (i & 7) * (tp.full >> 3) + (i >> 3), b, nt);
+                gemm_tile<BM, BN, WAVES_M, WAVES_N, WK, BK, S, G1, PAGED, ATOMIC>(a, g, b, nt);
+            } else if (i - tp.full < tp.tail * tp.ks) {
+                const int v = i - tp.full;
+                tile_at<GM>(ts, ntiles, tp.full + v / tp.ks, b, nt);
+                constexpr int BNE = G1 ? 2 * BN : BN;
+                gemm_tile<BM, BN, WAVES_M, WAVES_N, WK, BK, S, G1, PAGED, ATOMIC>(a, g, b, nt, v % tp.ks, tp.ks,
+                                                                                a.part + (int64_t)v * BM * BNE);
+            }
+            return;
+        }
+    }
+    if (!tile_of<GM>(a, BM, ntiles, b, nt))
         return;
     gemm_tile<BM, BN, WAVES_M, WAVES_N, WK, BK, S, G1, PAGED, ATOMIC>(a, g, b, nt);
 #endif
+}
+
+// The epilogue of the split tail tiles: partials added in range order.  Tile
+// t of the tail is handled by kFixupChunks(BM, BN) workgroups, each thread four
+// consecutive columns of one row.
+constexpr int fixup_chunks(int BM, int BN) { return BM * BN / 1024; }
+
+template <int BM, int BN, int GM, bool G1, bool ATOMIC>
+__global__ __launch_bounds__(256) void k_tail_fixup(const FwdArgs a)
+{
+    constexpr int CHUNKS = fixup_chunks(BM, BN);
+    static_assert(CHUNKS * 1024 == BM * BN, "tile size");
+    const int ntiles = (G1 ? a.f : a.d) / BN;
+    const TileSpace ts = tile_space(a, BM, ntiles);
+    const TailPlan tp = tail_plan(ts, a.slots[G1 ? 0 : 1]);
+    const int t = (int)blockIdx.x / CHUNKS;
+    if (t >= tp.tail)
+        return;
+    int b, nt;
+    tile_at<GM>(ts, ntiles, tp.full + t, b, nt);
+    if (block_owner(a, b) < 0)
+        return;
+    constexpr int BNE = G1 ? 2 * BN : BN;
+    const int q = (((int)blockIdx.x % CHUNKS) * 256 + (int)threadIdx.x) * 4;
+    const int row = q / BN, col = q % BN;
+    const float *p = a.part + (int64_t)t * tp.ks * BM * BNE + (int64_t)row * BNE + col;
+    float4 s0 = make_float4(0.f, 0.f, 0.f, 0.f), s1 = s0;
+    for (int k = 0; k < tp.ks; k++) {
+        const float4 v = *(const float4 *)(p + (int64_t)k * BM * BNE);
+        s0.x += v.x, s0.y += v.y, s0.z += v.z, s0.w += v.w;
+        if constexpr (G1) {
+            const float4 u = *(const float4 *)(p + (int64_t)k * BM * BNE + BN);
+            s1.x += u.x, s1.y += u.y, s1.z += u.z, s1.w += u.w;
+        }
+    }
+    const int n0 = nt * BN;
+    uint2 o;
+    if constexpr (G1) {
+        auto hv = [](float g, float u) { return (uint32_t)f32_to_bf16(g / (1.f + __expf(-g)) * u); };
+        o.x = hv(s0.x, s1.x) | (hv(s0.y, s1.y) << 16);
+        o.y = hv(s0.z, s1.z) | (hv(s0.w, s1.w) << 16);
+        *(uint2 *)&a.h[((int64_t)b * BM + row) * a.f + n0 + col] = o;
+    } else {
+        const int flat = a.sorted_ids[b * BM + row];
+        if (flat < 0 || flat >= a.T * a.keff)
+            return;
+        const float w = a.topk_w[flat];
+        if constexpr (ATOMIC) {
+            float *y32 = (float *)a.comb + (int64_t)(flat / a.keff) * a.d + n0 + col;
+            unsafeAtomicAdd(y32 + 0, s0.x * w);
+            unsafeAtomicAdd(y32 + 1, s0.y * w);
+            unsafeAtomicAdd(y32 + 2, s0.z * w);
+            unsafeAtomicAdd(y32 + 3, s0.w * w);
+        } else {
+            o.x = (uint32_t)f32_to_bf16(s0.x * w) | ((uint32_t)f32_to_bf16(s0.y * w) << 16);
+            o.y = (uint32_t)f32_to_bf16(s0.z * w) | ((uint32_t)f32_to_bf16(s0.w * w) << 16);
+            *(uint2 *)&((uint16_t *)a.comb)[(int64_t)flat * a.d + n0 + col] = o;
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------- combine / convert
@@ -614,31 +740,83 @@ using Tiles256n = Tiles<256, 64, 4, 2, 1, 32, 4, 64, 4, 1, 1, 32, 4>; // when f 
 
 constexpr int kGroupM = 4;
 
+// Workgroups of a kernel that fit on the current device at once (a multiple of
+// 8), or 0 if the runtime cannot tell.  Cached per kernel and device.
+int resident_slots(const void *kern, int threads)
+{
+    static std::mutex mu;
+    struct Entry {
+        const void *kern;
+        int dev, slots;
+    };
+    static Entry cache[64];
+    static int used = 0;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return 0;
+    }
+    std::lock_guard<std::mutex> lock(mu);
+    for (int i = 0; i < used; i++)
+        if (cache[i].kern == kern && cache[i].dev == dev)
+            return cache[i].slots;
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, threads, 0) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+        (void)hipGetLastError();
+        per_cu = cus = 0;
+    }
+    const int slots = per_cu * cus / 8 * 8;
+    if (used < 64)
+        cache[used++] = Entry{kern, dev, slots};
+    return slots;
+}
+
 template <class C, bool PAGED, bool ATOMIC>
-hipError_t launch_tiles_t(const FwdArgs &a, hipStream_t s)
+hipError_t launch_tiles_t(const FwdArgs &a_in, hipStream_t s)
 {
     constexpr int BM = C::BM;
+    // the last-wave split is used by the 256-row tiles, whose K loops are long
+    constexpr bool TAIL = BM == 256 && C::BN2 == 256;
+    FwdArgs a = a_in;
     const int64_t n = a.T * a.keff;
     int64_t grid_m = n / BM + (n < a.E_tot ? n : a.E_tot);
     if (grid_m > a.blocks_cap)
         grid_m = a.blocks_cap;
     if (a.f % C::BN1 || a.d % C::BN2)
         return hipErrorInvalidValue;
+    constexpr int T1 = 64 * C::WM1 * C::WN1 * C::WK1, T2 = 64 * C::WM2 * C::WN2 * C::WK2;
+    auto k1 = k_gemm<BM, C::BN1, C::WM1, C::WN1, C::WK1, C::BK1, C::S1, kGroupM, true, PAGED, false, TAIL>;
+    auto k2 = k_gemm<BM, C::BN2, C::WM2, C::WN2, C::WK2, C::BK2, C::S2, kGroupM, false, PAGED, ATOMIC, TAIL>;
+    a.slots[0] = a.slots[1] = 0;
+    if constexpr (TAIL) {
+        const int p1 = resident_slots((const void *)k1, T1), p2 = resident_slots((const void *)k2, T2);
+        if ((int64_t)p1 * BM * 2 * C::BN1 * 4 <= a.part_bytes)
+            a.slots[0] = p1;
+        if ((int64_t)p2 * BM * C::BN2 * 4 <= a.part_bytes)
+            a.slots[1] = p2;
+    }
     auto mark = [&](int i) {
         if (a.ev[i])
             (void)hipEventRecord(a.ev[i], s);
     };
-    auto grid = [&](int ntiles) { return (unsigned)((grid_m * ntiles + 7) / 8 * 8); };
+    auto grid = [&](int ntiles, int slots) { return (unsigned)((grid_m * ntiles + 7) / 8 * 8 + slots); };
     if (ATOMIC) {
         const int64_t n4 = a.T * a.d / 4;
         k_zero<<<(unsigned)((n4 + 255) / 256), 256, 0, s>>>((float4 *)a.comb, n4);
     }
     mark(0);
-    k_gemm<BM, C::BN1, C::WM1, C::WN1, C::WK1, C::BK1, C::S1, kGroupM, true, PAGED, false>
-        <<<grid(a.f / C::BN1), 64 * C::WM1 * C::WN1 * C::WK1, 0, s>>>(a);
+    k1<<<grid(a.f / C::BN1, a.slots[0]), T1, 0, s>>>(a);
+    if constexpr (TAIL)
+        if (a.slots[0])
+            k_tail_fixup<BM, C::BN1, kGroupM, true, false>
+                <<<(unsigned)(a.slots[0] / 2 * fixup_chunks(BM, C::BN1)), 256, 0, s>>>(a);
     mark(1);
-    k_gemm<BM, C::BN2, C::WM2, C::WN2, C::WK2, C::BK2, C::S2, kGroupM, false, PAGED, ATOMIC>
-        <<<grid(a.d / C::BN2), 64 * C::WM2 * C::WN2 * C::WK2, 0, s>>>(a);
+    k2<<<grid(a.d / C::BN2, a.slots[1]), T2, 0, s>>>(a);
+    if constexpr (TAIL)
+        if (a.slots[1])
+            k_tail_fixup<BM, C::BN2, kGroupM, false, ATOMIC>
+                <<<(unsigned)(a.slots[1] / 2 * fixup_chunks(BM, C::BN2)), 256, 0, s>>>(a);
     mark(2);
     const int64_t nq = a.T * a.d / 4;
     if (ATOMIC)

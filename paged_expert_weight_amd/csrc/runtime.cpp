@@ -99,7 +99,7 @@ int check_desc(const moe_pool_desc *d)
 
 struct Sizes {
     int64_t n, sorted_cap, blocks_cap;
-    size_t off_counts, off_h, off_comb, total;
+    size_t off_counts, off_h, off_comb, off_part, part, total;
 };
 
 size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -114,10 +114,21 @@ Sizes sizes_for(const moe_pool *p, int64_t T, int bm, uint32_t flags)
     const size_t h = (size_t)s.sorted_cap * p->desc.f * 2;
     const size_t comb = (flags & MOE_FLAG_ATOMIC_COMBINE) ? (size_t)T * p->desc.d * 4
                                                           : (size_t)s.n * p->desc.d * 2;
+    // fp32 partial tiles of a split last wave (256-row tiles, one workgroup per CU: at most
+    // one 256 x 256 tile per CU)
+    s.part = 0;
+    if (bm == 256) {
+        int dev = 0, cus = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess)
+            s.part = (size_t)cus * 256 * 256 * 4;
+        (void)hipGetLastError();
+    }
     s.off_counts = 0;
     s.off_h = up256(counts);
     s.off_comb = s.off_h + up256(h);
-    s.total = s.off_comb + up256(comb);
+    s.off_part = s.off_comb + up256(comb);
+    s.total = s.off_part + up256(s.part);
     return s;
 }
 
@@ -202,6 +213,8 @@ int forward_common(const moe_pool *p, const void *w13, const void *w2, bool page
     a.y = (uint16_t *)y;
     a.h = (uint16_t *)((char *)ws + sz.off_h);
     a.comb = (char *)ws + sz.off_comb;
+    a.part = (float *)((char *)ws + sz.off_part);
+    a.part_bytes = (int64_t)sz.part;
     a.atomic = (flags & MOE_FLAG_ATOMIC_COMBINE) != 0;
     if (ev)
         for (int i = 0; i < 4; i++)
@@ -586,6 +599,11 @@ int32_t moe_suggest_block_m(const moe_pool *p, int64_t T)
         return 32;
     if (per <= 64)
         return 64;
+    // 256-row tiles (with 256-column down tiles) only pay off once an expert
+    // fills several of them: they halve the operand traffic per MFMA but need
+    // d to be a multiple of 256
+    if (per >= 512 && p->desc.d % 256 == 0 && p->desc.f % 128 == 0)
+        return 256;
     return 128;
 }
 

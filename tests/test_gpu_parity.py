@@ -11,6 +11,8 @@ Bars:
 Every pool holds bf16 NaN outside expert pages, and the load buffer that is not
 active is NaN as well, so a stray read shows up as NaN in y.
 """
+import functools
+
 import numpy as np
 import pytest
 
@@ -191,7 +193,10 @@ def test_paged_equals_contiguous_bitwise(name):
 
 # Tile heights 32..256 share one K summation order (32-wide MFMA steps in K
 # order); the 16-row decode tile splits K over four waves and adds the partial
-# sums in wave order, so it is held to the oracle tolerance instead.
+# sums in wave order, so it is held to the oracle tolerance instead, and so is
+# a 256-row launch whose last partial wave is cut into K ranges (the layers
+# below).  qwen15 and tiny never take that path: their last waves are more
+# than half full (qwen15) or use the 64-column 256-row tiles (tiny).
 SAME_K_ORDER = (32, 64, 128, 256)
 
 
@@ -210,6 +215,42 @@ def test_every_tile_height_matches_oracle(name, T):
     for bm in BLOCK_MS:
         y, _ = c.forward(bm)
         _check_y(c, y)
+
+
+# Layers whose 256-row GEMM launches split their last wave into K ranges on a
+# 256-CU device (one 256-row tile per CU): in "split_all" every tile is split
+# (fewer tiles than half the CUs); in "split_tail" the gate/up launch has one
+# whole wave of 256 tiles and a tail of about 64 split tiles.
+SPLIT_SPECS = {
+    "split_all": synth.LayerSpec("split_all", 512, 512, 512, 4, 2, 0, 16, (3,), 1, None, 0, 2001),
+    "split_tail": synth.LayerSpec("split_tail", 3840, 1024, 1280, 8, 2, 0, 24, (7,), 1, None, 0, 2002),
+}
+
+
+@functools.lru_cache(maxsize=1)
+def split_case(name):
+    return Case(synth.make_layer(SPLIT_SPECS[name]))
+
+
+@pytest.mark.parametrize("name,ntok", [("split_all", None), ("split_tail", 96)])
+def test_split_last_wave_matches_oracle(name, ntok):
+    c = split_case(name)
+    toks = None
+    if ntok:
+        g = np.random.default_rng(5)
+        toks = np.unique(np.concatenate([[0, c.layer.T - 1], g.choice(c.layer.T, ntok, replace=False)]))
+    for flags in (0, pm.MOE_FLAG_ATOMIC_COMBINE):
+        y, _ = c.forward(256, flags)
+        _check_y(c, y, toks)
+
+
+@pytest.mark.parametrize("name", ["split_all", "split_tail"])
+def test_split_last_wave_paged_equals_contiguous(name):
+    c = split_case(name)
+    y, _ = c.forward(256)
+    yc, _ = c.contiguous(256)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), yc.view(torch.int16))
 
 
 @pytest.mark.parametrize("name", ["tiny", "qwen15"])
