@@ -228,6 +228,7 @@ struct Gemm {
     static constexpr int STAGE_BYTES = ROWS * Geo::ROWB;
     static constexpr int LDS_BYTES = WK * S * STAGE_BYTES;
     static_assert(S >= 2 && S <= 8 && (S - 2) * IPW < 64, "stages");
+    static constexpr int BM_ = BM, BN_ = BN, WK_ = WK, WAVES_N_ = WAVES_N;
 
     __amdgpu_buffer_rsrc_t ra, rb0, rb1;
     uint32_t voff[IPW];
@@ -394,11 +395,12 @@ struct Gemm {
 };
 
 // One output tile (block b, column tile nt) of a grouped GEMM.
-template <int BM, int BN, int WAVES_M, int WAVES_N, int WK, int BK, int S, bool G1, bool PAGED, bool ATOMIC>
-__device__ __forceinline__ void gemm_tile(const FwdArgs &a, Gemm<BM, BN, WAVES_M, WAVES_N, WK, BK, S, G1> &g, int b,
-                                          int nt, int ks = 0, int nks = 1, float *part = nullptr)
+template <class G, bool G1, bool PAGED, bool ATOMIC>
+__device__ __forceinline__ void gemm_tile(const FwdArgs &a, G &g, int b, int nt, int ks = 0, int nks = 1,
+                                          float *part = nullptr)
 {
-    using G = Gemm<BM, BN, WAVES_M, WAVES_N, WK, BK, S, G1>;
+    constexpr int BM = G::BM_, BN = G::BN_, WK = G::WK_;
+    constexpr int BK = G::Geo::ROWB / 2;
     using Geo = typename G::Geo;
     const int lane = threadIdx.x & 63;
     const int e = block_owner(a, b);
@@ -530,14 +532,13 @@ __device__ __forceinline__ void gemm_tile(const FwdArgs &a, Gemm<BM, BN, WAVES_M
     }
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int WK, int BK, int S, int GM, bool G1, bool PAGED, bool ATOMIC,
-          bool TAIL>
-__global__ __launch_bounds__(64 * WAVES_M * WAVES_N * WK) void k_gemm(const FwdArgs a)
+template <class G, int GM, bool G1, bool PAGED, bool ATOMIC, bool TAIL>
+__global__ __launch_bounds__(64 * G::NW) void k_gemm(const FwdArgs a)
 {
     // The host pass only needs this kernel's signature (for its launch stub);
     // the pipeline's gfx950 builtins are compiled in the device pass.
 #if defined(__HIP_DEVICE_COMPILE__)
-    using G = Gemm<BM, BN, WAVES_M, WAVES_N, WK, BK, S, G1>;
+    constexpr int BM = G::BM_, BN = G::BN_;
     __shared__ __attribute__((aligned(1024))) uint8_t lds[G::LDS_BYTES];
     G g;
     g.lds = lds;
@@ -545,8 +546,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N * WK) void k_gemm(const FwdA
     g.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     g.wt = g.wave % G::NT;  // wave within the tile
     g.kg = g.wave / G::NT;  // K range of this wave
-    g.wm = g.wt / WAVES_N;
-    g.wn = g.wt % WAVES_N;
+    g.wm = g.wt / G::WAVES_N_;
+    g.wn = g.wt % G::WAVES_N_;
     g.l16 = lane & 15;
     g.lg = lane >> 4;
     const int ntiles = (G1 ? a.f : a.d) / BN;
@@ -558,12 +559,12 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N * WK) void k_gemm(const FwdA
             const int i = (int)blockIdx.x;
             if (i < tp.full) { // whole tiles, dealt to the XCDs as in tile_of (full is a multiple of 8)
                 tile_at<GM>(ts, ntiles, (i & 7) * (tp.full >> 3) + (i >> 3), b, nt);
-                gemm_tile<BM, BN, WAVES_M, WAVES_N, WK, BK, S, G1, PAGED, ATOMIC>(a, g, b, nt);
+                gemm_tile<G, G1, PAGED, ATOMIC>(a, g, b, nt);
             } else if (i - tp.full < tp.tail * tp.ks) {
                 const int v = i - tp.full;
                 tile_at<GM>(ts, ntiles, tp.full + v / tp.ks, b, nt);
                 constexpr int BNE = G1 ? 2 * BN : BN;
-                gemm_tile<BM, BN, WAVES_M, WAVES_N, WK, BK, S, G1, PAGED, ATOMIC>(a, g, b, nt, v % tp.ks, tp.ks,
+                gemm_tile<G, G1, PAGED, ATOMIC>(a, g, b, nt, v % tp.ks, tp.ks,
                                                                                 a.part + (int64_t)v * BM * BNE);
             }
             return;
@@ -571,7 +572,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N * WK) void k_gemm(const FwdA
     }
     if (!tile_of<GM>(a, BM, ntiles, b, nt))
         return;
-    gemm_tile<BM, BN, WAVES_M, WAVES_N, WK, BK, S, G1, PAGED, ATOMIC>(a, g, b, nt);
+    gemm_tile<G, G1, PAGED, ATOMIC>(a, g, b, nt);
 #endif
 }
 
@@ -719,24 +720,25 @@ __global__ __launch_bounds__(256) void k_resolve(const ResolveArgs r, const FwdA
     r.base[q] = in_pool ? 0 : 1 + r.active_buf;
 }
 
-// Tile shapes: block height BM; for each GEMM the column tile BN, the wave
-// grid (M x N), the split-K wave count WK, the K-step BK and the LDS stages.
-template <int BM_, int BN1_, int WM1_, int WN1_, int WK1_, int BK1_, int S1_, int BN2_, int WM2_, int WN2_, int WK2_,
-          int BK2_, int S2_>
+// Tile shapes per block height: the gate/up and down GEMMs,
+// Gemm<BM, BN, waves M, waves N, split-K waves, BK, stages, gate/up>.
+template <int BM_, class G1T, class G2T>
 struct Tiles {
     static constexpr int BM = BM_;
-    static constexpr int BN1 = BN1_, WM1 = WM1_, WN1 = WN1_, WK1 = WK1_, BK1 = BK1_, S1 = S1_;
-    static constexpr int BN2 = BN2_, WM2 = WM2_, WN2 = WN2_, WK2 = WK2_, BK2 = BK2_, S2 = S2_;
+    using K1 = G1T;
+    using K2 = G2T;
+    static_assert(G1T::BM_ == BM_ && G2T::BM_ == BM_, "block height");
 };
-// decode-sized blocks: one wave per 16x16 tile, four waves splitting K (many bytes in flight)
-using Tiles16 = Tiles<16, 16, 1, 1, 4, 64, 3, 32, 1, 1, 2, 64, 4>;
-using Tiles32 = Tiles<32, 32, 1, 2, 1, 64, 2, 32, 1, 2, 1, 64, 2>;
-using Tiles64 = Tiles<64, 64, 2, 2, 1, 64, 2, 64, 2, 2, 1, 64, 2>;
-using Tiles128 = Tiles<128, 64, 2, 2, 1, 64, 2, 128, 2, 2, 1, 64, 2>;
+// decode-sized blocks: one wave per 16-row tile, waves splitting K (many bytes in flight)
+using Tiles16 = Tiles<16, Gemm<16, 16, 1, 1, 4, 64, 3, true>, Gemm<16, 32, 1, 1, 2, 64, 4, false>>;
+using Tiles32 = Tiles<32, Gemm<32, 32, 1, 2, 1, 64, 2, true>, Gemm<32, 32, 1, 2, 1, 64, 2, false>>;
+using Tiles64 = Tiles<64, Gemm<64, 64, 2, 2, 1, 64, 2, true>, Gemm<64, 64, 2, 2, 1, 64, 2, false>>;
+using Tiles128 = Tiles<128, Gemm<128, 64, 2, 2, 1, 64, 2, true>, Gemm<128, 128, 2, 2, 1, 64, 2, false>>;
 // large blocks (MFMA-bound shapes): 8 waves, two per SIMD, each with a 64x128
 // accumulator tile (gate/up: 64 x (64 gate + 64 up)); 256x256 down tiles
-using Tiles256 = Tiles<256, 128, 4, 2, 1, 32, 4, 256, 4, 2, 1, 32, 4>;
-using Tiles256n = Tiles<256, 64, 4, 2, 1, 32, 4, 64, 4, 1, 1, 32, 4>; // when f or d is not a multiple of 128
+using Tiles256 = Tiles<256, Gemm<256, 128, 4, 2, 1, 32, 4, true>, Gemm<256, 256, 4, 2, 1, 32, 4, false>>;
+// when f or d is not a multiple of 128 / 256
+using Tiles256n = Tiles<256, Gemm<256, 64, 4, 2, 1, 32, 4, true>, Gemm<256, 64, 4, 1, 1, 32, 4, false>>;
 
 constexpr int kGroupM = 4;
 
@@ -776,24 +778,27 @@ template <class C, bool PAGED, bool ATOMIC>
 hipError_t launch_tiles_t(const FwdArgs &a_in, hipStream_t s)
 {
     constexpr int BM = C::BM;
+    using G1T = typename C::K1;
+    using G2T = typename C::K2;
+    constexpr int BN1 = G1T::BN_, BN2 = G2T::BN_;
     // the last-wave split is used by the 256-row tiles, whose K loops are long
-    constexpr bool TAIL = BM == 256 && C::BN2 == 256;
+    constexpr bool TAIL = BM == 256 && BN2 == 256;
     FwdArgs a = a_in;
     const int64_t n = a.T * a.keff;
     int64_t grid_m = n / BM + (n < a.E_tot ? n : a.E_tot);
     if (grid_m > a.blocks_cap)
         grid_m = a.blocks_cap;
-    if (a.f % C::BN1 || a.d % C::BN2)
+    if (a.f % BN1 || a.d % BN2)
         return hipErrorInvalidValue;
-    constexpr int T1 = 64 * C::WM1 * C::WN1 * C::WK1, T2 = 64 * C::WM2 * C::WN2 * C::WK2;
-    auto k1 = k_gemm<BM, C::BN1, C::WM1, C::WN1, C::WK1, C::BK1, C::S1, kGroupM, true, PAGED, false, TAIL>;
-    auto k2 = k_gemm<BM, C::BN2, C::WM2, C::WN2, C::WK2, C::BK2, C::S2, kGroupM, false, PAGED, ATOMIC, TAIL>;
+    constexpr int T1 = 64 * G1T::NW, T2 = 64 * G2T::NW;
+    auto k1 = k_gemm<G1T, kGroupM, true, PAGED, false, TAIL>;
+    auto k2 = k_gemm<G2T, kGroupM, false, PAGED, ATOMIC, TAIL>;
     a.slots[0] = a.slots[1] = 0;
     if constexpr (TAIL) {
         const int p1 = resident_slots((const void *)k1, T1), p2 = resident_slots((const void *)k2, T2);
-        if ((int64_t)p1 * BM * 2 * C::BN1 * 4 <= a.part_bytes)
+        if ((int64_t)p1 * BM * 2 * BN1 * 4 <= a.part_bytes)
             a.slots[0] = p1;
-        if ((int64_t)p2 * BM * C::BN2 * 4 <= a.part_bytes)
+        if ((int64_t)p2 * BM * BN2 * 4 <= a.part_bytes)
             a.slots[1] = p2;
     }
     auto mark = [&](int i) {
@@ -806,17 +811,17 @@ hipError_t launch_tiles_t(const FwdArgs &a_in, hipStream_t s)
         k_zero<<<(unsigned)((n4 + 255) / 256), 256, 0, s>>>((float4 *)a.comb, n4);
     }
     mark(0);
-    k1<<<grid(a.f / C::BN1, a.slots[0]), T1, 0, s>>>(a);
+    k1<<<grid(a.f / BN1, a.slots[0]), T1, 0, s>>>(a);
     if constexpr (TAIL)
         if (a.slots[0])
-            k_tail_fixup<BM, C::BN1, kGroupM, true, false>
-                <<<(unsigned)(a.slots[0] / 2 * fixup_chunks(BM, C::BN1)), 256, 0, s>>>(a);
+            k_tail_fixup<BM, BN1, kGroupM, true, false>
+                <<<(unsigned)(a.slots[0] / 2 * fixup_chunks(BM, BN1)), 256, 0, s>>>(a);
     mark(1);
-    k2<<<grid(a.d / C::BN2, a.slots[1]), T2, 0, s>>>(a);
+    k2<<<grid(a.d / BN2, a.slots[1]), T2, 0, s>>>(a);
     if constexpr (TAIL)
         if (a.slots[1])
-            k_tail_fixup<BM, C::BN2, kGroupM, false, ATOMIC>
-                <<<(unsigned)(a.slots[1] / 2 * fixup_chunks(BM, C::BN2)), 256, 0, s>>>(a);
+            k_tail_fixup<BM, BN2, kGroupM, false, ATOMIC>
+                <<<(unsigned)(a.slots[1] / 2 * fixup_chunks(BM, BN2)), 256, 0, s>>>(a);
     mark(2);
     const int64_t nq = a.T * a.d / 4;
     if (ATOMIC)
@@ -842,7 +847,7 @@ hipError_t launch_paged(const FwdArgs &a, hipStream_t s)
     case 64: return launch_tiles<Tiles64, PAGED>(a, s);
     case 128: return launch_tiles<Tiles128, PAGED>(a, s);
     case 256:
-        if (a.f % Tiles256::BN1 == 0 && a.d % Tiles256::BN2 == 0)
+        if (a.f % Tiles256::K1::BN_ == 0 && a.d % Tiles256::K2::BN_ == 0)
             return launch_tiles<Tiles256, PAGED>(a, s);
         return launch_tiles<Tiles256n, PAGED>(a, s);
     default: return hipErrorInvalidValue;
