@@ -23,8 +23,8 @@
 //      matching lane advances the run's cursor by the match count.  Distinct
 //      experts of a group update distinct cursors, so the 64 entries of a group
 //      are placed at once, in flat order.
-// Small batches run routing and alignment in one workgroup (one launch);
-// larger ones route with one wave per token and align in one workgroup up to
+// Small batches run routing and alignment in one workgroup (one launch; the
+// smallest with a leaner eight-wave form); larger ones route with one wave per token and align in one workgroup up to
 // kChunkElems entries, or with histogram / scan / scatter kernels over chunks.
 #include "internal.h"
 
@@ -427,6 +427,108 @@ __global__ __launch_bounds__(kAlignThreads) void k_route_align_small(const Route
     align_in_one_wg(sm, (int)a.T * a.keff, a);
 }
 
+// Tiny batches (T <= kTinyTokens, T*(k+S) <= kTinyPicks): routing and alignment
+// in one workgroup of eight waves with four barriers.  Wave w routes tokens w,
+// w+8, ...; then holds flat picks [64w, 64w+64) and counts them per expert with
+// the bit-sliced lane match; thread t scans experts 2t and 2t+1 (padded counts,
+// exclusive over experts, then per-wave cursors) and writes their padding and
+// block map; finally every pick is placed at its wave's cursor plus its rank
+// among the lanes below with the same expert.
+constexpr int kTinyWaves = 8, kTinyThreads = 64 * kTinyWaves;
+constexpr int kTinyTokens = 32, kTinyPicks = 64 * kTinyWaves;
+
+template <int NV>
+__global__ __launch_bounds__(kTinyThreads) void k_route_align_tiny(const RouteArgs a)
+{
+    __shared__ int32_t s_ids[kTinyPicks];
+    __shared__ int s_cnt[kTinyWaves * kMaxExpertsTotal]; // per-wave counts, then per-wave cursors
+    __shared__ int s_wsum[kTinyWaves];
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int E_tot = a.E_tot, BM = a.BM;
+    const int n = (int)a.T * a.keff;
+    for (int i = threadIdx.x; i < kTinyWaves * E_tot; i += kTinyThreads)
+        s_cnt[i] = 0;
+    constexpr int TPW = kTinyTokens / kTinyWaves;
+    float v[TPW][NV];
+#pragma unroll
+    for (int r = 0; r < TPW; r++) {
+        const int t = w + r * kTinyWaves;
+        if (t < (int)a.T)
+            load_logits<NV>(a.logits + (int64_t)t * a.E, a.E, lane, v[r]);
+    }
+#pragma unroll
+    for (int r = 0; r < TPW; r++) {
+        const int t = w + r * kTinyWaves;
+        if (t < (int)a.T)
+            route_token<NV>(v[r], a.E, a.k, a.S, lane, a.topk_ids + (int64_t)t * a.keff,
+                            a.topk_w + (int64_t)t * a.keff, s_ids + t * a.keff);
+    }
+    lds_sync();
+
+    // per-wave counts and each pick's rank within its wave
+    const int p = 64 * w + lane;
+    const bool valid = p < n;
+    const int e = valid ? s_ids[p] : 0;
+    const uint64_t m = same_id_lanes(e, valid, id_bits(E_tot));
+    const int rank = __popcll(m & lanes_below());
+    if (valid && rank == 0)
+        s_cnt[w * E_tot + e] = __popcll(m);
+    lds_sync();
+
+    // experts 2t, 2t+1: totals, padded segment starts, cursors, padding, block map
+    int tot[2], pad[2];
+#pragma unroll
+    for (int q = 0; q < 2; q++) {
+        const int x = 2 * (int)threadIdx.x + q;
+        int c = 0;
+        if (x < E_tot)
+            for (int ww = 0; ww < kTinyWaves; ww++)
+                c += s_cnt[ww * E_tot + x];
+        tot[q] = c;
+        pad[q] = (c + BM - 1) / BM * BM;
+    }
+    const int local = pad[0] + pad[1];
+    int incl = local;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(incl, off);
+        if (lane >= off)
+            incl += y;
+    }
+    if (lane == 63)
+        s_wsum[w] = incl;
+    lds_sync();
+    int base = 0, all = 0;
+    for (int ww = 0; ww < kTinyWaves; ww++) {
+        const int sv = s_wsum[ww];
+        base += ww < w ? sv : 0;
+        all += sv;
+    }
+    if (threadIdx.x == 0)
+        *a.num_padded = all;
+    int seg = base + incl - local;
+#pragma unroll
+    for (int q = 0; q < 2; q++) {
+        const int x = 2 * (int)threadIdx.x + q;
+        if (x < E_tot && pad[q] > 0) {
+            int run = seg;
+            for (int ww = 0; ww < kTinyWaves; ww++) {
+                const int c = s_cnt[ww * E_tot + x];
+                s_cnt[ww * E_tot + x] = run;
+                run += c;
+            }
+            for (int i = seg + tot[q]; i < seg + pad[q]; i++)
+                a.sorted_ids[i] = n;
+            for (int bb = seg / BM; bb < (seg + pad[q]) / BM; bb++)
+                a.block_expert[bb] = x;
+        }
+        seg += pad[q];
+    }
+    lds_sync();
+    if (valid)
+        a.sorted_ids[s_cnt[w * E_tot + e] + rank] = p;
+}
+
 __global__ __launch_bounds__(kAlignThreads) void k_align_single(const RouteArgs a)
 {
     __shared__ AlignSmem sm;
@@ -524,6 +626,10 @@ template <int NV>
 hipError_t launch_nv(const RouteArgs &a, hipStream_t s)
 {
     const int64_t n = a.T * a.keff;
+    if (a.T <= kTinyTokens && n <= kTinyPicks && a.E_tot <= 2 * kTinyThreads) {
+        k_route_align_tiny<NV><<<1, kTinyThreads, 0, s>>>(a);
+        return hipGetLastError();
+    }
     if (a.T <= kSmallTokens && n <= kChunkElems) {
         k_route_align_small<NV><<<1, kAlignThreads, 0, s>>>(a);
         return hipGetLastError();

@@ -449,8 +449,17 @@ int moe_paged_forward(moe_pool *p, const void *x, int64_t T, int32_t block_m, co
         return fail(MOE_ERR_STATE, "load buffer " + std::to_string(active_buf) +
                                        " was never filled but the table reads from it");
     hipStream_t s = (hipStream_t)stream;
-    if (T > 0 && p->uses_loadbuf)
-        HIP_TRY(hipStreamWaitEvent(s, p->filled[active_buf], 0));
+    if (T > 0 && p->uses_loadbuf) {
+        // a fill that has already completed needs no wait on the stream (the
+        // wait would still cost a queue round trip before the first kernel)
+        const hipError_t q = hipEventQuery(p->filled[active_buf]);
+        if (q == hipErrorNotReady) {
+            (void)hipGetLastError();
+            HIP_TRY(hipStreamWaitEvent(s, p->filled[active_buf], 0));
+        } else if (q != hipSuccess) {
+            return hip_fail(q, "hipEventQuery");
+        }
+    }
     CHECK(forward_common(p, nullptr, nullptr, true, x, T, block_m, topk_ids, topk_w, sorted_ids, block_expert,
                          num_padded, active_buf, y, ws, ws_bytes, flags, s, T > 0 ? next_timing_events(p) : nullptr));
     if (T > 0 && p->uses_loadbuf) {

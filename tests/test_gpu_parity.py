@@ -83,6 +83,22 @@ def test_route_align_bitexact_large(name, block_m):
     _check_routing(c, r, block_m)
 
 
+# The one-workgroup routing forms at their limits: many experts with a shared
+# one (lanes hold 8 logits each), the largest expert count (E+S = 1024) with
+# k = 32 and the most picks the smallest form takes (T*(k+S) = 495), and the
+# first batch sizes past it.
+@pytest.mark.parametrize("E,k,S,T", [(512, 10, 1, 1), (512, 10, 1, 16), (512, 10, 1, 32), (1023, 32, 1, 15),
+                                     (1023, 32, 1, 16), (60, 4, 0, 33), (8, 2, 0, 64)])
+@pytest.mark.parametrize("block_m", (16, 256))
+def test_route_align_small_batch_forms(E, k, S, T, block_m):
+    s = synth.spec("tiny", T=T, E=E, k=k, S=S, pool_pages=3 * (E + S), loadbuf_experts=(), loadbuf_slots=0,
+                   seed=3000 + E + T)
+    c = Case(synth.make_layer(s))
+    r, _ = c.route(block_m)
+    torch.cuda.synchronize()
+    _check_routing(c, r, block_m)
+
+
 def test_route_ties_and_edge_logits():
     """Exact ties everywhere: the lower expert id must win."""
     s = synth.spec("tiny", T=300, E=40, k=6, pool_pages=3 * 40, loadbuf_experts=(), loadbuf_slots=0)
