@@ -33,7 +33,7 @@ HBM_PEAK_GBS = 8000.0
 # HBM bytes per k_gemm1 launch measured with rocprofv3 (FETCH_SIZE scaled by 2.0, the factor a
 # 1 GiB copy reads back, plus WRITE_SIZE), keyed by workload, T, block_m, atomic combine and a
 # hash of the GEMM sources the counters were taken on.  Reported only while that hash matches.
-MEASURED_TRAFFIC = {("qwen15", 1024, 128, False, "c69bb44f8ec19010"): 751173833}
+MEASURED_TRAFFIC = {("qwen15", 1024, 128, False, "6be7d2f7bb126373"): 751285358}
 GEMM_SOURCES = ("paged_expert_weight_amd/csrc/moe_gemm.hip", "paged_expert_weight_amd/csrc/internal.h")
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 MALL_BYTES = 256 << 20

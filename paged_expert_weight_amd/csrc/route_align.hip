@@ -44,7 +44,8 @@ __device__ __forceinline__ void lds_sync()
 
 constexpr int kAlignWaves = 16;
 constexpr int kAlignThreads = 64 * kAlignWaves;
-constexpr int kChunkElems = 8192; // flat entries per alignment workgroup
+constexpr int kChunkElems = 8192; // flat entries aligned by one workgroup (the one-workgroup forms)
+constexpr int kMultiChunk = 2048;  // flat entries per histogram / scatter workgroup of larger batches
 constexpr int kSmallTokens = 64;  // route + align in one workgroup when T <= this (and T*keff <= kChunkElems)
 
 __device__ __forceinline__ bool beats(float va, int ia, float vb, int ib)
@@ -543,11 +544,11 @@ __global__ __launch_bounds__(kAlignThreads) void k_align_hist(const RouteArgs a)
 {
     __shared__ int hist[kMaxExpertsTotal];
     const int64_t n = a.T * a.keff;
-    const int64_t lo = (int64_t)blockIdx.x * kChunkElems;
-    const int cn = (int)min((int64_t)kChunkElems, n - lo);
+    const int64_t lo = (int64_t)blockIdx.x * kMultiChunk;
+    const int cn = (int)min((int64_t)kMultiChunk, n - lo);
     for (int e = threadIdx.x; e < a.E_tot; e += kAlignThreads)
         hist[e] = 0;
-    constexpr int R = kChunkElems / kAlignThreads;
+    constexpr int R = kMultiChunk / kAlignThreads;
     int32_t v[R];
 #pragma unroll
     for (int r = 0; r < R; r++) {
@@ -609,8 +610,8 @@ __global__ __launch_bounds__(kAlignThreads) void k_align_scatter(const RouteArgs
 {
     __shared__ AlignSmem sm;
     const int64_t n = a.T * a.keff;
-    const int64_t lo = (int64_t)blockIdx.x * kChunkElems;
-    const int cn = (int)min((int64_t)kChunkElems, n - lo);
+    const int64_t lo = (int64_t)blockIdx.x * kMultiChunk;
+    const int cn = (int)min((int64_t)kMultiChunk, n - lo);
     zero_counts(sm, a.E_tot);
     stage_ids(sm.ids, a.topk_ids + lo, cn);
     lds_sync();
@@ -638,7 +639,7 @@ hipError_t launch_nv(const RouteArgs &a, hipStream_t s)
     if (n <= kChunkElems) {
         k_align_single<<<1, kAlignThreads, 0, s>>>(a);
     } else {
-        const int nch = (int)((n + kChunkElems - 1) / kChunkElems);
+        const int nch = (int)((n + kMultiChunk - 1) / kMultiChunk);
         k_align_hist<<<nch, kAlignThreads, 0, s>>>(a);
         k_align_scan<<<1, kAlignThreads, 0, s>>>(a, nch);
         k_align_scatter<<<nch, kAlignThreads, 0, s>>>(a);
@@ -653,7 +654,7 @@ int64_t route_workspace_bytes(int64_t T, int keff, int E_tot)
     const int64_t n = T * keff;
     if (n <= kChunkElems)
         return 0;
-    const int64_t nch = (n + kChunkElems - 1) / kChunkElems;
+    const int64_t nch = (n + kMultiChunk - 1) / kMultiChunk;
     return nch * E_tot * (int64_t)sizeof(int32_t);
 }
 
