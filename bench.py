@@ -270,6 +270,16 @@ def main():
                    "step_slowdown_pct": round((busy_ms / ms - 1) * 100, 2),
                    "fill_hidden_behind_one_step": fill_ms <= ms}
 
+    # ---- per-step spread (events around every step of one more timed pass)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        step(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    per_step = np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
+    spread = {q: round(float(np.percentile(per_step, p)), 2) for q, p in (("p10", 10), ("p50", 50), ("p90", 90))}
+
     line = {
         "metric": METRIC,
         "value": round(tflops, 3),
@@ -293,8 +303,10 @@ def main():
         "overhead_vs_contiguous_pct": round((ms / contig_ms - 1) * 100, 3) if contig_ms else None,
         "stages_us": {"route_align": round(route_us, 2), "gate_up": round(stage_us[0], 2),
                       "down": round(stage_us[1], 2), "combine": round(stage_us[2], 2)},
+        "step_us_spread": spread,
         "roofline": roof,
         "loadbuf": loadbuf,
+        "adjuster": adjuster_timing(s.E),
     }
 
     if not args.no_cpu_baseline:
@@ -303,6 +315,24 @@ def main():
     print(json.dumps(line), flush=True)
     for c in copies:
         c["h"].close()
+
+
+def adjuster_timing(E: int, layers: int = 48, rounds: int = 2000):
+    """Host cost of one adjuster round (amounts + selection) for a model of `layers`
+    MoE layers of E experts: grows of 5 and shrinks of 3 alternating."""
+    import numpy as np
+    import paged_expert_weight_amd as pm
+    g = np.random.default_rng(0)
+    ranking = np.stack([g.permutation(E) for _ in range(layers)]).astype(np.int32)
+    prob = -np.sort(-g.random((layers, E)).astype(np.float32), axis=1)
+    resident = [E // 2] * layers
+    t0 = time.perf_counter()
+    for r in range(rounds):
+        ev, add = pm.adjust_amounts(8 if r % 2 else 0, 0 if r % 2 else 24)
+        _, resident = pm.adjust_select(ranking, prob, resident, E, ev, add)
+    us = (time.perf_counter() - t0) / rounds * 1e6
+    return {"layers": layers, "experts": E, "us_per_round": round(us, 2),
+            "note": "host-side policy incl. Python marshalling of the C calls"}
 
 
 def cpu_baseline(layer, seconds: float):

@@ -268,6 +268,50 @@ int32_t moe_suggest_block_m(const moe_pool *pool, int64_t T);
 int moe_stage_timing(moe_pool *pool, int32_t enable);
 int moe_stage_times(moe_pool *pool, float *ms, int32_t *count);
 
+/* ---------------------------------------------------------------- adjuster
+ * Host-side policy of the digest's section "The adjuster: when to evict an
+ * expert, and which one?", run once per scheduling round after the scheduler
+ * has placed requests.  All pointers are host memory; nothing touches the
+ * GPU.
+ */
+
+/*
+ * How many experts to evict or add this round.  short_pages: expert pages the
+ * scheduler is short of (R_b); free_pages: free expert pages (F_b).  An expert
+ * holds 3 expert pages.  R_b > 0: *n_evict = ceil((R_b + 1) / 3).  Else
+ * F_b < 2: *n_evict = 1.  Else F_b > 9: *n_add = min(5, floor((F_b - 9) / 3)).
+ * Else both 0.  MOE_ERR_INVALID_ARG for negative counts or null outputs.
+ */
+int moe_adjust_amounts(int32_t short_pages, int32_t free_pages, int32_t *n_evict, int32_t *n_add);
+
+/*
+ * Offline hot-expert ranking of one layer from sample routing.  topk_ids
+ * [T][k] (as written by moe_route, k = top_k + num_shared); ids outside
+ * [0, E) (the shared expert) are not ranked.  ranking[E] receives the expert
+ * ids by descending routing probability (count / T; ties to the lower id),
+ * prob[E] the probabilities in the same order.
+ */
+int moe_rank_experts(const int32_t *topk_ids, int64_t T, int32_t k, int32_t E, int32_t *ranking, float *prob);
+
+/*
+ * Which experts: the change list of one round.  ranking / prob: [L][E] per-layer
+ * rankings and their probabilities (rows of moe_rank_experts); resident[L]:
+ * the number of top-ranked experts each layer keeps on the GPU, updated in
+ * place.  offload_limit: a layer that already offloads this many experts
+ * (E - resident[l] >= offload_limit) is left out of shrinking.  Exactly one of
+ * n_evict, n_add may be > 0 (a round shrinks or grows).  Experts are decided
+ * one at a time: growing, each layer nominates ranking[l][resident[l]] and the
+ * highest probability wins; shrinking, each layer nominates
+ * ranking[l][resident[l] - 1] and the lowest wins; ties go to the lower layer.
+ * out_layer / out_expert / out_add (1 add, 0 evict) receive the decisions in
+ * order (capacity n_evict + n_add), *n_out their number (fewer when no layer
+ * can nominate).  MOE_ERR_INVALID_ARG for bad sizes, a ranking row that is not
+ * a permutation of [0, E), or resident[l] outside [0, E].
+ */
+int moe_adjust_select(int32_t L, int32_t E, const int32_t *ranking, const float *prob, int32_t *resident,
+                      int32_t offload_limit, int32_t n_evict, int32_t n_add, int32_t *out_layer,
+                      int32_t *out_expert, int32_t *out_add, int32_t *n_out);
+
 /* Message for the last non-zero return on this thread ("" if none). */
 const char *moe_last_error(void);
 

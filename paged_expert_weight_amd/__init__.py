@@ -38,6 +38,7 @@ EXPORTS = (
     "moe_route_capacity", "moe_workspace_bytes", "moe_route", "moe_paged_forward",
     "moe_contiguous_forward", "moe_loadbuf_fill", "moe_resolve_addrs", "moe_suggest_block_m",
     "moe_stage_timing", "moe_stage_times", "moe_last_error", "moe_version",
+    "moe_adjust_amounts", "moe_rank_experts", "moe_adjust_select",
 )
 
 
@@ -90,6 +91,9 @@ def lib():
     L.moe_resolve_addrs.argtypes = [P, i32, i64, P, P, P, P, P, P, P]
     L.moe_stage_timing.argtypes = [P, i32]
     L.moe_stage_times.argtypes = [P, P, P]
+    L.moe_adjust_amounts.argtypes = [i32, i32, P, P]
+    L.moe_rank_experts.argtypes = [P, i64, i32, i32, P, P]
+    L.moe_adjust_select.argtypes = [i32, i32, P, P, P, i32, i32, i32, P, P, P, P]
     L.moe_suggest_block_m.argtypes = [P, i64]
     L.moe_suggest_block_m.restype = i32
     L.moe_last_error.restype = ctypes.c_char_p
@@ -299,3 +303,42 @@ def contiguous_forward(p: MoePool, w13, w2, x, r: RouteOut, ws, flags: int = 0, 
     moe_contiguous_forward(p, w13, w2, x, r.block_m, r.topk_ids, r.topk_w, r.sorted_ids, r.block_expert,
                            r.num_padded, y, ws, flags, stream)
     return y
+
+
+# ----------------------------------------------------------------------------- adjuster (host policy)
+
+def adjust_amounts(short_pages: int, free_pages: int):
+    """(experts to evict, experts to add) for one scheduling round."""
+    import numpy as np
+    out = np.zeros(2, dtype=np.int32)
+    _check(lib().moe_adjust_amounts(int(short_pages), int(free_pages), out[0:].ctypes.data,
+                                    out[1:].ctypes.data))
+    return int(out[0]), int(out[1])
+
+
+def rank_experts(topk_ids, E: int):
+    """(ranking, prob) of one layer from sample routing topk_ids [T][k] (host array)."""
+    import numpy as np
+    ids = np.ascontiguousarray(np.asarray(topk_ids, dtype=np.int32))
+    T, k = (ids.shape[0], ids.shape[1]) if ids.ndim == 2 else (0, 0)
+    ranking = np.empty(E, dtype=np.int32)
+    prob = np.empty(E, dtype=np.float32)
+    _check(lib().moe_rank_experts(ids.ctypes.data, T, k, int(E), ranking.ctypes.data, prob.ctypes.data))
+    return ranking, prob
+
+
+def adjust_select(ranking, prob, resident, offload_limit: int, n_evict: int, n_add: int):
+    """Change list [(layer, expert, 1 add / 0 evict)] and the new resident counts."""
+    import numpy as np
+    rk = np.ascontiguousarray(np.asarray(ranking, dtype=np.int32))
+    pr = np.ascontiguousarray(np.asarray(prob, dtype=np.float32))
+    L, E = rk.shape
+    res = np.ascontiguousarray(np.asarray(resident, dtype=np.int32)).copy()
+    cap = max(1, int(n_evict) + int(n_add))
+    ol, oe, oa = (np.zeros(cap, dtype=np.int32) for _ in range(3))
+    n = np.zeros(1, dtype=np.int32)
+    _check(lib().moe_adjust_select(L, E, rk.ctypes.data, pr.ctypes.data, res.ctypes.data, int(offload_limit),
+                                   int(n_evict), int(n_add), ol.ctypes.data, oe.ctypes.data, oa.ctypes.data,
+                                   n.ctypes.data))
+    m = int(n[0])
+    return [(int(ol[i]), int(oe[i]), int(oa[i])) for i in range(m)], [int(v) for v in res]

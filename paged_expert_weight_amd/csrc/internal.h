@@ -75,4 +75,7 @@ struct ResolveArgs {
 };
 hipError_t launch_resolve(const ResolveArgs &a, hipStream_t s);
 
+// Records msg for moe_last_error() and returns code.
+int set_error(int code, const char *msg);
+
 } // namespace pmoe

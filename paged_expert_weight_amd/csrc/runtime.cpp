@@ -240,6 +240,10 @@ hipEvent_t *next_timing_events(moe_pool *p)
 
 } // namespace
 
+namespace pmoe {
+int set_error(int code, const char *msg) { return fail(code, msg); }
+} // namespace pmoe
+
 extern "C" {
 
 const char *moe_last_error(void) { return g_err.c_str(); }

@@ -126,3 +126,68 @@ def test_rank_experts_ties_go_to_the_lower_id():
     ranking, prob = ora.rank_experts(ids, 5)
     assert ranking.tolist() == [1, 3, 0, 2, 4]
     np.testing.assert_array_equal(prob, np.array([2, 2, 1, 1, 0], dtype=np.float32) / 3)
+
+
+# ----------------------------------------------------------------------------- library vs oracle
+
+@pytest.fixture(scope="module")
+def lib_adj():
+    import paged_expert_weight_amd as pm
+    try:
+        pm.lib()
+    except (RuntimeError, OSError) as e:  # the library has not been built
+        pytest.skip(str(e))
+    return pm
+
+
+def test_library_amounts_match_oracle(lib_adj):
+    for short in range(0, 60):
+        for free in range(0, 60):
+            if short and free % 7:
+                continue
+            assert lib_adj.adjust_amounts(short, free) == ora.adjust_amounts(short, free)
+    g = json.load(open(GOLDEN))
+    for c in g["cases"]:
+        assert lib_adj.adjust_amounts(c["short_pages"], c["free_pages"]) == (c["evict"], c["add"])
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_library_ranking_matches_oracle(lib_adj, seed):
+    g = np.random.default_rng(seed)
+    T, E, k = int(g.integers(1, 400)), int(g.integers(1, 70)), int(g.integers(1, 6))
+    k = min(k, E)
+    w = g.random(E) ** 3 + 1e-3
+    ids = np.stack([g.choice(E, k, replace=False, p=w / w.sum()) for _ in range(T)]).astype(np.int32)
+    if seed % 2:  # a shared expert column (id E) is not ranked
+        ids = np.concatenate([ids, np.full((T, 1), E, np.int32)], axis=1)
+    r_lib, p_lib = lib_adj.rank_experts(ids, E)
+    r_ora, p_ora = ora.rank_experts(ids, E)
+    assert np.array_equal(r_lib, r_ora)
+    np.testing.assert_array_equal(p_lib, p_ora)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_library_selection_matches_oracle(lib_adj, seed):
+    g = np.random.default_rng(1000 + seed)
+    L, E = int(g.integers(1, 9)), int(g.integers(1, 40))
+    ranking, prob = _rankings(seed, L, E, ties=bool(seed % 3 == 0))
+    resident = g.integers(0, E + 1, size=L).tolist()
+    limit = int(g.integers(0, E + 2))
+    for n_ev, n_add in ((0, 0), (0, 1), (0, 5), (1, 0), (3, 0), (7, 0), (0, 40), (40, 0)):
+        got = lib_adj.adjust_select(ranking, prob, resident, limit, n_ev, n_add)
+        assert got == ora.select(ranking, prob, resident, limit, n_ev, n_add), (n_ev, n_add)
+
+
+def test_library_rejects_bad_inputs(lib_adj):
+    from paged_expert_weight_amd import MoeError
+    with pytest.raises(MoeError):
+        lib_adj.adjust_amounts(-1, 3)
+    ranking, prob = _rankings(0, 2, 4)
+    bad = ranking.copy()
+    bad[1, 0] = bad[1, 1]
+    with pytest.raises(MoeError):
+        lib_adj.adjust_select(bad, prob, [2, 2], 4, 1, 0)
+    with pytest.raises(MoeError):
+        lib_adj.adjust_select(ranking, prob, [5, 2], 4, 1, 0)
+    with pytest.raises(MoeError):
+        lib_adj.adjust_select(ranking, prob, [2, 2], 4, 1, 1)
