@@ -78,6 +78,10 @@ def parse():
     ap.add_argument("--no-contig", action="store_true")
     ap.add_argument("--no-fill", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target seconds of oracle work")
+    ap.add_argument("--pipeline", action="store_true",
+                    help="time an L-layer pass through moe_pipeline_* instead (one JSON line of its own)")
+    ap.add_argument("--layers", type=int, default=8, help="--pipeline: layers per pass")
+    ap.add_argument("--offloaded", type=int, default=1, help="--pipeline: experts per layer via the load buffer")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB fp32 read + 1 GiB write elementwise kernel (scales HBM counters)")
     return ap.parse_args()
@@ -99,6 +103,9 @@ def main():
     args = parse()
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.pipeline and args.gpus == 1:
+        pipeline_bench(args)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the layer's hot path runs on a single MI355X and there is no "
@@ -315,6 +322,198 @@ def main():
     print(json.dumps(line), flush=True)
     for c in copies:
         c["h"].close()
+
+
+def pipeline_bench(args):
+    """An L-layer pass of Qwen1.5-MoE-shaped layers over one shared pool: every
+    layer keeps E - n experts in its own pool pages and takes n through the
+    alternating load buffers, filled from pinned host memory on a copy stream.
+    Timed four ways, passes back to back with the host at most one pass ahead:
+    overlapped (prefetch of layer l + 1 issued ahead of the forward of layer
+    l), serialized (each fill waits for the previous forward), fills alone and
+    forwards alone; plus a pass in which every layer switches tables (the
+    copy-before-switch wait and the table upload), one pass at a time from an
+    idle GPU, and the host cost of each call."""
+    import numpy as np
+    import torch
+
+    import paged_expert_weight_amd as pm
+    from workloads import device as wdev
+    from workloads import synth
+
+    pm.lib()
+    L, n_lb = args.layers, args.offloaded
+    T = args.T or 1024
+    base = synth.SPECS["qwen15"]
+    E = base.E
+    s = synth.spec("qwen15", T=max(T, base.T), pool_pages=3 * (E - n_lb),
+                   loadbuf_experts=tuple(range(E - n_lb, E)), loadbuf_slots=n_lb)
+    t0 = time.time()
+    layer = synth.make_layer(s, T)
+    dev = wdev.to_device(layer)
+    print(f"# layer generated in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    Pl = s.pool_pages
+    fd = s.f * s.d
+    pool = torch.empty((L * Pl, fd), dtype=torch.bfloat16, device="cuda")
+    for l in range(L):
+        pool[l * Pl:(l + 1) * Pl].copy_(dev.pool)  # every layer reads pages of its own
+    del dev.pool
+    lbuf = tuple(dev.loadbuf)
+    slots = sorted(dev.host_blobs)
+    blobs = [dev.host_blobs[k] for k in slots]
+    tables = []
+    hs = []
+    for l in range(L):
+        t = layer.placement.locs.copy()
+        for e in range(s.E_tot):
+            if t[e]["kind"] == synth.LOC_POOL:
+                t[e]["idx"] = t[e]["idx"] + l * Pl
+        tables.append(t)
+        h = pm.moe_pool_create(pool, L * Pl, s.d, s.f, s.E, s.k, s.S, n_lb, lbuf)
+        pm.moe_set_expert_locs(h, t)
+        pm.moe_loadbuf_fill(h, l % 2, slots, blobs)  # for the forwards-alone timing
+        hs.append(h)
+    torch.cuda.synchronize()
+    bm = pm.moe_suggest_block_m(hs[0], T)
+    ws = pm.workspace(hs[0], T, bm)
+    r = pm.route(hs[0], dev.logits, bm, ws)
+    y = torch.empty_like(dev.x)
+    comp = torch.cuda.current_stream()
+    copy = torch.cuda.Stream()
+    pipe = pm.MoePipeline(hs, copy)
+
+    def fwd(l):
+        pipe.forward(l, dev.x, r, ws, y=y, stream=comp)
+
+    def pass_overlapped():
+        pipe.prefetch(0, slots, blobs)
+        for l in range(L):
+            if l + 1 < L:
+                pipe.prefetch(l + 1, slots, blobs)
+            fwd(l)
+
+    def pass_serialized():
+        for l in range(L):
+            copy.wait_stream(comp)
+            pipe.prefetch(l, slots, blobs)
+            fwd(l)
+
+    def pass_fills():
+        for l in range(L):
+            pm.moe_loadbuf_fill(hs[l], l % 2, slots, blobs, copy)
+
+    def pass_forwards():
+        for l in range(L):
+            pm.moe_paged_forward(hs[l], dev.x, bm, r.topk_ids, r.topk_w, r.sorted_ids, r.block_expert,
+                                 r.num_padded, l % 2, y, ws, 0, comp)
+
+    def pass_switch():
+        for l in range(L):
+            pipe.stage_table(l, tables[l])
+        pass_overlapped()
+
+    def bounded(fn, n):
+        """n passes back to back, the host at most one pass ahead of the GPU (as a
+        serving loop that enqueues the next step while the current one runs)."""
+        prev = None
+        for _ in range(n):
+            if prev is not None:
+                prev[0].synchronize()
+                prev[1].synchronize()
+            e = (torch.cuda.Event(), torch.cuda.Event())
+            e[0].record(comp)
+            e[1].record(copy)
+            fn()
+            prev = e
+
+    def timed(fn, K, W):
+        bounded(fn, W)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(comp)
+        copy.wait_stream(comp)
+        bounded(fn, K)
+        comp.wait_stream(copy)
+        e1.record(comp)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / K * 1e3
+
+    def isolated(fn, K):
+        """One pass at a time from an idle GPU, start of the first copy or kernel to the end of the last."""
+        tot = 0.0
+        for _ in range(K):
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(comp)
+            copy.wait_stream(comp)
+            fn()
+            comp.wait_stream(copy)
+            e1.record(comp)
+            e1.synchronize()
+            tot += e0.elapsed_time(e1)
+        return tot / K * 1e3
+
+    K, W = max(1, args.steps // 2), max(2, args.warmup // 2)
+    us = {}
+    # two interleaved rounds; the second (warm) one is reported
+    for rnd in range(2):
+        for key, fn in (("overlapped", pass_overlapped), ("serialized", pass_serialized),
+                        ("fills_alone", pass_fills), ("forwards_alone", pass_forwards),
+                        ("overlapped_with_table_switch", pass_switch)):
+            us[key] = round(timed(fn, K, W), 1)
+            print(f"# round {rnd} {key}: {us[key]} us/pass", file=sys.stderr, flush=True)
+        us["isolated_overlapped"] = round(isolated(pass_overlapped, K), 1)
+        print(f"# round {rnd} isolated_overlapped: {us['isolated_overlapped']} us/pass", file=sys.stderr, flush=True)
+    # host cost per call (enqueue only)
+    torch.cuda.synchronize()
+    reps = 200
+    t0 = time.perf_counter()
+    for i in range(reps):
+        pm.moe_paged_forward(hs[0], dev.x, bm, r.topk_ids, r.topk_w, r.sorted_ids, r.block_expert, r.num_padded, 0,
+                             y, ws, 0, comp)
+    plain_us = (time.perf_counter() - t0) / reps * 1e6
+    torch.cuda.synchronize()
+    pipe.prefetch(0, slots, blobs)
+    t0 = time.perf_counter()
+    for i in range(reps):
+        fwd(0)
+    pipe_us = (time.perf_counter() - t0) / reps * 1e6
+    torch.cuda.synchronize()
+    copy_l = us["fills_alone"] / L
+    comp_l = us["forwards_alone"] / L
+    # back to back, the first fill of a pass overlaps the end of the previous one
+    ideal = L * max(copy_l, comp_l)
+    ideal_iso = L * max(copy_l, comp_l) + min(copy_l, comp_l)
+    hideable = us["serialized"] - ideal
+    nbytes = n_lb * 3 * fd * 2
+    line = {
+        "metric": "multi-layer pipeline pass time (us)",
+        "value": us["overlapped"],
+        "unit": "us/pass",
+        "higher_is_better": False,
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{L} Qwen1.5-MoE-shaped layers (d=2048 f=1408 E=60 top-4) over one pool, "
+                               f"{n_lb} expert(s) per layer via the alternating load buffers",
+                   "layers": L, "T": T, "block_m": bm, "offloaded_per_layer": n_lb,
+                   "fill_bytes_per_layer": nbytes},
+        "pass_us": us,
+        "per_layer_us": {"fill": round(copy_l, 1), "forward": round(comp_l, 1)},
+        "h2d_gbs": round(nbytes / (copy_l * 1e-6) / 1e9, 2),
+        "ideal_us": {"overlapped": round(ideal, 1), "isolated_overlapped": round(ideal_iso, 1)},
+        "frac_of_ideal": {"overlapped": round(ideal / us["overlapped"], 3),
+                          "isolated_overlapped": round(ideal_iso / us["isolated_overlapped"], 3)},
+        "overlap_efficiency": round((us["serialized"] - us["overlapped"]) / hideable, 3) if hideable > 0 else None,
+        "table_switch_cost_us_per_layer": round((us["overlapped_with_table_switch"] - us["overlapped"]) / L, 2),
+        "host_us_per_call": {"moe_paged_forward": round(plain_us, 2), "moe_pipeline_forward": round(pipe_us, 2)},
+    }
+    print(json.dumps(line), flush=True)
+    pipe.close()
+    for h in hs:
+        h.close()
 
 
 def adjuster_timing(E: int, layers: int = 48, rounds: int = 2000):

@@ -312,6 +312,86 @@ int moe_adjust_select(int32_t L, int32_t E, const int32_t *ranking, const float 
                       int32_t offload_limit, int32_t n_evict, int32_t n_add, int32_t *out_layer,
                       int32_t *out_expert, int32_t *out_add, int32_t *n_out);
 
+/* ---------------------------------------------------------------- multi-layer pipeline
+ * One forward pass over L MoE layers, following the digest's sections "The
+ * pipeline: what happens in one scheduling round" (two loading buffers that
+ * alternate between layers) and the ordering rules at the end of "The
+ * adjuster: when to evict an expert, and which one?" (copy before the page
+ * table changes; compute before pages are reclaimed).
+ *
+ * The layers are moe_pool handles over ONE pool (same pool_base, num_pages,
+ * d, f, loadbuf_slots and load buffers), each with its table set and no two
+ * tables naming one page.  Layer l reads load buffer l % 2, so the fill for
+ * layer l + 1 overlaps the forward of layer l.  The pipeline does not own the
+ * handles: destroy it before them, and change their tables only through
+ * moe_pipeline_stage_table while it exists.  All forwards run on one stream
+ * (the first forward fixes it); fills, page copies and table uploads run on
+ * copy_stream.  Each layer gets a second device table (16 bytes per expert)
+ * and a pinned staging copy: a staged table is uploaded into the second one
+ * with its page copies, and the switch exchanges the two.
+ */
+typedef struct moe_pipeline moe_pipeline;
+
+/* MOE_ERR_INVALID_ARG (handles null, repeated, on other devices or over other
+ * pools / buffers), MOE_ERR_STATE (a handle without a table),
+ * MOE_ERR_PAGE_ALIAS (two tables share a page). */
+int moe_pipeline_create(int32_t L, moe_pool *const *layers, void *copy_stream, moe_pipeline **out);
+
+/* Waits for the pipeline's pending copies and reads, then frees it.  NULL is a no-op. */
+int moe_pipeline_destroy(moe_pipeline *pipe);
+
+/*
+ * Stage one change of layer `layer`'s table: locs (host, n = E + S entries,
+ * validated as by moe_validate_locs) replaces the table at the layer's next
+ * moe_pipeline_forward.  copy_expert[i] (host, n_copy entries, distinct) is
+ * an expert the new table places in pool pages that it newly receives;
+ * copy_src[i] (pinned host, 3*f*d bf16: W1, W3, W2 back to back) is copied
+ * into those three pages now, on copy_stream, after the upload of the table
+ * itself; the forward that switches tables waits for all of them first.  The
+ * call blocks the host only while this layer's previous change is still
+ * being uploaded.  Pages the current table names but
+ * the new one does not are dropped: moe_pipeline_reclaim reports them once
+ * every forward enqueued before the switch has finished.
+ * Errors: MOE_ERR_STATE (the layer already has a change waiting);
+ * MOE_ERR_PAGE_ALIAS (a copy target the current table reads; a page another
+ * layer's current or staged table names; a dropped page not yet reclaimable);
+ * MOE_ERR_INVALID_ARG (a copied expert not placed in the pool by locs, listed
+ * twice, or a source that is not pinned host memory).  Nothing is enqueued
+ * on an error.
+ */
+int moe_pipeline_stage_table(moe_pipeline *pipe, int32_t layer, const moe_expert_loc *locs, int32_t n,
+                             int32_t n_copy, const int32_t *copy_expert, const void *const *copy_src);
+
+/*
+ * Fill slots of load buffer layer % 2 for layer `layer` (as moe_loadbuf_fill:
+ * slots distinct, host_src pinned, 3*f*d bf16 each).  The copies wait on
+ * copy_stream for the last forward that read the buffer.  MOE_ERR_STATE if
+ * the buffer still holds experts filled for another layer that has not run
+ * since.
+ */
+int moe_pipeline_prefetch(moe_pipeline *pipe, int32_t layer, int32_t n, const int32_t *slots,
+                          const void *const *host_src);
+
+/*
+ * The paged forward of layer `layer` (arguments as moe_paged_forward, the
+ * load buffer being layer % 2).  Applies a staged table first: the stream
+ * waits for its upload and page copies, then the layer reads the new table
+ * (no copy on the forward stream).  MOE_ERR_STATE if
+ * the table reads the load buffer and the buffer's last fill was for another
+ * layer; MOE_ERR_INVALID_ARG for a stream other than the pipeline's.
+ */
+int moe_pipeline_forward(moe_pipeline *pipe, int32_t layer, const void *x, int64_t T, int32_t block_m,
+                         const int32_t *topk_ids, const float *topk_w, const int32_t *sorted_ids,
+                         const int32_t *block_expert, const int32_t *num_padded, void *y, void *ws,
+                         size_t ws_bytes, uint32_t flags, void *stream);
+
+/*
+ * Non-blocking: writes up to cap dropped pages that may be reused (every
+ * forward that could read them has finished) to pages[] and their number to
+ * *n; pages beyond cap are reported by the next call.
+ */
+int moe_pipeline_reclaim(moe_pipeline *pipe, int32_t *pages, int32_t cap, int32_t *n);
+
 /* Message for the last non-zero return on this thread ("" if none). */
 const char *moe_last_error(void);
 

@@ -39,6 +39,8 @@ EXPORTS = (
     "moe_contiguous_forward", "moe_loadbuf_fill", "moe_resolve_addrs", "moe_suggest_block_m",
     "moe_stage_timing", "moe_stage_times", "moe_last_error", "moe_version",
     "moe_adjust_amounts", "moe_rank_experts", "moe_adjust_select",
+    "moe_pipeline_create", "moe_pipeline_destroy", "moe_pipeline_stage_table", "moe_pipeline_prefetch",
+    "moe_pipeline_forward", "moe_pipeline_reclaim",
 )
 
 
@@ -94,6 +96,12 @@ def lib():
     L.moe_adjust_amounts.argtypes = [i32, i32, P, P]
     L.moe_rank_experts.argtypes = [P, i64, i32, i32, P, P]
     L.moe_adjust_select.argtypes = [i32, i32, P, P, P, i32, i32, i32, P, P, P, P]
+    L.moe_pipeline_create.argtypes = [i32, P, P, ctypes.POINTER(P)]
+    L.moe_pipeline_destroy.argtypes = [P]
+    L.moe_pipeline_stage_table.argtypes = [P, i32, P, i32, i32, P, P]
+    L.moe_pipeline_prefetch.argtypes = [P, i32, i32, P, P]
+    L.moe_pipeline_forward.argtypes = [P, i32, P, i64, i32, P, P, P, P, P, P, P, sz, u32, P]
+    L.moe_pipeline_reclaim.argtypes = [P, P, i32, P]
     L.moe_suggest_block_m.argtypes = [P, i64]
     L.moe_suggest_block_m.restype = i32
     L.moe_last_error.restype = ctypes.c_char_p
@@ -236,6 +244,69 @@ def moe_loadbuf_fill(p: MoePool, buf: int, slots: Sequence[int], host_src: Seque
     s = np.ascontiguousarray(np.asarray(slots, dtype=np.int32))
     srcs = (ctypes.c_void_p * max(1, n))(*[_ptr(t) if not isinstance(t, int) else t for t in host_src])
     _check(lib().moe_loadbuf_fill(p.handle, buf, n, s.ctypes.data if n else None, srcs, _stream(copy_stream)))
+
+
+def _ptr_array(ts: Sequence):
+    n = len(ts)
+    return (ctypes.c_void_p * max(1, n))(*[_ptr(t) if not isinstance(t, int) else t for t in ts])
+
+
+class MoePipeline:
+    """Owner of one moe_pipeline handle over the layers' MoePool objects (kept
+    alive by it)."""
+
+    def __init__(self, layers: Sequence[MoePool], copy_stream=None):
+        self.layers = list(layers)
+        hs = (ctypes.c_void_p * len(self.layers))(*[p.handle.value for p in self.layers])
+        h = ctypes.c_void_p()
+        self._copy = copy_stream
+        _check(lib().moe_pipeline_create(len(self.layers), hs, _stream(copy_stream), ctypes.byref(h)))
+        self.handle = h
+        self._keep = []  # host sources of copies that may still be in flight
+
+    def close(self):
+        if self.handle:
+            _check(lib().moe_pipeline_destroy(self.handle))
+            self.handle = None
+            self._keep = []
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def stage_table(self, layer: int, locs: np.ndarray, copies=()) -> None:
+        """copies: [(expert, pinned host tensor of 3*f*d bf16)]."""
+        a = locs_array(locs)
+        n = len(copies)
+        e = np.ascontiguousarray(np.asarray([c[0] for c in copies], dtype=np.int32))
+        srcs = _ptr_array([c[1] for c in copies])
+        _check(lib().moe_pipeline_stage_table(self.handle, layer, a.ctypes.data, a.shape[0], n,
+                                              e.ctypes.data if n else None, srcs))
+        self._keep.append([c[1] for c in copies])
+
+    def prefetch(self, layer: int, slots: Sequence[int], host_src: Sequence) -> None:
+        n = len(slots)
+        s = np.ascontiguousarray(np.asarray(slots, dtype=np.int32))
+        _check(lib().moe_pipeline_prefetch(self.handle, layer, n, s.ctypes.data if n else None,
+                                           _ptr_array(host_src)))
+
+    def forward(self, layer: int, x, r: "RouteOut", ws, flags: int = 0, y=None, stream=None):
+        import torch
+        if y is None:
+            y = torch.empty_like(x)
+        _check(lib().moe_pipeline_forward(self.handle, layer, _ptr(x), x.shape[0], r.block_m, _ptr(r.topk_ids),
+                                          _ptr(r.topk_w), _ptr(r.sorted_ids), _ptr(r.block_expert),
+                                          _ptr(r.num_padded), _ptr(y), _ptr(ws), ws.numel() * ws.element_size(),
+                                          flags, _stream(stream)))
+        return y
+
+    def reclaim(self, cap: int = 4096):
+        out = np.zeros(max(1, cap), dtype=np.int32)
+        n = ctypes.c_int32()
+        _check(lib().moe_pipeline_reclaim(self.handle, out.ctypes.data, cap, ctypes.byref(n)))
+        return [int(v) for v in out[: n.value]]
 
 
 def moe_resolve_addrs(p: MoePool, active_buf: int, e, which, row, col, off, base, stream=None) -> None:

@@ -5,7 +5,9 @@
 #include "moe.h"
 #include "internal.h"
 
+#include <algorithm>
 #include <array>
+#include <iterator>
 #include <cstring>
 #include <string>
 #include <vector>
@@ -248,7 +250,7 @@ extern "C" {
 
 const char *moe_last_error(void) { return g_err.c_str(); }
 
-int moe_version(void) { return 100; }
+int moe_version(void) { return 101; }
 
 int moe_validate_locs(const moe_pool_desc *desc, const moe_expert_loc *locs, int32_t n)
 {
@@ -618,6 +620,400 @@ int32_t moe_suggest_block_m(const moe_pool *p, int64_t T)
     if (per >= 512 && p->desc.d % 256 == 0 && p->desc.f % 128 == 0)
         return 256;
     return 128;
+}
+
+} // extern "C"
+
+// ---------------------------------------------------------------------------- multi-layer pipeline
+// One forward pass over L MoE layers (the digest's pipeline section and its
+// two alternating loading buffers; the ordering rules at the end of the
+// adjuster section).  Layer l reads load buffer l mod 2, so the fill for layer
+// l + 1 runs on the copy stream while layer l computes, and the fill for
+// layer l + 2 waits until layer l has read the buffer.  A change of a layer's
+// table (experts newly cached in reserved pages, experts evicted) is applied
+// when the layer next runs, after the copies into the new pages have landed;
+// pages the table stops naming stay readable until every forward enqueued
+// before the switch (the pass that was running) has finished, and only then
+// does moe_pipeline_reclaim report them.
+
+struct moe_pipeline {
+    int L = 0;
+    std::vector<moe_pool *> layers;
+    hipStream_t copy = nullptr;
+    hipEvent_t filled[2] = {nullptr, nullptr}, consumed[2] = {nullptr, nullptr};
+    bool filled_rec[2] = {false, false}, consumed_rec[2] = {false, false};
+    int filled_for[2] = {-1, -1}; // layer the last fill of buffer b was for
+    bool unread[2] = {false, false}; // that layer has not run since the fill
+    struct Staged {
+        bool pending = false;
+        std::vector<moe_expert_loc> locs;
+        std::vector<int32_t> dropped; // pages of the current table the new one does not name
+        hipEvent_t copied = nullptr;  // table upload and page copies done (copy stream)
+        bool copied_rec = false;
+        // The layer's second device table: the staged table is uploaded into it
+        // on the copy stream, and the switch swaps it with the handle's.
+        DevLoc *alt = nullptr;
+        moe_expert_loc *h_up = nullptr; // pinned source of that upload
+        hipEvent_t switched = nullptr;  // forward stream at the last switch
+        bool switched_rec = false;
+    };
+    std::vector<Staged> staged;
+    std::vector<std::vector<moe_expert_loc>> current; // table each layer runs with
+    hipStream_t fwd = nullptr;                        // the one stream all forwards run on
+    bool fwd_set = false;
+    struct Batch {
+        hipEvent_t done; // recorded on the forward stream at the table switch
+        std::vector<int32_t> pages;
+    };
+    std::vector<Batch> batches; // dropped pages whose last readers may still run
+    std::vector<int32_t> ready;  // reclaimable, not yet reported
+};
+
+namespace {
+
+std::vector<int32_t> table_pages(const std::vector<moe_expert_loc> &t)
+{
+    std::vector<int32_t> pg;
+    for (const auto &L : t)
+        if (L.kind == MOE_LOC_POOL)
+            for (int m = 0; m < 3; m++)
+                pg.push_back(L.idx[m]);
+    std::sort(pg.begin(), pg.end());
+    return pg;
+}
+
+bool is_pinned(const void *p)
+{
+    hipPointerAttribute_t attr;
+    const hipError_t e = hipPointerGetAttributes(&attr, p);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return false;
+    }
+    return attr.type == hipMemoryTypeHost;
+}
+
+} // namespace
+
+extern "C" {
+
+int moe_pipeline_create(int32_t L, moe_pool *const *layers, void *copy_stream, moe_pipeline **out)
+{
+    if (!out)
+        return fail(MOE_ERR_INVALID_ARG, "out is null");
+    *out = nullptr;
+    if (L < 1 || !layers)
+        return fail(MOE_ERR_INVALID_ARG, "need L >= 1 layer handles");
+    const moe_pool_desc &d0 = layers[0] ? layers[0]->desc : moe_pool_desc{};
+    for (int l = 0; l < L; l++) {
+        if (!layers[l])
+            return fail(MOE_ERR_INVALID_ARG, "layer handle " + std::to_string(l) + " is null");
+        const moe_pool_desc &d = layers[l]->desc;
+        if (d.pool_base != d0.pool_base || d.num_pages != d0.num_pages || d.d != d0.d || d.f != d0.f ||
+            d.loadbuf_slots != d0.loadbuf_slots || d.loadbuf_base[0] != d0.loadbuf_base[0] ||
+            d.loadbuf_base[1] != d0.loadbuf_base[1])
+            return fail(MOE_ERR_INVALID_ARG, "layers must share the pool, d, f and the two load buffers");
+        if (layers[l]->device != layers[0]->device)
+            return fail(MOE_ERR_INVALID_ARG, "layers must live on one device");
+        for (int m = 0; m < l; m++)
+            if (layers[m] == layers[l])
+                return fail(MOE_ERR_INVALID_ARG, "a layer handle is listed twice");
+        if (!layers[l]->locs_set)
+            return fail(MOE_ERR_STATE, "layer " + std::to_string(l) + " has no location table");
+    }
+    moe_pipeline *p = new moe_pipeline();
+    p->L = L;
+    p->layers.assign(layers, layers + L);
+    p->copy = (hipStream_t)copy_stream;
+    p->staged.resize(L);
+    p->current.resize(L);
+    for (int l = 0; l < L; l++) {
+        const moe_pool *h = layers[l];
+        p->current[l].assign(h->h_stage, h->h_stage + h->E_tot); // the table the handle holds
+    }
+    {
+        std::vector<int32_t> all;
+        for (int l = 0; l < L; l++) {
+            const std::vector<int32_t> pg = table_pages(p->current[l]);
+            all.insert(all.end(), pg.begin(), pg.end());
+        }
+        std::sort(all.begin(), all.end());
+        if (std::adjacent_find(all.begin(), all.end()) != all.end()) {
+            delete p;
+            return fail(MOE_ERR_PAGE_ALIAS, "two layers' tables name the same page");
+        }
+    }
+    hipError_t e = hipSuccess;
+    for (int b = 0; b < 2 && e == hipSuccess; b++) {
+        e = hipEventCreateWithFlags(&p->filled[b], hipEventDisableTiming);
+        if (e == hipSuccess)
+            e = hipEventCreateWithFlags(&p->consumed[b], hipEventDisableTiming);
+    }
+    for (int l = 0; l < L && e == hipSuccess; l++) {
+        moe_pipeline::Staged &st = p->staged[l];
+        const size_t n = (size_t)layers[l]->E_tot;
+        e = hipEventCreateWithFlags(&st.copied, hipEventDisableTiming);
+        if (e == hipSuccess)
+            e = hipEventCreateWithFlags(&st.switched, hipEventDisableTiming);
+        if (e == hipSuccess)
+            e = hipMalloc((void **)&st.alt, sizeof(DevLoc) * n);
+        if (e == hipSuccess)
+            e = hipHostMalloc((void **)&st.h_up, sizeof(moe_expert_loc) * n, hipHostMallocDefault);
+    }
+    if (e != hipSuccess) {
+        moe_pipeline_destroy(p);
+        return hip_fail(e, "pipeline set-up");
+    }
+    *out = p;
+    return MOE_OK;
+}
+
+int moe_pipeline_destroy(moe_pipeline *p)
+{
+    if (!p)
+        return MOE_OK;
+    for (int b = 0; b < 2; b++) {
+        if (p->filled[b]) {
+            if (p->filled_rec[b])
+                (void)hipEventSynchronize(p->filled[b]);
+            (void)hipEventDestroy(p->filled[b]);
+        }
+        if (p->consumed[b]) {
+            if (p->consumed_rec[b])
+                (void)hipEventSynchronize(p->consumed[b]);
+            (void)hipEventDestroy(p->consumed[b]);
+        }
+    }
+    for (auto &s : p->staged) {
+        if (s.copied) {
+            if (s.copied_rec)
+                (void)hipEventSynchronize(s.copied);
+            (void)hipEventDestroy(s.copied);
+        }
+        if (s.switched) {
+            if (s.switched_rec)
+                (void)hipEventSynchronize(s.switched); // forwards that read the table in alt
+            (void)hipEventDestroy(s.switched);
+        }
+        if (s.alt)
+            (void)hipFree(s.alt);
+        if (s.h_up)
+            (void)hipHostFree(s.h_up);
+    }
+    for (auto &bt : p->batches) {
+        (void)hipEventSynchronize(bt.done);
+        (void)hipEventDestroy(bt.done);
+    }
+    delete p;
+    return MOE_OK;
+}
+
+int moe_pipeline_stage_table(moe_pipeline *p, int32_t layer, const moe_expert_loc *locs, int32_t n, int32_t n_copy,
+                             const int32_t *copy_expert, const void *const *copy_src)
+{
+    if (!p)
+        return fail(MOE_ERR_INVALID_ARG, "pipeline is null");
+    if (layer < 0 || layer >= p->L)
+        return fail(MOE_ERR_INVALID_ARG, "layer out of range");
+    moe_pipeline::Staged &st = p->staged[layer];
+    if (st.pending)
+        return fail(MOE_ERR_STATE, "layer " + std::to_string(layer) + " already has a change waiting to be applied");
+    moe_pool *h = p->layers[layer];
+    CHECK(moe_validate_locs(&h->desc, locs, n));
+    if (n_copy < 0 || (n_copy > 0 && (!copy_expert || !copy_src)))
+        return fail(MOE_ERR_INVALID_ARG, "copy list is null or negative");
+    // pages this layer may not name: those of the other layers' tables (current
+    // and staged) and dropped pages whose last reading pass has not ended
+    std::vector<int32_t> busy;
+    for (int l = 0; l < p->L; l++) {
+        if (l == layer)
+            continue;
+        for (const auto *t : {&p->current[l], p->staged[l].pending ? &p->staged[l].locs : nullptr})
+            if (t) {
+                const std::vector<int32_t> pg = table_pages(*t);
+                busy.insert(busy.end(), pg.begin(), pg.end());
+            }
+        if (p->staged[l].pending)
+            busy.insert(busy.end(), p->staged[l].dropped.begin(), p->staged[l].dropped.end());
+    }
+    for (const auto &bt : p->batches)
+        busy.insert(busy.end(), bt.pages.begin(), bt.pages.end());
+    std::sort(busy.begin(), busy.end());
+    const std::vector<moe_expert_loc> nt(locs, locs + n);
+    for (int32_t pg : table_pages(nt))
+        if (std::binary_search(busy.begin(), busy.end(), pg))
+            return fail(MOE_ERR_PAGE_ALIAS, "page " + std::to_string(pg) +
+                                                " belongs to another layer or awaits the end of a pass");
+    const std::vector<int32_t> cur = table_pages(p->current[layer]);
+    std::vector<char> copied(n, 0);
+    for (int i = 0; i < n_copy; i++) {
+        const int e = copy_expert[i];
+        if (e < 0 || e >= n || locs[e].kind != MOE_LOC_POOL)
+            return fail(MOE_ERR_INVALID_ARG, "copied expert " + std::to_string(e) + " must be a pool expert of the new table");
+        if (copied[e])
+            return fail(MOE_ERR_INVALID_ARG, "expert " + std::to_string(e) + " listed twice in the copy list");
+        copied[e] = 1;
+        for (int m = 0; m < 3; m++)
+            if (std::binary_search(cur.begin(), cur.end(), locs[e].idx[m]))
+                return fail(MOE_ERR_PAGE_ALIAS, "page " + std::to_string(locs[e].idx[m]) +
+                                                    " is read by the current table and cannot receive a copy");
+        if (!copy_src[i] || !is_pinned(copy_src[i]))
+            return fail(MOE_ERR_INVALID_ARG, "copy sources must be pinned host memory");
+    }
+    if (st.copied_rec)
+        HIP_TRY(hipEventSynchronize(st.copied)); // the last upload from h_up has finished
+    std::memcpy(st.h_up, locs, sizeof(moe_expert_loc) * n);
+    if (st.switched_rec)
+        HIP_TRY(hipStreamWaitEvent(p->copy, st.switched, 0)); // no forward reads alt any more
+    HIP_TRY(hipMemcpyAsync(st.alt, st.h_up, sizeof(moe_expert_loc) * n, hipMemcpyHostToDevice, p->copy));
+    const int64_t fd = (int64_t)h->desc.f * h->desc.d;
+    char *pool = (char *)h->desc.pool_base;
+    for (int i = 0; i < n_copy; i++) {
+        const moe_expert_loc &L = locs[copy_expert[i]];
+        for (int m = 0; m < 3; m++)
+            HIP_TRY(hipMemcpyAsync(pool + (int64_t)L.idx[m] * fd * 2, (const char *)copy_src[i] + m * fd * 2, fd * 2,
+                                   hipMemcpyHostToDevice, p->copy));
+    }
+    HIP_TRY(hipEventRecord(st.copied, p->copy));
+    st.copied_rec = true;
+    st.locs.assign(locs, locs + n);
+    const std::vector<int32_t> nxt = table_pages(st.locs);
+    st.dropped.clear();
+    std::set_difference(cur.begin(), cur.end(), nxt.begin(), nxt.end(), std::back_inserter(st.dropped));
+    st.pending = true;
+    return MOE_OK;
+}
+
+int moe_pipeline_prefetch(moe_pipeline *p, int32_t layer, int32_t n, const int32_t *slots, const void *const *host_src)
+{
+    if (!p)
+        return fail(MOE_ERR_INVALID_ARG, "pipeline is null");
+    if (layer < 0 || layer >= p->L)
+        return fail(MOE_ERR_INVALID_ARG, "layer out of range");
+    moe_pool *h = p->layers[layer];
+    if (h->desc.loadbuf_slots <= 0)
+        return fail(MOE_ERR_STATE, "the layers have no load buffers");
+    if (n < 0 || n > h->desc.loadbuf_slots || (n > 0 && (!slots || !host_src)))
+        return fail(MOE_ERR_INVALID_ARG, "bad slot list");
+    std::vector<char> seen(h->desc.loadbuf_slots, 0);
+    for (int i = 0; i < n; i++) {
+        if (slots[i] < 0 || slots[i] >= h->desc.loadbuf_slots || seen[slots[i]])
+            return fail(MOE_ERR_SLOT_RANGE, "slot " + std::to_string(slots[i]) + " out of range or listed twice");
+        seen[slots[i]] = 1;
+        if (!host_src[i] || !is_pinned(host_src[i]))
+            return fail(MOE_ERR_INVALID_ARG, "host_src must be pinned host memory");
+    }
+    const int b = layer & 1;
+    if (p->unread[b] && p->filled_for[b] != layer)
+        return fail(MOE_ERR_STATE, "load buffer " + std::to_string(b) + " still holds the experts of layer " +
+                                       std::to_string(p->filled_for[b]) + ", which has not run yet");
+    if (p->consumed_rec[b])
+        HIP_TRY(hipStreamWaitEvent(p->copy, p->consumed[b], 0)); // the previous reader of buffer b is done
+    const size_t bytes = (size_t)3 * h->desc.f * h->desc.d * 2;
+    char *dst0 = (char *)h->desc.loadbuf_base[b];
+    for (int i = 0; i < n; i++)
+        HIP_TRY(hipMemcpyAsync(dst0 + (size_t)slots[i] * bytes, host_src[i], bytes, hipMemcpyHostToDevice, p->copy));
+    HIP_TRY(hipEventRecord(p->filled[b], p->copy));
+    p->filled_rec[b] = true;
+    p->filled_for[b] = layer;
+    p->unread[b] = true;
+    return MOE_OK;
+}
+
+int moe_pipeline_forward(moe_pipeline *p, int32_t layer, const void *x, int64_t T, int32_t block_m,
+                         const int32_t *topk_ids, const float *topk_w, const int32_t *sorted_ids,
+                         const int32_t *block_expert, const int32_t *num_padded, void *y, void *ws, size_t ws_bytes,
+                         uint32_t flags, void *stream)
+{
+    if (!p)
+        return fail(MOE_ERR_INVALID_ARG, "pipeline is null");
+    if (layer < 0 || layer >= p->L)
+        return fail(MOE_ERR_INVALID_ARG, "layer out of range");
+    moe_pool *h = p->layers[layer];
+    hipStream_t s = (hipStream_t)stream;
+    moe_pipeline::Staged &st = p->staged[layer];
+    const std::vector<moe_expert_loc> &tab = st.pending ? st.locs : p->current[layer];
+    bool uses_lb = false;
+    for (const auto &L : tab)
+        uses_lb |= L.kind == MOE_LOC_LOADBUF;
+    const int b = layer & 1;
+    if (uses_lb && p->filled_for[b] != layer)
+        return fail(MOE_ERR_STATE, "layer " + std::to_string(layer) + " reads load buffer " + std::to_string(b) +
+                                       ", which was last filled for another layer");
+    if (p->fwd_set && s != p->fwd)
+        return fail(MOE_ERR_INVALID_ARG, "all forwards of a pipeline must run on one stream");
+    p->fwd = s;
+    p->fwd_set = true;
+    if (st.pending) {
+        // finish copying (pages and the table) before pointing the layer at the new table
+        HIP_TRY(hipStreamWaitEvent(s, st.copied, 0));
+        std::swap(h->d_locs, st.alt);
+        HIP_TRY(hipEventRecord(st.switched, s));
+        st.switched_rec = true;
+        h->uses_loadbuf = uses_lb;
+        if (h->upload_pending) {
+            HIP_TRY(hipEventSynchronize(h->upload_done));
+            h->upload_pending = false;
+        }
+        std::memcpy(h->h_stage, st.locs.data(), sizeof(moe_expert_loc) * st.locs.size());
+        p->current[layer] = st.locs;
+        st.pending = false;
+        if (!st.dropped.empty()) {
+            // every earlier forward that may read the dropped pages is on s already
+            moe_pipeline::Batch bt;
+            bt.pages.swap(st.dropped);
+            HIP_TRY(hipEventCreateWithFlags(&bt.done, hipEventDisableTiming));
+            const hipError_t e = hipEventRecord(bt.done, s);
+            if (e != hipSuccess) {
+                (void)hipEventDestroy(bt.done);
+                return hip_fail(e, "hipEventRecord");
+            }
+            p->batches.push_back(std::move(bt));
+        }
+    }
+    if (T > 0 && uses_lb) {
+        const hipError_t q = hipEventQuery(p->filled[b]);
+        if (q == hipErrorNotReady) {
+            (void)hipGetLastError();
+            HIP_TRY(hipStreamWaitEvent(s, p->filled[b], 0));
+        } else if (q != hipSuccess) {
+            return hip_fail(q, "hipEventQuery");
+        }
+    }
+    CHECK(forward_common(h, nullptr, nullptr, true, x, T, block_m, topk_ids, topk_w, sorted_ids, block_expert,
+                         num_padded, b, y, ws, ws_bytes, flags, s, nullptr));
+    if (T > 0 && uses_lb) {
+        HIP_TRY(hipEventRecord(p->consumed[b], s));
+        p->consumed_rec[b] = true;
+    }
+    if (p->filled_for[b] == layer)
+        p->unread[b] = false;
+    return MOE_OK;
+}
+
+int moe_pipeline_reclaim(moe_pipeline *p, int32_t *pages, int32_t cap, int32_t *n)
+{
+    if (!p || !n || cap < 0 || (cap > 0 && !pages))
+        return fail(MOE_ERR_INVALID_ARG, "bad arguments");
+    for (size_t i = 0; i < p->batches.size();) {
+        const hipError_t q = hipEventQuery(p->batches[i].done);
+        if (q == hipErrorNotReady) {
+            (void)hipGetLastError();
+            i++;
+            continue;
+        }
+        if (q != hipSuccess)
+            return hip_fail(q, "hipEventQuery");
+        p->ready.insert(p->ready.end(), p->batches[i].pages.begin(), p->batches[i].pages.end());
+        (void)hipEventDestroy(p->batches[i].done);
+        p->batches.erase(p->batches.begin() + i);
+    }
+    const int32_t m = (int32_t)std::min<size_t>(p->ready.size(), (size_t)cap);
+    for (int32_t i = 0; i < m; i++)
+        pages[i] = p->ready[i];
+    p->ready.erase(p->ready.begin(), p->ready.begin() + m);
+    *n = m;
+    return MOE_OK;
 }
 
 } // extern "C"

@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol(lib):
     for name in sorted(declared):
         assert hasattr(lib, name), f"{name} declared in include/ but not exported"
     assert declared == set(pm.EXPORTS)
-    assert lib.moe_version() == 100
+    assert lib.moe_version() == 101
 
 
 def _desc(**kw):
@@ -120,6 +120,24 @@ def test_null_handles_rejected(lib):
     assert lib.moe_paged_forward(None, None, 1, 16, None, None, None, None, None, 0, None, None, 0, 0,
                                  None) == pm.MOE_ERR_INVALID_ARG
     assert lib.moe_pool_destroy(None) == pm.MOE_OK
+
+
+def test_pipeline_host_checks(lib):
+    """Argument errors of the pipeline entry points are caught before any device call."""
+    E = pm.MOE_ERR_INVALID_ARG
+    h = ctypes.c_void_p()
+    assert lib.moe_pipeline_create(0, None, None, ctypes.byref(h)) == E
+    assert lib.moe_pipeline_create(1, None, None, None) == E
+    two_null = (ctypes.c_void_p * 2)(None, None)
+    assert lib.moe_pipeline_create(2, two_null, None, ctypes.byref(h)) == E
+    assert not h.value
+    assert lib.moe_pipeline_destroy(None) == pm.MOE_OK
+    n = ctypes.c_int32()
+    assert lib.moe_pipeline_reclaim(None, None, 0, ctypes.byref(n)) == E
+    assert lib.moe_pipeline_stage_table(None, 0, None, 0, 0, None, None) == E
+    assert lib.moe_pipeline_prefetch(None, 0, 0, None, None) == E
+    assert lib.moe_pipeline_forward(None, 0, None, 1, 16, None, None, None, None, None, None, None, 0, 0,
+                                    None) == E
 
 
 def test_library_has_no_oracle_dependency():
