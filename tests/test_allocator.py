@@ -1,0 +1,300 @@
+"""The three-tier page pool: its oracle pinned to the digest's section "One
+pool for data whose sizes differ by orders of magnitude" (worked example,
+split-down order, merge-up, same-request packing, invariants), and the
+library's allocator compared with the oracle decision by decision.  CPU only."""
+import json
+import math
+import os
+import random
+
+import pytest
+
+from oracle import allocator as ao
+from oracle.allocator import CONV, KV, AllocError, Pool
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def _run_steps(make, steps, apply):
+    for st in steps:
+        apply(make, st)
+
+
+# ----------------------------------------------------------------------------- worked example
+
+def _golden():
+    with open(os.path.join(HERE, "golden", "allocator_example.json")) as f:
+        return json.load(f)
+
+
+def _apply_oracle(p: Pool, st):
+    op = st["op"]
+    if op == "alloc_kv":
+        if st["expect"] == "fail":
+            with pytest.raises(AllocError):
+                p.alloc_small(KV, st["request"], st["n"])
+        else:
+            assert p.alloc_small(KV, st["request"], st["n"]) == st["expect"], st
+    elif op == "alloc_expert":
+        if st["expect"] == "fail":
+            with pytest.raises(AllocError):
+                p.alloc_expert(st["n"])
+        else:
+            assert p.alloc_expert(st["n"]) == st["expect"], st
+    elif op == "free_request":
+        p.free_request(st["request"])
+    elif op == "stats":
+        s = p.stats()
+        for k, v in st["expect"].items():
+            assert s[k] == v, (st, s)
+
+
+def test_oracle_worked_example():
+    g = _golden()
+    p = Pool(**g["pool"])
+    for st in g["steps"]:
+        _apply_oracle(p, st)
+
+
+# ----------------------------------------------------------------------------- split-down order
+
+def test_split_down_order():
+    # two huge pages of two expert pages each; four KV pages per expert page
+    p = Pool(pool_bytes=4 * 4096, expert_bytes=4096, kv_bytes=1024, ssm_bytes=0)
+    assert p.n_huge == 4  # no SSM: the huge page is the expert page
+    p = Pool(pool_bytes=2 * 8192, expert_bytes=4096, kv_bytes=1024, ssm_bytes=8192)
+    assert p.huge_bytes == 8192 and p.n_huge == 2 and p.e_per_huge == 2
+    assert p.alloc_expert(1) == [0]                 # splits huge page 0
+    assert p.stats()["free_huge"] == 1
+    # a KV request splits the free expert page 1 before touching huge page 1
+    assert p.alloc_small(KV, 1, 1) == [4]
+    assert p.stats()["free_huge"] == 1
+    # the next KV request takes a small page that is already split off
+    assert p.alloc_small(KV, 2, 1) == [5]
+    # no free expert page is left in huge page 0: the next expert splits huge page 1
+    assert p.alloc_expert(1) == [2]
+    assert p.huge == ["expert", "expert"]
+
+
+def test_never_cuts_huge_into_small_pages():
+    p = Pool(pool_bytes=3 * 6144, expert_bytes=2048, kv_bytes=512, ssm_bytes=3072, conv_bytes=256)
+    assert p.huge_bytes == 6144  # lcm(2048, 3072)
+    p.alloc_ssm(2)                                   # huge page 0 becomes SSM pages
+    assert p.huge[0] == "ssm"
+    qs = p.alloc_small(KV, 7, 12)                    # 12 KV pages = 3 expert pages = huge page 1
+    assert p.huge[1] == "expert"
+    assert sorted({p.mid_of_small(KV, q) for q in qs}) == [3, 4, 5]
+    # small pages only ever come out of expert pages of an expert-split huge page
+    for (k, q), o in p.small.items():
+        m = p.mid_of_small(k, q)
+        assert p.mid[m] == ("split", k)
+        assert p.huge[p.huge_of_mid(m)] == "expert"
+    # SSM pages of huge page 0 never host small pages
+    assert p.alloc_small(CONV, 8, 1) == [6 * 8]      # splits expert page 6 (huge page 2)
+
+
+# ----------------------------------------------------------------------------- merge-up
+
+def test_merge_up_to_whole_pool():
+    # SSM pages of 8192 bytes make the huge page two expert pages
+    p = Pool(pool_bytes=2 * 8192, expert_bytes=4096, kv_bytes=1024, ssm_bytes=8192)
+    assert p.e_per_huge == 2
+    e = p.alloc_expert(2)
+    kv = p.alloc_small(KV, 1, 6)
+    assert p.stats()["free_huge"] == 0
+    p.free_small(KV, kv[:4])                         # expert page 2 has all four free again
+    s = p.stats()
+    assert s["free_expert"] == 1 and s["split"] == [1, 0] and s["free_huge"] == 0
+    p.free_small(KV, kv[4:])                         # page 3 free too: huge page 1 merges
+    assert p.stats()["free_huge"] == 1 and p.huge[1] is None
+    p.free_expert(e)
+    assert p.stats()["free_huge"] == 2 and not p.mid and not p.small
+
+
+# ----------------------------------------------------------------------------- same-request packing
+
+@pytest.mark.parametrize("packing", [True, False])
+def test_same_request_packing(packing):
+    p = Pool(pool_bytes=4 * 4096, expert_bytes=4096, kv_bytes=1024, packing=packing)
+    a = p.alloc_small(KV, 1, 4)                      # request 1 fills expert page 0
+    b = p.alloc_small(KV, 2, 4)                      # request 2 fills expert page 1
+    assert a == [0, 1, 2, 3] and b == [4, 5, 6, 7]
+    p.free_small(KV, [0])
+    p.free_small(KV, [4])
+    got = p.alloc_small(KV, 2, 1)
+    # packing keeps request 2 on its own page; without it the lowest free slot wins
+    assert got == ([4] if packing else [0])
+    before = p.stats()["expert_available"]
+    p.free_request(1)
+    after = p.stats()
+    if packing:
+        assert after["expert_available"] == before + 1 and after["trapped_bytes"] == 0
+    else:
+        # page 0 keeps request 2's page: its three free slots and page 1's free slot are trapped
+        assert after["expert_available"] == before and after["trapped_bytes"] == 4 * 1024
+
+
+# ----------------------------------------------------------------------------- closed forms
+
+@pytest.mark.parametrize("n", [1, 3, 4, 5, 16, 17])
+def test_closed_forms_fresh_pool(n):
+    per = 4
+    p = Pool(pool_bytes=8 * 4096, expert_bytes=4096, kv_bytes=4096 // per)
+    qs = p.alloc_small(KV, 1, n)
+    assert qs == list(range(n))
+    assert p.stats()["split"][KV] == math.ceil(n / per)
+    assert p.stats()["expert_available"] == 8 - math.ceil(n / per)
+    p2 = Pool(pool_bytes=8 * 4096, expert_bytes=4096, kv_bytes=1024)
+    assert p2.alloc_expert(min(n, 8)) == list(range(min(n, 8)))
+
+
+def test_capacity_and_all_or_nothing():
+    p = Pool(pool_bytes=4 * 4096, expert_bytes=4096, kv_bytes=512)
+    assert len(p.alloc_small(KV, 1, 4 * 8)) == 32     # the whole pool as KV pages
+    with pytest.raises(AllocError):
+        p.alloc_small(KV, 2, 1)
+    p.free_request(1)
+    p.alloc_expert(3)
+    snap = (list(p.huge), dict(p.mid), dict(p.small))
+    with pytest.raises(AllocError):
+        p.alloc_small(KV, 3, 9)                        # 8 fit, 9 do not: nothing changes
+    with pytest.raises(AllocError):
+        p.alloc_expert(2)
+    assert (list(p.huge), dict(p.mid), dict(p.small)) == snap
+    assert len(p.alloc_small(KV, 3, 8)) == 8
+
+
+def test_bad_arguments():
+    with pytest.raises(ValueError):
+        Pool(pool_bytes=4096, expert_bytes=4096, kv_bytes=3000)          # does not divide the page
+    with pytest.raises(ValueError):
+        Pool(pool_bytes=5000, expert_bytes=4096, kv_bytes=1024)          # not whole huge pages
+    with pytest.raises(ValueError):
+        Pool(pool_bytes=3 * 4096, expert_bytes=4096, kv_bytes=1024, ssm_bytes=8192)  # lcm 8192
+    p = Pool(pool_bytes=2 * 4096, expert_bytes=4096, kv_bytes=1024)
+    e = p.alloc_expert(1)
+    p.free_expert(e)
+    with pytest.raises(ValueError):
+        p.free_expert(e)                                                  # double free
+    q = p.alloc_small(KV, 1, 1)
+    with pytest.raises(ValueError):
+        p.free_small(KV, q + q)
+    with pytest.raises(ValueError):
+        p.alloc_ssm(1)
+
+
+# ----------------------------------------------------------------------------- invariants on random sequences
+
+def random_ops(seed: int, n_ops: int, ssm: bool, conv: bool):
+    """A seeded mix of allocations and frees (the host-side workload both sides replay)."""
+    g = random.Random(seed)
+    ops = []
+    reqs = list(range(1, 40))
+    for _ in range(n_ops):
+        r = g.random()
+        if r < 0.35:
+            ops.append(("alloc_kv", g.choice(reqs), g.randint(1, 6)))
+        elif r < 0.45 and conv:
+            ops.append(("alloc_conv", g.choice(reqs), g.randint(1, 2)))
+        elif r < 0.6:
+            ops.append(("free_request", g.choice(reqs)))
+        elif r < 0.72:
+            ops.append(("alloc_expert", g.randint(1, 3)))
+        elif r < 0.84:
+            ops.append(("free_expert", g.randint(1, 3)))
+        elif r < 0.92 and ssm:
+            ops.append(("alloc_ssm", g.randint(1, 2)))
+        elif ssm:
+            ops.append(("free_ssm", g.randint(1, 2)))
+    return ops
+
+
+POOLS = {
+    "plain": dict(pool_bytes=12 * 4096, expert_bytes=4096, kv_bytes=512),
+    "hybrid": dict(pool_bytes=4 * 12288, expert_bytes=4096, kv_bytes=1024, ssm_bytes=6144, conv_bytes=256),
+}
+
+
+def replay_oracle(p: Pool, ops, seed: int):
+    """Apply ops; frees pick victims with a seeded generator from the live sets.
+    Yields (op, result) with result a page list, 'fail' or a freed count."""
+    g = random.Random(seed ^ 0x5EED)
+    live_e, live_s = [], []
+    for op in ops:
+        kind = op[0]
+        try:
+            if kind in ("alloc_kv", "alloc_conv"):
+                res = p.alloc_small(KV if kind == "alloc_kv" else CONV, op[1], op[2])
+            elif kind == "alloc_expert":
+                res = p.alloc_expert(op[1])
+                live_e += res
+            elif kind == "alloc_ssm":
+                res = p.alloc_ssm(op[1])
+                live_s += res
+            elif kind == "free_expert":
+                k = min(op[1], len(live_e))
+                res = sorted(g.sample(live_e, k))
+                for x in res:
+                    live_e.remove(x)
+                p.free_expert(res)
+            elif kind == "free_ssm":
+                k = min(op[1], len(live_s))
+                res = sorted(g.sample(live_s, k))
+                for x in res:
+                    live_s.remove(x)
+                p.free_ssm(res)
+            else:
+                res = p.free_request(op[1])
+        except AllocError:
+            res = "fail"
+        yield op, res
+
+
+def _check_invariants(p: Pool):
+    r = p.byte_ranges()
+    for a, b in zip(r, r[1:]):
+        assert a[1] <= b[0], f"overlap {a} {b}"
+    s = p.stats()
+    used = (s["used_expert"] * p.expert_bytes + s["used_ssm"] * p.ssm_bytes
+            + sum(s["used_small"][k] * p.small_bytes[k] for k in (KV, CONV)))
+    free = (s["free_huge"] * p.huge_bytes + s["free_expert"] * p.expert_bytes + s["free_ssm"] * p.ssm_bytes
+            + s["trapped_bytes"])
+    assert used + free == p.n_huge * p.huge_bytes
+    for k in (KV, CONV):
+        assert s["split"][k] * p.expert_bytes == (s["used_small"][k] + s["free_small"][k]) * (p.small_bytes[k] or 1) \
+            or s["split"][k] == 0
+    # merge-up is complete: no split page whose children are all free
+    for m, v in p.mid.items():
+        if isinstance(v, tuple):
+            k = v[1]
+            n = p.per_mid(k)
+            assert any(p.small[(k, q)] is not None for q in range(m * n, (m + 1) * n))
+    for h, v in enumerate(p.huge):
+        if v == "expert":
+            assert any(p.mid[m] != "free" for m in range(h * p.e_per_huge, (h + 1) * p.e_per_huge))
+        elif v == "ssm":
+            assert any(p.ssm[x] != "free" for x in range(h * p.s_per_huge, (h + 1) * p.s_per_huge))
+
+
+@pytest.mark.parametrize("pool", sorted(POOLS))
+@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("packing", [True, False])
+def test_oracle_invariants(pool, seed, packing):
+    p = Pool(**POOLS[pool], packing=packing)
+    ops = random_ops(seed, 400, ssm=pool == "hybrid", conv=pool == "hybrid")
+    fails = 0
+    for op, res in replay_oracle(p, ops, seed):
+        _check_invariants(p)
+        if res == "fail":
+            fails += 1
+            # a refusal means the pool really is short
+            if op[0] == "alloc_expert":
+                assert p.expert_pages_available() < op[1]
+    assert fails < len(ops)
+    # free everything: the pool is whole again
+    for r in range(1, 40):
+        p.free_request(r)
+    p.free_expert(sorted(m for m, v in p.mid.items() if v == "used"))
+    if p.ssm_bytes:
+        p.free_ssm(sorted(x for x, v in p.ssm.items() if v == "used"))
+    assert p.stats()["free_huge"] == p.n_huge and not p.mid and not p.ssm and not p.small
