@@ -82,6 +82,11 @@ def parse():
                     help="time an L-layer pass through moe_pipeline_* instead (one JSON line of its own)")
     ap.add_argument("--layers", type=int, default=8, help="--pipeline: layers per pass")
     ap.add_argument("--offloaded", type=int, default=1, help="--pipeline: experts per layer via the load buffer")
+    ap.add_argument("--allocator", action="store_true",
+                    help="time the three-tier page allocator under a serving churn (host only; one JSON line)")
+    ap.add_argument("--placement", default="synth", choices=("synth", "allocator"),
+                    help="pages of the pool experts: a seeded permutation, or handed out by the page allocator "
+                         "during a seeded KV / eviction churn")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB fp32 read + 1 GiB write elementwise kernel (scales HBM counters)")
     return ap.parse_args()
@@ -107,6 +112,9 @@ def main():
     if args.pipeline and args.gpus == 1:
         pipeline_bench(args)
         return
+    if args.allocator:
+        allocator_bench(args)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the layer's hot path runs on a single MI355X and there is no "
               "multi-GPU path (experts would shard across GPUs with an all-to-all of routed tokens, not "
@@ -130,6 +138,8 @@ def main():
     T = args.T if args.T is not None else (1 if name == "decode" else s.T)
     t0 = time.time()
     layer = synth.make_layer(s, T)
+    if args.placement == "allocator":
+        layer = allocator_placed(layer)
     dev = wdev.to_device(layer)
     print(f"# layer {name} T={T} generated and placed in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
 
@@ -301,6 +311,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": WORKLOAD_TEXT[name], "name": name, "T": T, "block_m": bm,
+                   "placement": args.placement,
                    "combine": "atomic" if args.atomic else "ordered", "layer_copies_rotated": R},
         "hbm_gbs": round(gbs, 1),
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
@@ -322,6 +333,114 @@ def main():
     print(json.dumps(line), flush=True)
     for c in copies:
         c["h"].close()
+
+
+def allocator_placed(layer):
+    """The layer with its pool experts placed by the page allocator during a seeded
+    serving churn (KV pages of f*d*2 / kv_pages_per_hole bytes, else 64 KiB)."""
+    import numpy as np
+
+    import paged_expert_weight_amd as pm
+    from paged_expert_weight_amd import placement
+    from workloads import churn, synth
+    s = layer.spec
+    locs0 = layer.placement.locs
+    slots = {e: int(locs0[e]["idx"][0]) for e in range(s.E_tot) if locs0[e]["kind"] == synth.LOC_LOADBUF}
+    pool_experts = [e for e in range(s.E_tot) if e not in slots]
+    e_bytes = s.f * s.d * 2
+    kv_bytes = e_bytes // s.kv_pages_per_hole if s.kv_pages_per_hole else 64 * 1024
+    alloc = pm.PageAllocator(s.pool_pages * e_bytes, e_bytes, kv_bytes)
+    spare = s.pool_pages - 3 * len(pool_experts)
+    r = placement.replay(alloc, pool_experts, churn.events(s.seed, len(pool_experts), 300,
+                                                           arrivals=max(1.0, spare / 8.0)))
+    locs = placement.location_table(s.E_tot, r["pages"], slots)
+    per = e_bytes // kv_bytes
+    holes = sorted({q // per for v in r["kv"].values() for q in v})
+    used = sorted(p for v in r["pages"].values() for p in v)
+    free = sorted(set(range(s.pool_pages)) - set(used) - set(holes))
+    pl = synth.Placement(locs, np.asarray(used, np.int64), np.asarray(holes, np.int64), np.asarray(free, np.int64),
+                         layer.placement.slot_expert)
+    runs = 1 + sum(1 for a, b in zip(used, used[1:]) if b != a + 1)
+    print(f"# allocator placement: expert pages in {runs} runs, {len(holes)} pages split into KV pages",
+          file=sys.stderr, flush=True)
+    return synth.Layer(s, layer.x, layer.logits, layer.w13, layer.w2, pl)
+
+
+def allocator_bench(args):
+    """The page allocator under a serving churn on a 64 GiB pool of 2 MiB expert
+    pages (Qwen3-Next-shaped: f=512, d=2048) and 32 KiB KV pages (16 tokens):
+    host microseconds per call through the C ABI, and the space that KV pages
+    trap inside expert pages, with and without same-request packing."""
+    import numpy as np
+
+    import paged_expert_weight_amd as pm
+    from workloads import churn
+
+    e_bytes, kv_bytes = 512 * 2048 * 2, 32 * 1024
+    n_pages = 32768
+    n_experts = 6000  # 18 000 expert pages resident at the start
+    ev = churn.events(7, n_experts, 4000, arrivals=12.0, mean_life=60.0, evict_rate=0.5)
+    out = {}
+    for packing in (True, False):
+        a = pm.PageAllocator(n_pages * e_bytes, e_bytes, kv_bytes, packing=packing)
+        pages = {e: a.alloc_expert(3) for e in range(n_experts)}
+        kv = {}
+        trapped, avail = [], []
+        calls = 0
+        t_alloc = t_free = 0.0
+        n_kv_pages = 0
+        n_alloc_calls = 0
+        refused = 0
+        for i, e in enumerate(ev):
+            t0 = time.perf_counter()
+            if e[0] == "req" or (e[0] == "grow" and e[1] in kv):
+                try:
+                    got = a.alloc_small(pm.MOE_PAGE_KV, e[1], e[2])
+                    kv[e[1]] = kv.get(e[1], []) + got
+                    n_kv_pages += e[2]
+                    n_alloc_calls += 1
+                except pm.MoeError:
+                    refused += 1
+                t_alloc += time.perf_counter() - t0
+            elif e[0] == "done":
+                if kv.pop(e[1], None) is not None:
+                    a.free_request(e[1])
+                t_free += time.perf_counter() - t0
+            elif e[0] == "evict" and e[1] in pages:
+                a.free_expert(pages.pop(e[1]))
+            elif e[0] == "add" and e[1] not in pages:
+                try:
+                    pages[e[1]] = a.alloc_expert(3)
+                except pm.MoeError:
+                    pass
+            calls += 1
+            if i % 50 == 0:
+                st = a.stats()
+                trapped.append(st["trapped_bytes"])
+                avail.append(st["expert_available"])
+        st = a.stats()
+        n_done = sum(1 for e in ev if e[0] == "done")
+        out["packing" if packing else "no_packing"] = {
+            "mean_trapped_mib": round(float(np.mean(trapped)) / 2**20, 1),
+            "max_trapped_mib": round(float(np.max(trapped)) / 2**20, 1),
+            "mean_expert_pages_available": round(float(np.mean(avail)), 1),
+            "refused_requests": refused,
+            "us_per_alloc_call": round(t_alloc / max(1, n_alloc_calls) * 1e6, 2),
+            "us_per_kv_page": round(t_alloc / max(1, n_kv_pages) * 1e6, 3),
+            "us_per_request_free": round(t_free / max(1, n_done) * 1e6, 2),
+            "final_split_pages": st["split"][0],
+        }
+        print(f"# packing={packing}: {out['packing' if packing else 'no_packing']}", file=sys.stderr, flush=True)
+        a.close()
+    line = {"metric": "three-tier page allocator: host us per call and trapped KV space under churn",
+            "value": out["packing"]["us_per_kv_page"], "unit": "us/KV page", "higher_is_better": False,
+            "n_gpus": 0, "data": "synthetic",
+            "config": {"workload": "64 GiB pool of 2 MiB expert pages, 32 KiB KV pages (16 tokens); 6000 experts "
+                                   "resident at the start; 4000 decode steps; log-normal prompt lengths (median "
+                                   "300 tokens), one more KV page per 16 generated tokens, random expert evictions "
+                                   "and re-adds", "events": len(ev)},
+            "results": out}
+    print(json.dumps(line), flush=True)
 
 
 def pipeline_bench(args):

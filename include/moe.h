@@ -59,6 +59,7 @@ extern "C" {
 #define MOE_ERR_STATE (-7)       /* double-buffer misuse, e.g. reading a never-filled buffer */
 #define MOE_ERR_HIP (-8)         /* a HIP runtime call failed */
 #define MOE_ERR_UNSUPPORTED (-9) /* shape the kernels do not handle (see moe_pool_desc) */
+#define MOE_ERR_NO_SPACE (-10)   /* the page pool cannot serve the request (nothing changed) */
 
 /* kinds of one location-table entry */
 #define MOE_LOC_POOL 0    /* idx = {W1 page, W3 page, W2 page} */
@@ -391,6 +392,75 @@ int moe_pipeline_forward(moe_pipeline *pipe, int32_t layer, const void *x, int64
  * *n; pages beyond cap are reported by the next call.
  */
 int moe_pipeline_reclaim(moe_pipeline *pipe, int32_t *pages, int32_t cap, int32_t *n);
+
+/* ---------------------------------------------------------------- three-tier page pool
+ * Host-side allocator of the digest's section "One pool for data whose sizes
+ * differ by orders of magnitude".  The pool is one byte range seen through a
+ * view per page kind: page i of a kind of B bytes covers bytes [i*B, (i+1)*B),
+ * so an expert page index is the page number moe_expert_loc takes (with
+ * expert_page_bytes = f*d*2) and a KV page index addresses the KV cache view
+ * of the same bytes.
+ *
+ * Tiers: huge pages of lcm(expert, SSM) bytes (the expert page without SSM
+ * layers) split into expert or SSM pages; an expert page splits into KV or
+ * convolution-state pages (small pages are carved from expert pages only, so
+ * their sizes must divide the expert page).  A small-page request takes, in
+ * order: a free slot of an expert page that already holds pages of the same
+ * request (same-request packing; off with MOE_ALLOC_NO_PACKING), a free slot
+ * of any split page of that kind, a free expert page split now, a free huge
+ * page split into expert pages now.  Expert and SSM requests take a free page
+ * of their kind, else split a free huge page.  Among equals the lowest index
+ * wins.  Frees merge upward at once: an expert page whose small pages are all
+ * free becomes a free expert page, and a huge page whose pages are all free
+ * returns to the pool.  Requests for n pages are all or nothing
+ * (MOE_ERR_NO_SPACE leaves the pool unchanged).  Not thread-safe: one caller
+ * at a time per allocator.  No call touches the GPU.
+ */
+typedef struct moe_alloc moe_alloc;
+
+#define MOE_PAGE_KV 0
+#define MOE_PAGE_CONV 1
+#define MOE_ALLOC_NO_PACKING 1u
+
+typedef struct {
+    int64_t pool_bytes;        /* a whole number of huge pages */
+    int64_t expert_page_bytes; /* > 0 */
+    int64_t ssm_page_bytes;    /* 0: no SSM pages */
+    int64_t kv_page_bytes;     /* > 0, divides expert_page_bytes */
+    int64_t conv_page_bytes;   /* 0: no convolution-state pages; else divides expert_page_bytes */
+    uint32_t flags;            /* MOE_ALLOC_NO_PACKING */
+} moe_alloc_desc;
+
+typedef struct {
+    int64_t huge_bytes, n_huge;
+    int64_t free_huge;                    /* whole huge pages */
+    int64_t free_expert, used_expert;     /* expert pages of split huge pages */
+    int64_t free_ssm, used_ssm;
+    int64_t split[2];                     /* expert pages split into KV / conv pages */
+    int64_t used_small[2], free_small[2]; /* small pages inside those split pages */
+    int64_t expert_available;             /* free_expert + free_huge * (huge / expert page) */
+    int64_t trapped_bytes;                /* free small pages that cannot hold an expert yet */
+} moe_alloc_stats;
+
+/* MOE_ERR_INVALID_ARG for sizes that break the rules above or unknown flags. */
+int moe_alloc_create(const moe_alloc_desc *desc, moe_alloc **out);
+int moe_alloc_destroy(moe_alloc *a); /* NULL is a no-op */
+
+/* n pages into pages[n] (host).  Frees take distinct allocated pages of that
+ * kind (MOE_ERR_INVALID_ARG otherwise, with nothing freed). */
+int moe_alloc_expert_pages(moe_alloc *a, int32_t n, int64_t *pages);
+int moe_free_expert_pages(moe_alloc *a, int32_t n, const int64_t *pages);
+int moe_alloc_ssm_pages(moe_alloc *a, int32_t n, int64_t *pages);
+int moe_free_ssm_pages(moe_alloc *a, int32_t n, const int64_t *pages);
+
+/* kind: MOE_PAGE_KV or MOE_PAGE_CONV; request >= 0 names the owner (packing). */
+int moe_alloc_small_pages(moe_alloc *a, int32_t kind, int64_t request, int32_t n, int64_t *pages);
+int moe_free_small_pages(moe_alloc *a, int32_t kind, int32_t n, const int64_t *pages);
+
+/* Free every small page of one request (KV, then conv, ascending). */
+int moe_free_request(moe_alloc *a, int64_t request, int64_t *n_freed);
+
+int moe_alloc_get_stats(const moe_alloc *a, moe_alloc_stats *stats);
 
 /* Message for the last non-zero return on this thread ("" if none). */
 const char *moe_last_error(void);

@@ -27,10 +27,14 @@ MOE_ERR_WORKSPACE = -6
 MOE_ERR_STATE = -7
 MOE_ERR_HIP = -8
 MOE_ERR_UNSUPPORTED = -9
+MOE_ERR_NO_SPACE = -10
 
 MOE_LOC_POOL = 0
 MOE_LOC_LOADBUF = 1
 MOE_FLAG_ATOMIC_COMBINE = 1
+MOE_PAGE_KV = 0
+MOE_PAGE_CONV = 1
+MOE_ALLOC_NO_PACKING = 1
 
 # every function moe.h declares
 EXPORTS = (
@@ -41,6 +45,9 @@ EXPORTS = (
     "moe_adjust_amounts", "moe_rank_experts", "moe_adjust_select",
     "moe_pipeline_create", "moe_pipeline_destroy", "moe_pipeline_stage_table", "moe_pipeline_prefetch",
     "moe_pipeline_forward", "moe_pipeline_reclaim",
+    "moe_alloc_create", "moe_alloc_destroy", "moe_alloc_expert_pages", "moe_free_expert_pages",
+    "moe_alloc_ssm_pages", "moe_free_ssm_pages", "moe_alloc_small_pages", "moe_free_small_pages",
+    "moe_free_request", "moe_alloc_get_stats",
 )
 
 
@@ -62,6 +69,20 @@ class moe_pool_desc(ctypes.Structure):
         ("loadbuf_slots", ctypes.c_int32),
         ("loadbuf_base", ctypes.c_void_p * 2),
     ]
+
+
+class moe_alloc_desc(ctypes.Structure):
+    _fields_ = [("pool_bytes", ctypes.c_int64), ("expert_page_bytes", ctypes.c_int64),
+                ("ssm_page_bytes", ctypes.c_int64), ("kv_page_bytes", ctypes.c_int64),
+                ("conv_page_bytes", ctypes.c_int64), ("flags", ctypes.c_uint32)]
+
+
+class moe_alloc_stats(ctypes.Structure):
+    _fields_ = [("huge_bytes", ctypes.c_int64), ("n_huge", ctypes.c_int64), ("free_huge", ctypes.c_int64),
+                ("free_expert", ctypes.c_int64), ("used_expert", ctypes.c_int64), ("free_ssm", ctypes.c_int64),
+                ("used_ssm", ctypes.c_int64), ("split", ctypes.c_int64 * 2), ("used_small", ctypes.c_int64 * 2),
+                ("free_small", ctypes.c_int64 * 2), ("expert_available", ctypes.c_int64),
+                ("trapped_bytes", ctypes.c_int64)]
 
 
 class moe_expert_loc(ctypes.Structure):
@@ -102,6 +123,14 @@ def lib():
     L.moe_pipeline_prefetch.argtypes = [P, i32, i32, P, P]
     L.moe_pipeline_forward.argtypes = [P, i32, P, i64, i32, P, P, P, P, P, P, P, sz, u32, P]
     L.moe_pipeline_reclaim.argtypes = [P, P, i32, P]
+    L.moe_alloc_create.argtypes = [ctypes.POINTER(moe_alloc_desc), ctypes.POINTER(P)]
+    L.moe_alloc_destroy.argtypes = [P]
+    for nm in ("moe_alloc_expert_pages", "moe_free_expert_pages", "moe_alloc_ssm_pages", "moe_free_ssm_pages"):
+        getattr(L, nm).argtypes = [P, i32, P]
+    L.moe_alloc_small_pages.argtypes = [P, i32, i64, i32, P]
+    L.moe_free_small_pages.argtypes = [P, i32, i32, P]
+    L.moe_free_request.argtypes = [P, i64, ctypes.POINTER(i64)]
+    L.moe_alloc_get_stats.argtypes = [P, ctypes.POINTER(moe_alloc_stats)]
     L.moe_suggest_block_m.argtypes = [P, i64]
     L.moe_suggest_block_m.restype = i32
     L.moe_last_error.restype = ctypes.c_char_p
@@ -413,3 +442,73 @@ def adjust_select(ranking, prob, resident, offload_limit: int, n_evict: int, n_a
                                    n.ctypes.data))
     m = int(n[0])
     return [(int(ol[i]), int(oe[i]), int(oa[i])) for i in range(m)], [int(v) for v in res]
+
+
+# ----------------------------------------------------------------------------- three-tier page pool (host)
+
+class PageAllocator:
+    """Owner of one moe_alloc: the three-tier page pool over one byte range."""
+
+    def __init__(self, pool_bytes: int, expert_bytes: int, kv_bytes: int, ssm_bytes: int = 0, conv_bytes: int = 0,
+                 packing: bool = True):
+        d = moe_alloc_desc(pool_bytes, expert_bytes, ssm_bytes, kv_bytes, conv_bytes,
+                           0 if packing else MOE_ALLOC_NO_PACKING)
+        h = ctypes.c_void_p()
+        _check(lib().moe_alloc_create(ctypes.byref(d), ctypes.byref(h)))
+        self.handle = h
+
+    def close(self):
+        if self.handle:
+            _check(lib().moe_alloc_destroy(self.handle))
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    @staticmethod
+    def _pages(n):
+        return np.zeros(max(1, n), dtype=np.int64)
+
+    def alloc_expert(self, n: int):
+        out = self._pages(n)
+        _check(lib().moe_alloc_expert_pages(self.handle, n, out.ctypes.data))
+        return [int(v) for v in out[:n]]
+
+    def free_expert(self, pages):
+        a = np.ascontiguousarray(np.asarray(pages, dtype=np.int64))
+        _check(lib().moe_free_expert_pages(self.handle, a.size, a.ctypes.data if a.size else None))
+
+    def alloc_ssm(self, n: int):
+        out = self._pages(n)
+        _check(lib().moe_alloc_ssm_pages(self.handle, n, out.ctypes.data))
+        return [int(v) for v in out[:n]]
+
+    def free_ssm(self, pages):
+        a = np.ascontiguousarray(np.asarray(pages, dtype=np.int64))
+        _check(lib().moe_free_ssm_pages(self.handle, a.size, a.ctypes.data if a.size else None))
+
+    def alloc_small(self, kind: int, request: int, n: int):
+        out = self._pages(n)
+        _check(lib().moe_alloc_small_pages(self.handle, kind, request, n, out.ctypes.data))
+        return [int(v) for v in out[:n]]
+
+    def free_small(self, kind: int, pages):
+        a = np.ascontiguousarray(np.asarray(pages, dtype=np.int64))
+        _check(lib().moe_free_small_pages(self.handle, kind, a.size, a.ctypes.data if a.size else None))
+
+    def free_request(self, request: int) -> int:
+        n = ctypes.c_int64()
+        _check(lib().moe_free_request(self.handle, request, ctypes.byref(n)))
+        return n.value
+
+    def stats(self) -> dict:
+        s = moe_alloc_stats()
+        _check(lib().moe_alloc_get_stats(self.handle, ctypes.byref(s)))
+        return {"free_huge": s.free_huge, "free_expert": s.free_expert, "used_expert": s.used_expert,
+                "free_ssm": s.free_ssm, "used_ssm": s.used_ssm, "split": list(s.split),
+                "used_small": list(s.used_small), "free_small": list(s.free_small),
+                "expert_available": s.expert_available, "trapped_bytes": s.trapped_bytes,
+                "huge_bytes": s.huge_bytes, "n_huge": s.n_huge}

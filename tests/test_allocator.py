@@ -215,7 +215,7 @@ POOLS = {
 }
 
 
-def replay_oracle(p: Pool, ops, seed: int):
+def replay(p, ops, seed: int):
     """Apply ops; frees pick victims with a seeded generator from the live sets.
     Yields (op, result) with result a page list, 'fail' or a freed count."""
     g = random.Random(seed ^ 0x5EED)
@@ -283,7 +283,7 @@ def test_oracle_invariants(pool, seed, packing):
     p = Pool(**POOLS[pool], packing=packing)
     ops = random_ops(seed, 400, ssm=pool == "hybrid", conv=pool == "hybrid")
     fails = 0
-    for op, res in replay_oracle(p, ops, seed):
+    for op, res in replay(p, ops, seed):
         _check_invariants(p)
         if res == "fail":
             fails += 1
@@ -298,3 +298,122 @@ def test_oracle_invariants(pool, seed, packing):
     if p.ssm_bytes:
         p.free_ssm(sorted(x for x, v in p.ssm.items() if v == "used"))
     assert p.stats()["free_huge"] == p.n_huge and not p.mid and not p.ssm and not p.small
+
+
+# ----------------------------------------------------------------------------- library vs oracle
+
+pm = pytest.importorskip("paged_expert_weight_amd")
+STAT_KEYS = ("free_huge", "free_expert", "used_expert", "free_ssm", "used_ssm", "split", "used_small",
+             "free_small", "expert_available", "trapped_bytes")
+
+
+class LibPool:
+    """The library allocator behind the oracle's interface (errors mapped to the same exceptions)."""
+
+    def __init__(self, pool_bytes, expert_bytes, kv_bytes, ssm_bytes=0, conv_bytes=0, packing=True):
+        try:
+            self.a = pm.PageAllocator(pool_bytes, expert_bytes, kv_bytes, ssm_bytes, conv_bytes, packing)
+        except pm.MoeError as e:
+            raise ValueError(str(e))
+
+    def _call(self, fn, *a):
+        try:
+            return fn(*a)
+        except pm.MoeError as e:
+            if e.code == pm.MOE_ERR_NO_SPACE:
+                raise AllocError(str(e))
+            raise ValueError(str(e))
+
+    def alloc_expert(self, n):
+        return self._call(self.a.alloc_expert, n)
+
+    def free_expert(self, pages):
+        return self._call(self.a.free_expert, pages)
+
+    def alloc_ssm(self, n):
+        return self._call(self.a.alloc_ssm, n)
+
+    def free_ssm(self, pages):
+        return self._call(self.a.free_ssm, pages)
+
+    def alloc_small(self, kind, request, n):
+        return self._call(self.a.alloc_small, kind, request, n)
+
+    def free_small(self, kind, pages):
+        return self._call(self.a.free_small, kind, pages)
+
+    def free_request(self, request):
+        return self._call(self.a.free_request, request)
+
+    def stats(self):
+        return self.a.stats()
+
+
+@pytest.fixture(scope="module")
+def lib():
+    try:
+        return pm.lib()
+    except RuntimeError as e:
+        pytest.skip(str(e))
+
+
+def test_library_worked_example(lib):
+    g = _golden()
+    p = LibPool(**g["pool"])
+    for st in g["steps"]:
+        _apply_oracle(p, st)
+
+
+@pytest.mark.parametrize("pool", sorted(POOLS))
+@pytest.mark.parametrize("seed", range(8))
+@pytest.mark.parametrize("packing", [True, False])
+def test_library_matches_oracle(lib, pool, seed, packing):
+    ops = random_ops(100 + seed, 600, ssm=pool == "hybrid", conv=pool == "hybrid")
+    po = Pool(**POOLS[pool], packing=packing)
+    pl = LibPool(**POOLS[pool], packing=packing)
+    for (op, ro), (op2, rl) in zip(replay(po, ops, seed), replay(pl, ops, seed)):
+        assert op == op2
+        assert rl == ro, op
+        so, sl = po.stats(), pl.stats()
+        assert {k: so[k] for k in STAT_KEYS} == {k: sl[k] for k in STAT_KEYS}, op
+
+
+def test_library_large_pages_many_slots(lib):
+    """Bitmaps wider than one word (200 KV pages per expert page, a partial last word) and a pool of
+    several huge pages."""
+    kw = dict(pool_bytes=6 * 200 * 64, expert_bytes=200 * 64, kv_bytes=64)
+    ops = random_ops(7, 200, ssm=False, conv=False)
+    ops = [(o[0], o[1], o[2] * 30) if o[0] == "alloc_kv" else o for o in ops]
+    po, pl = Pool(**kw), LibPool(**kw)
+    for (op, ro), (_, rl) in zip(replay(po, ops, 7), replay(pl, ops, 7)):
+        assert rl == ro, op
+        assert po.stats()["trapped_bytes"] == pl.stats()["trapped_bytes"]
+
+
+def test_library_rejects(lib):
+    for kw in (dict(pool_bytes=4096, expert_bytes=4096, kv_bytes=3000),
+               dict(pool_bytes=5000, expert_bytes=4096, kv_bytes=1024),
+               dict(pool_bytes=3 * 4096, expert_bytes=4096, kv_bytes=1024, ssm_bytes=8192),
+               dict(pool_bytes=4096, expert_bytes=4096, kv_bytes=0)):
+        with pytest.raises(ValueError):
+            LibPool(**kw)
+    p = LibPool(pool_bytes=2 * 4096, expert_bytes=4096, kv_bytes=1024)
+    e = p.alloc_expert(1)
+    with pytest.raises(ValueError):
+        p.free_expert(e + e)                        # listed twice: nothing freed
+    p.free_expert(e)
+    with pytest.raises(ValueError):
+        p.free_expert(e)                            # double free
+    q = p.alloc_small(KV, 1, 2)
+    with pytest.raises(ValueError):
+        p.free_small(KV, [q[0], 99])               # one bad page: nothing freed
+    assert p.stats()["used_small"] == [2, 0]
+    with pytest.raises(ValueError):
+        p.alloc_small(CONV, 1, 1)                  # no conv pages in this pool
+    with pytest.raises(ValueError):
+        p.alloc_ssm(1)
+    with pytest.raises(ValueError):
+        p.alloc_small(KV, -1, 1)                   # request ids are >= 0
+    with pytest.raises(AllocError):
+        p.alloc_expert(2)
+    assert p.stats()["used_small"] == [2, 0]
