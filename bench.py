@@ -33,7 +33,7 @@ HBM_PEAK_GBS = 8000.0
 # HBM bytes per k_gemm1 launch measured with rocprofv3 (FETCH_SIZE scaled by 2.0, the factor a
 # 1 GiB copy reads back, plus WRITE_SIZE), keyed by workload, T, block_m, atomic combine and a
 # hash of the GEMM sources the counters were taken on.  Reported only while that hash matches.
-MEASURED_TRAFFIC = {("qwen15", 1024, 128, False, "6be7d2f7bb126373"): 751285358}
+MEASURED_TRAFFIC = {("qwen15", 1024, 128, False, "046dc99fa6a7a0b5"): 751567663}
 GEMM_SOURCES = ("paged_expert_weight_amd/csrc/moe_gemm.hip", "paged_expert_weight_amd/csrc/internal.h")
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 MALL_BYTES = 256 << 20
@@ -87,6 +87,9 @@ def parse():
     ap.add_argument("--placement", default="synth", choices=("synth", "allocator"),
                     help="pages of the pool experts: a seeded permutation, or handed out by the page allocator "
                          "during a seeded KV / eviction churn")
+    ap.add_argument("--vmm", action="store_true",
+                    help="compare the paged forward with the contiguous kernels over remapped expert views "
+                         "(moe_vmm_*) on the same physical pages (one JSON line of its own)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB fp32 read + 1 GiB write elementwise kernel (scales HBM counters)")
     return ap.parse_args()
@@ -114,6 +117,9 @@ def main():
         return
     if args.allocator:
         allocator_bench(args)
+        return
+    if args.vmm and args.gpus == 1:
+        vmm_bench(args)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the layer's hot path runs on a single MI355X and there is no "
@@ -441,6 +447,161 @@ def allocator_bench(args):
                                    "and re-adds", "events": len(ev)},
             "results": out}
     print(json.dumps(line), flush=True)
+
+
+def vmm_bench(args):
+    """One layer on physical pages that are mapped twice: into the pool view the
+    paged kernels read through the location table, and into remapped expert
+    views the contiguous kernels read unchanged.  Times route + forward for the
+    paged path, the remapped views and the contiguous twin on ordinary
+    allocations (interleaved, second round reported), and the cost of
+    remapping."""
+    import ctypes
+
+    import numpy as np
+    import torch
+
+    import paged_expert_weight_amd as pm
+    from workloads import synth
+
+    name = args.workload
+    s = synth.SPECS[name]
+    T = args.T if args.T is not None else (32 if name == "decode" else s.T)
+    layer = synth.make_layer(s, T)
+    P, fd = s.f * s.d * 2, s.f * s.d
+    try:
+        ev = pm.ExpertViews(P, s.pool_pages, s.loadbuf_slots, s.E_tot)
+    except pm.MoeError as e:
+        print(json.dumps({"metric": "remapped expert views", "error": str(e), "workload": name}), flush=True)
+        return
+    gmin, grec = ev.granularity()
+    v = ev.views()
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipMemcpy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int]
+    hip.hipMemsetD16.argtypes = [ctypes.c_void_p, ctypes.c_uint16, ctypes.c_size_t]
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+    w13, w2, x = dev(layer.w13), dev(layer.w2), dev(layer.x)
+    logits = torch.from_numpy(layer.logits).cuda()
+    torch.cuda.synchronize()
+    assert hip.hipMemsetD16(v["pool"], 0x7FC0, s.pool_pages * fd) == 0
+    locs = layer.placement.locs.copy()
+
+    def write(e, pages):
+        for m, p in enumerate(pages):
+            src = w13[e, m * s.f:(m + 1) * s.f] if m < 2 else w2[e]
+            assert hip.hipMemcpy(v["pool"] + int(p) * P, src.data_ptr(), P, 3) == 0
+
+    for e in range(s.E_tot):
+        if locs[e]["kind"] == synth.LOC_POOL:
+            write(e, locs[e]["idx"])
+    pool = pm.moe_pool_create(v["pool"], s.pool_pages, s.d, s.f, s.E, s.k, s.S, s.loadbuf_slots,
+                              (v["loadbuf0"], v["loadbuf1"]))
+    pm.moe_set_expert_locs(pool, locs)
+    blobs = {}
+    for e in range(s.E_tot):
+        b = torch.empty(3 * fd, dtype=torch.bfloat16, pin_memory=True)
+        b.view(torch.int16).copy_(torch.from_numpy(synth.expert_blob(s, layer.w13, layer.w2, e).view(np.int16)))
+        blobs[e] = b
+
+    def fill(buf):
+        lb = [e for e in range(s.E_tot) if locs[e]["kind"] == synth.LOC_LOADBUF]
+        if lb:
+            pm.moe_loadbuf_fill(pool, buf, [int(locs[e]["idx"][0]) for e in lb], [blobs[e] for e in lb])
+        torch.cuda.synchronize()
+
+    fill(0)
+    t0 = time.perf_counter()
+    n_first = ev.map_experts(locs, 0)
+    first_ms = (time.perf_counter() - t0) * 1e3
+    bm = args.block_m or pm.moe_suggest_block_m(pool, T)
+    ws = pm.workspace(pool, T, bm)
+    rt = pm.RouteOut(pool, T, bm)
+    y = torch.empty_like(x)
+    stream = torch.cuda.current_stream()
+    wv = ev.views()
+
+    def step(mode):
+        pm.moe_route(pool, logits, bm, rt.topk_ids, rt.topk_w, rt.sorted_ids, rt.block_expert, rt.num_padded, ws,
+                     stream)
+        if mode == "paged":
+            pm.moe_paged_forward(pool, x, bm, rt.topk_ids, rt.topk_w, rt.sorted_ids, rt.block_expert,
+                                 rt.num_padded, 0, y, ws, 0, stream)
+        elif mode == "vmm":
+            ev.forward(pool, x, rt, ws, y=y, stream=stream)
+        else:
+            pm.moe_contiguous_forward(pool, w13, w2, x, bm, rt.topk_ids, rt.topk_w, rt.sorted_ids,
+                                      rt.block_expert, rt.num_padded, y, ws, 0, stream)
+
+    def timed(mode, K, W):
+        for _ in range(W):
+            step(mode)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(K):
+            step(mode)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / K * 1e3
+
+    outs = {}
+    for mode in ("paged", "vmm", "contiguous"):
+        step(mode)
+        torch.cuda.synchronize()
+        outs[mode] = y.view(torch.int16).cpu().numpy().copy()
+    identical = bool(np.array_equal(outs["paged"], outs["vmm"]) and np.array_equal(outs["vmm"], outs["contiguous"]))
+    us = {}
+    for rnd in range(2):
+        for mode in ("paged", "vmm", "contiguous"):
+            us[mode] = round(timed(mode, args.steps, args.warmup), 2)
+            print(f"# round {rnd} {mode}: {us[mode]} us/step", file=sys.stderr, flush=True)
+    # remap costs: one expert evicted into a free slot and one cached in free pages; a buffer swap
+    remap = {"first_full_map_ms": round(first_ms, 2), "first_full_map_pages": n_first}
+    pool_e = [e for e in range(s.E) if locs[e]["kind"] == synth.LOC_POOL]
+    lb_e = [e for e in range(s.E) if locs[e]["kind"] == synth.LOC_LOADBUF]
+    used = {int(p) for e in range(s.E_tot) if locs[e]["kind"] == synth.LOC_POOL for p in locs[e]["idx"]}
+    free = [p for p in range(s.pool_pages) if p not in used]
+    if pool_e and lb_e and len(free) >= 3:
+        ev_e, add_e = pool_e[0], lb_e[0]
+        slot = int(locs[add_e]["idx"][0])
+        locs[add_e]["kind"] = synth.LOC_POOL
+        locs[add_e]["idx"] = free[:3]
+        write(add_e, free[:3])
+        locs[ev_e]["kind"] = synth.LOC_LOADBUF
+        locs[ev_e]["idx"] = (slot, 0, 0)
+        fill(0)
+        t0 = time.perf_counter()
+        n = ev.map_experts(locs, 0)
+        remap["evict_and_add_ms"] = round((time.perf_counter() - t0) * 1e3, 3)
+        remap["evict_and_add_pages"] = n
+    if s.loadbuf_slots:
+        fill(1)
+        t0 = time.perf_counter()
+        n = ev.map_experts(locs, 1)
+        remap["buffer_swap_ms"] = round((time.perf_counter() - t0) * 1e3, 3)
+        remap["buffer_swap_pages"] = n
+    # two experts trade pages (timing only: no forward runs on this table)
+    pe = [e for e in range(s.E_tot) if locs[e]["kind"] == synth.LOC_POOL]
+    if len(pe) >= 2:
+        a, b = pe[0], pe[1]
+        ia, ib = locs[a]["idx"].copy(), locs[b]["idx"].copy()
+        locs[a]["idx"], locs[b]["idx"] = ib, ia
+        t0 = time.perf_counter()
+        n = ev.map_experts(locs, 1 if s.loadbuf_slots else 0)
+        remap["swap_two_experts_ms"] = round((time.perf_counter() - t0) * 1e3, 3)
+        remap["swap_two_experts_pages"] = n
+    line = {"metric": "remapped expert views (PagedTensor) vs in-kernel page lookup, us per step",
+            "value": us["vmm"], "unit": "us/step", "higher_is_better": False, "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": WORKLOAD_TEXT[name], "name": name, "T": T, "block_m": bm,
+                       "page_bytes": P, "granularity": {"minimum": gmin, "recommended": grec}},
+            "us_per_step": us,
+            "vs_contiguous_pct": {m: round((us[m] / us["contiguous"] - 1) * 100, 2) for m in ("paged", "vmm")},
+            "outputs_bit_identical": identical,
+            "remap": remap}
+    print(json.dumps(line), flush=True)
+    pool.close()
+    ev.close()
 
 
 def pipeline_bench(args):

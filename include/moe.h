@@ -462,6 +462,61 @@ int moe_free_request(moe_alloc *a, int64_t request, int64_t *n_freed);
 
 int moe_alloc_get_stats(const moe_alloc *a, moe_alloc_stats *stats);
 
+/* ---------------------------------------------------------------- remapped expert views
+ * The PagedTensor alternative of the wiki page "FluxMoE: Decoupling Expert
+ * Residency for High-Performance MoE Serving" (core method): instead of a page
+ * lookup inside the kernel, every expert matrix gets a fixed virtual address
+ * and the GPU's page tables point it at whichever physical page holds the
+ * matrix, so the contiguous kernels run unchanged.
+ *
+ * moe_vmm_create makes num_pages + 6*loadbuf_slots physical allocations of
+ * page_bytes (= f*d*2; must be a multiple of the device's mapping
+ * granularity, else MOE_ERR_UNSUPPORTED, as is a device without virtual memory
+ * management) and maps each into a contiguous view: the pool (page p at
+ * p*page_bytes) and two load buffers (slot s holds W1, W3, W2 at
+ * (3s + m)*page_bytes).  Those views are ordinary device memory for every entry
+ * point above: use them as moe_pool_desc.pool_base and loadbuf_base[b].  It
+ * also reserves the expert views w13 [E+S][2f][d] and w2 [E+S][d][f], which
+ * stay unmapped until moe_vmm_map_experts.
+ */
+typedef struct moe_vmm moe_vmm;
+
+int moe_vmm_create(int64_t page_bytes, int64_t num_pages, int32_t loadbuf_slots, int32_t n_experts_total,
+                   moe_vmm **out);
+
+/* Waits for the whole device, unmaps and frees everything.  NULL is a no-op. */
+int moe_vmm_destroy(moe_vmm *vmm);
+
+/* Device addresses of the views (any output may be NULL).  w13 and w2 are NULL
+ * until a moe_vmm_map_experts call has succeeded. */
+int moe_vmm_views(const moe_vmm *vmm, void **pool_base, void **loadbuf0, void **loadbuf1, void **w13,
+                  void **w2);
+
+/* The device's minimum mapping granularity (page_bytes is a multiple of it)
+ * and the recommended one (the alignment of every view). */
+int moe_vmm_granularity(const moe_vmm *vmm, int64_t *minimum, int64_t *recommended);
+
+/*
+ * Point the expert views at the pages a location table names (host, all
+ * n = E + S experts; load-buffer experts at the slots of buffer active_buf).
+ * Validation as moe_validate_locs, before anything changes.  The call first
+ * synchronises `stream`: every forward that reads the views must run on it
+ * (or have finished), because a view page is re-pointed in place.  Only view
+ * pages whose physical page changes are remapped; *n_remapped (may be NULL)
+ * receives their number.  MOE_ERR_HIP from a mapping call leaves the views
+ * unusable (MOE_ERR_STATE afterwards): destroy the object.
+ */
+int moe_vmm_map_experts(moe_vmm *vmm, const moe_expert_loc *locs, int32_t n, int32_t active_buf, void *stream,
+                        int32_t *n_remapped);
+
+/* The contiguous forward over the expert views (arguments as
+ * moe_contiguous_forward).  MOE_ERR_STATE until the views are fully mapped;
+ * MOE_ERR_INVALID_ARG if the layer handle's E + S or f*d*2 differ. */
+int moe_vmm_forward(const moe_vmm *vmm, const moe_pool *pool, const void *x, int64_t T, int32_t block_m,
+                    const int32_t *topk_ids, const float *topk_w, const int32_t *sorted_ids,
+                    const int32_t *block_expert, const int32_t *num_padded, void *y, void *ws,
+                    size_t ws_bytes, uint32_t flags, void *stream);
+
 /* Message for the last non-zero return on this thread ("" if none). */
 const char *moe_last_error(void);
 

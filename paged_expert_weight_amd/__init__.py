@@ -48,6 +48,8 @@ EXPORTS = (
     "moe_alloc_create", "moe_alloc_destroy", "moe_alloc_expert_pages", "moe_free_expert_pages",
     "moe_alloc_ssm_pages", "moe_free_ssm_pages", "moe_alloc_small_pages", "moe_free_small_pages",
     "moe_free_request", "moe_alloc_get_stats",
+    "moe_vmm_create", "moe_vmm_destroy", "moe_vmm_views", "moe_vmm_granularity", "moe_vmm_map_experts",
+    "moe_vmm_forward",
 )
 
 
@@ -131,6 +133,13 @@ def lib():
     L.moe_free_small_pages.argtypes = [P, i32, i32, P]
     L.moe_free_request.argtypes = [P, i64, ctypes.POINTER(i64)]
     L.moe_alloc_get_stats.argtypes = [P, ctypes.POINTER(moe_alloc_stats)]
+    L.moe_vmm_create.argtypes = [i64, i64, i32, i32, ctypes.POINTER(P)]
+    L.moe_vmm_destroy.argtypes = [P]
+    L.moe_vmm_views.argtypes = [P, ctypes.POINTER(P), ctypes.POINTER(P), ctypes.POINTER(P), ctypes.POINTER(P),
+                                ctypes.POINTER(P)]
+    L.moe_vmm_map_experts.argtypes = [P, P, i32, i32, P, ctypes.POINTER(i32)]
+    L.moe_vmm_granularity.argtypes = [P, ctypes.POINTER(i64), ctypes.POINTER(i64)]
+    L.moe_vmm_forward.argtypes = [P, P, P, i64, i32, P, P, P, P, P, P, P, sz, u32, P]
     L.moe_suggest_block_m.argtypes = [P, i64]
     L.moe_suggest_block_m.restype = i32
     L.moe_last_error.restype = ctypes.c_char_p
@@ -512,3 +521,55 @@ class PageAllocator:
                 "used_small": list(s.used_small), "free_small": list(s.free_small),
                 "expert_available": s.expert_available, "trapped_bytes": s.trapped_bytes,
                 "huge_bytes": s.huge_bytes, "n_huge": s.n_huge}
+
+
+# ----------------------------------------------------------------------------- remapped expert views
+
+class ExpertViews:
+    """Owner of one moe_vmm: physical pages, the pool / load-buffer views over
+    them, and the remappable expert views w13 / w2."""
+
+    def __init__(self, page_bytes: int, num_pages: int, loadbuf_slots: int, n_experts_total: int):
+        h = ctypes.c_void_p()
+        _check(lib().moe_vmm_create(page_bytes, num_pages, loadbuf_slots, n_experts_total, ctypes.byref(h)))
+        self.handle = h
+        self.page_bytes, self.num_pages, self.slots, self.E_tot = page_bytes, num_pages, loadbuf_slots, n_experts_total
+
+    def close(self):
+        if self.handle:
+            _check(lib().moe_vmm_destroy(self.handle))
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def views(self):
+        """{"pool", "loadbuf0", "loadbuf1", "w13", "w2"}: device addresses (None where unset)."""
+        ps = [ctypes.c_void_p() for _ in range(5)]
+        _check(lib().moe_vmm_views(self.handle, *[ctypes.byref(p) for p in ps]))
+        return dict(zip(("pool", "loadbuf0", "loadbuf1", "w13", "w2"), [p.value for p in ps]))
+
+    def granularity(self):
+        """(minimum, recommended) mapping granularity in bytes."""
+        a, b = ctypes.c_int64(), ctypes.c_int64()
+        _check(lib().moe_vmm_granularity(self.handle, ctypes.byref(a), ctypes.byref(b)))
+        return a.value, b.value
+
+    def map_experts(self, locs: np.ndarray, active_buf: int = 0, stream=None) -> int:
+        a = locs_array(locs)
+        n = ctypes.c_int32()
+        _check(lib().moe_vmm_map_experts(self.handle, a.ctypes.data, a.shape[0], active_buf, _stream(stream),
+                                         ctypes.byref(n)))
+        return n.value
+
+    def forward(self, p: MoePool, x, r: "RouteOut", ws, flags: int = 0, y=None, stream=None):
+        import torch
+        if y is None:
+            y = torch.empty_like(x)
+        _check(lib().moe_vmm_forward(self.handle, p.handle, _ptr(x), x.shape[0], r.block_m, _ptr(r.topk_ids),
+                                     _ptr(r.topk_w), _ptr(r.sorted_ids), _ptr(r.block_expert), _ptr(r.num_padded),
+                                     _ptr(y), _ptr(ws), ws.numel() * ws.element_size(), flags, _stream(stream)))
+        return y

@@ -244,6 +244,14 @@ hipEvent_t *next_timing_events(moe_pool *p)
 
 namespace pmoe {
 int set_error(int code, const char *msg) { return fail(code, msg); }
+bool pool_shape(const moe_pool *p, int32_t *E_tot, int64_t *page_bytes)
+{
+    if (!p)
+        return false;
+    *E_tot = p->E_tot;
+    *page_bytes = (int64_t)p->desc.f * p->desc.d * 2;
+    return true;
+}
 } // namespace pmoe
 
 extern "C" {
