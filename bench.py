@@ -255,7 +255,9 @@ def main():
                 "unit": "TFLOP/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
     roof["traffic"] = measured_traffic(name, T, bm, args.atomic)
-    roof["kernel"] = "k_gemm1 (paged gate/up GEMM + SiLU*mul)"
+    decode_form = pm.moe_forward_form(h0, T) == pm.MOE_FORM_DECODE
+    roof["kernel"] = ("k_dec_gate_up (paged gate/up, decode form: weight rows dotted with the picks' x rows + SiLU*mul)"
+                      if decode_form else "k_gemm1 (paged gate/up GEMM + SiLU*mul)")
     roof["avg_launch_us"] = round(stage_us[0], 2)
     roof["algorithmic_bytes_per_launch"] = int(g1_bytes)
     roof["algorithmic_flops_per_launch"] = int(g1_flops)
@@ -317,7 +319,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": WORKLOAD_TEXT[name], "name": name, "T": T, "block_m": bm,
-                   "placement": args.placement,
+                   "placement": args.placement, "gemm_form": "decode" if decode_form else "tiles",
                    "combine": "atomic" if args.atomic else "ordered", "layer_copies_rotated": R},
         "hbm_gbs": round(gbs, 1),
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),

@@ -256,6 +256,22 @@ int moe_resolve_addrs(moe_pool *pool, int32_t active_buf, int64_t n, const int32
 int32_t moe_suggest_block_m(const moe_pool *pool, int64_t T);
 
 /*
+ * Which form of the two GEMMs a forward of T tokens takes (the same for every
+ * block_m and for paged and contiguous weights):
+ *   MOE_FORM_TILES   MFMA tiles over the aligned blocks, then the combine;
+ *   MOE_FORM_DECODE  for 1..8 tokens with d <= 4096 and f <= 2048 (and at most
+ *                    64 picks per token): each weight row is read once
+ *                    and dotted on the vector ALUs with the x rows of the picks
+ *                    of its expert block; the down projection adds the token's
+ *                    picks in slot order and writes y directly (no combine
+ *                    pass; MOE_FLAG_ATOMIC_COMBINE has no effect).
+ * MOE_ERR_INVALID_ARG for a NULL pool or T < 0.
+ */
+#define MOE_FORM_TILES 0
+#define MOE_FORM_DECODE 1
+int32_t moe_forward_form(const moe_pool *pool, int64_t T);
+
+/*
  * Stage timing of paged forwards, for measurement.  With enable != 0 every
  * moe_paged_forward of this handle records four hipEvents on its stream:
  * before the gate/up GEMM, after it, after the down GEMM and after the

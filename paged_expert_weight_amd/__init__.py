@@ -32,6 +32,8 @@ MOE_ERR_NO_SPACE = -10
 MOE_LOC_POOL = 0
 MOE_LOC_LOADBUF = 1
 MOE_FLAG_ATOMIC_COMBINE = 1
+MOE_FORM_TILES = 0
+MOE_FORM_DECODE = 1
 MOE_PAGE_KV = 0
 MOE_PAGE_CONV = 1
 MOE_ALLOC_NO_PACKING = 1
@@ -39,7 +41,7 @@ MOE_ALLOC_NO_PACKING = 1
 # every function moe.h declares
 EXPORTS = (
     "moe_pool_create", "moe_pool_destroy", "moe_validate_locs", "moe_set_expert_locs",
-    "moe_route_capacity", "moe_workspace_bytes", "moe_route", "moe_paged_forward",
+    "moe_route_capacity", "moe_workspace_bytes", "moe_route", "moe_paged_forward", "moe_forward_form",
     "moe_contiguous_forward", "moe_loadbuf_fill", "moe_resolve_addrs", "moe_suggest_block_m",
     "moe_stage_timing", "moe_stage_times", "moe_last_error", "moe_version",
     "moe_adjust_amounts", "moe_rank_experts", "moe_adjust_select",
@@ -142,9 +144,11 @@ def lib():
     L.moe_vmm_forward.argtypes = [P, P, P, i64, i32, P, P, P, P, P, P, P, sz, u32, P]
     L.moe_suggest_block_m.argtypes = [P, i64]
     L.moe_suggest_block_m.restype = i32
+    L.moe_forward_form.argtypes = [P, i64]
+    L.moe_forward_form.restype = i32
     L.moe_last_error.restype = ctypes.c_char_p
     for name in EXPORTS:
-        if name not in ("moe_last_error", "moe_suggest_block_m"):
+        if name not in ("moe_last_error", "moe_suggest_block_m", "moe_forward_form"):
             getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -362,6 +366,14 @@ def moe_stage_times(p: MoePool):
     n = ctypes.c_int32()
     _check(lib().moe_stage_times(p.handle, ctypes.addressof(ms), ctypes.addressof(n)))
     return [float(v) for v in ms], n.value
+
+
+def moe_forward_form(p: MoePool, T: int) -> int:
+    """MOE_FORM_TILES or MOE_FORM_DECODE: the GEMM form a forward of T tokens takes."""
+    v = int(lib().moe_forward_form(p.handle, T))
+    if v < 0:
+        _check(v)
+    return v
 
 
 def moe_version() -> int:

@@ -36,6 +36,19 @@ struct moe_pool {
 
 constexpr size_t kMaxTimedForwards = 1024;
 
+// Events that only mark "the readers of a buffer have finished" (before it is
+// overwritten or handed out again) need no system-scope fence: nothing they
+// order has to become visible to anyone, and the fence would write back and
+// invalidate the caches after every forward.
+constexpr unsigned kReadDoneEvent = hipEventDisableTiming | hipEventDisableSystemFence;
+
+namespace pmoe {
+// Decode form of the two GEMMs for a few tokens (vector-ALU dot products,
+// down projection and combine in one pass); used when decode_fits holds.
+bool decode_fits(const FwdArgs &a);
+hipError_t launch_decode(const FwdArgs &a, hipStream_t s);
+} // namespace pmoe
+
 namespace {
 
 thread_local std::string g_err;
@@ -221,7 +234,10 @@ int forward_common(const moe_pool *p, const void *w13, const void *w2, bool page
     if (ev)
         for (int i = 0; i < 4; i++)
             a.ev[i] = ev[i];
-    HIP_TRY(pmoe::launch_forward(a, s));
+    if (pmoe::decode_fits(a))
+        HIP_TRY(pmoe::launch_decode(a, s));
+    else
+        HIP_TRY(pmoe::launch_forward(a, s));
     return MOE_OK;
 }
 
@@ -258,7 +274,7 @@ extern "C" {
 
 const char *moe_last_error(void) { return g_err.c_str(); }
 
-int moe_version(void) { return 101; }
+int moe_version(void) { return 102; }
 
 int moe_validate_locs(const moe_pool_desc *desc, const moe_expert_loc *locs, int32_t n)
 {
@@ -326,7 +342,8 @@ int moe_pool_create(const moe_pool_desc *desc, moe_pool **out)
     for (int b = 0; b < 2; b++) {
         if ((e = hipEventCreateWithFlags(&p->filled[b], hipEventDisableTiming)) != hipSuccess)
             return cleanup(hip_fail(e, "hipEventCreate"));
-        if ((e = hipEventCreateWithFlags(&p->consumed[b], hipEventDisableTiming)) != hipSuccess)
+        // marks the end of reads only: no cache writeback is needed before a later overwrite
+        if ((e = hipEventCreateWithFlags(&p->consumed[b], kReadDoneEvent)) != hipSuccess)
             return cleanup(hip_fail(e, "hipEventCreate"));
     }
     *out = p;
@@ -606,6 +623,18 @@ int moe_stage_times(moe_pool *p, float *ms, int32_t *count)
     return MOE_OK;
 }
 
+int32_t moe_forward_form(const moe_pool *p, int64_t T)
+{
+    if (!p || T < 0)
+        return fail(MOE_ERR_INVALID_ARG, "bad arguments");
+    pmoe::FwdArgs a{};
+    a.T = T;
+    a.d = p->desc.d;
+    a.f = p->desc.f;
+    a.keff = p->keff;
+    return pmoe::decode_fits(a) ? MOE_FORM_DECODE : MOE_FORM_TILES;
+}
+
 int32_t moe_suggest_block_m(const moe_pool *p, int64_t T)
 {
     if (!p || T <= 0)
@@ -755,14 +784,14 @@ int moe_pipeline_create(int32_t L, moe_pool *const *layers, void *copy_stream, m
     for (int b = 0; b < 2 && e == hipSuccess; b++) {
         e = hipEventCreateWithFlags(&p->filled[b], hipEventDisableTiming);
         if (e == hipSuccess)
-            e = hipEventCreateWithFlags(&p->consumed[b], hipEventDisableTiming);
+            e = hipEventCreateWithFlags(&p->consumed[b], kReadDoneEvent);
     }
     for (int l = 0; l < L && e == hipSuccess; l++) {
         moe_pipeline::Staged &st = p->staged[l];
         const size_t n = (size_t)layers[l]->E_tot;
         e = hipEventCreateWithFlags(&st.copied, hipEventDisableTiming);
         if (e == hipSuccess)
-            e = hipEventCreateWithFlags(&st.switched, hipEventDisableTiming);
+            e = hipEventCreateWithFlags(&st.switched, kReadDoneEvent);
         if (e == hipSuccess)
             e = hipMalloc((void **)&st.alt, sizeof(DevLoc) * n);
         if (e == hipSuccess)
@@ -970,7 +999,7 @@ int moe_pipeline_forward(moe_pipeline *p, int32_t layer, const void *x, int64_t 
             // every earlier forward that may read the dropped pages is on s already
             moe_pipeline::Batch bt;
             bt.pages.swap(st.dropped);
-            HIP_TRY(hipEventCreateWithFlags(&bt.done, hipEventDisableTiming));
+            HIP_TRY(hipEventCreateWithFlags(&bt.done, kReadDoneEvent));
             const hipError_t e = hipEventRecord(bt.done, s);
             if (e != hipSuccess) {
                 (void)hipEventDestroy(bt.done);

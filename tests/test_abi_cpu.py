@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol(lib):
     for name in sorted(declared):
         assert hasattr(lib, name), f"{name} declared in include/ but not exported"
     assert declared == set(pm.EXPORTS)
-    assert lib.moe_version() == 101
+    assert lib.moe_version() == 102
 
 
 def _desc(**kw):
