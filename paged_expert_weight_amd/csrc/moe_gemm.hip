@@ -734,6 +734,13 @@ using Tiles16 = Tiles<16, Gemm<16, 16, 1, 1, 4, 64, 3, true>, Gemm<16, 32, 1, 1,
 using Tiles32 = Tiles<32, Gemm<32, 32, 1, 2, 1, 64, 2, true>, Gemm<32, 32, 1, 2, 1, 64, 2, false>>;
 using Tiles64 = Tiles<64, Gemm<64, 64, 2, 2, 1, 64, 2, true>, Gemm<64, 64, 2, 2, 1, 64, 2, false>>;
 using Tiles128 = Tiles<128, Gemm<128, 64, 2, 2, 1, 64, 2, true>, Gemm<128, 128, 2, 2, 1, 64, 2, false>>;
+// 128-row blocks of layers with many small experts (a block's x or h rows are
+// re-read once per column tile): 256-column tiles, 8 waves of 64x64
+// accumulators (gate/up: 64 x (64 gate + 64 up)); the gate/up stages fill all
+// 160 KB of LDS, the down GEMM's short K loop (K = f) keeps three stages.
+using Down128w = Gemm<128, 256, 2, 4, 1, 64, 3, false>;
+using Tiles128w = Tiles<128, Gemm<128, 256, 2, 4, 1, 64, 2, true>, Down128w>;
+using Tiles128d = Tiles<128, Gemm<128, 64, 2, 2, 1, 64, 2, true>, Down128w>;
 // large blocks (MFMA-bound shapes): 8 waves, two per SIMD, each with a 64x128
 // accumulator tile (gate/up: 64 x (64 gate + 64 up)); 256x256 down tiles.  K
 // steps of 64: every staged row is a 128-byte segment, which L2 feeds into LDS
@@ -847,7 +854,10 @@ hipError_t launch_paged(const FwdArgs &a, hipStream_t s)
     case 16: return launch_tiles<Tiles16, PAGED>(a, s);
     case 32: return launch_tiles<Tiles32, PAGED>(a, s);
     case 64: return launch_tiles<Tiles64, PAGED>(a, s);
-    case 128: return launch_tiles<Tiles128, PAGED>(a, s);
+    case 128:
+        if (a.d % 256 == 0)
+            return a.f % 256 == 0 ? launch_tiles<Tiles128w, PAGED>(a, s) : launch_tiles<Tiles128d, PAGED>(a, s);
+        return launch_tiles<Tiles128, PAGED>(a, s);
     case 256:
         if (a.f % Tiles256::K1::BN_ == 0 && a.d % Tiles256::K2::BN_ == 0)
             return launch_tiles<Tiles256, PAGED>(a, s);
