@@ -33,8 +33,13 @@ HBM_PEAK_GBS = 8000.0
 # HBM bytes per k_gemm1 launch measured with rocprofv3 (FETCH_SIZE scaled by 2.0, the factor a
 # 1 GiB copy reads back, plus WRITE_SIZE), keyed by workload, T, block_m, atomic combine and a
 # hash of the GEMM sources the counters were taken on.  Reported only while that hash matches.
-MEASURED_TRAFFIC = {("qwen15", 1024, 128, False, "046dc99fa6a7a0b5"): 751567663}
-GEMM_SOURCES = ("paged_expert_weight_amd/csrc/moe_gemm.hip", "paged_expert_weight_amd/csrc/internal.h")
+MEASURED_TRAFFIC = {
+    ("qwen15", 1024, 128, False, "b6c2d9577edcbefc"): 751406118,
+    ("qwen3n", 8192, 128, False, "b6c2d9577edcbefc"): 2841410419,
+    ("decode", 1, 16, False, "b6c2d9577edcbefc"): 46249759,
+}
+GEMM_SOURCES = ("paged_expert_weight_amd/csrc/moe_gemm.hip", "paged_expert_weight_amd/csrc/decode.hip",
+                "paged_expert_weight_amd/csrc/internal.h")
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 MALL_BYTES = 256 << 20
 
