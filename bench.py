@@ -189,8 +189,10 @@ def main():
             pm.moe_contiguous_forward(c["h"], c["w13"], c["w2"], dev.x, bm, rt.topk_ids, rt.topk_w, rt.sorted_ids,
                                       rt.block_expert, rt.num_padded, y, ws, flags, stream)
         else:
+            # the load buffer is refilled only by the concurrent-fill measurement (buffer 1): the
+            # "buffer read" mark of buffer 0 is deferred to its next fill instead of a stream marker per step
             pm.moe_paged_forward(c["h"], dev.x, bm, rt.topk_ids, rt.topk_w, rt.sorted_ids, rt.block_expert,
-                                 rt.num_padded, 0, y, ws, flags, stream)
+                                 rt.num_padded, 0, y, ws, flags | pm.MOE_FLAG_DEFER_READ_DONE, stream)
 
     def timed(K, W, contiguous=False):
         for i in range(W):
@@ -234,7 +236,7 @@ def main():
                      rt.num_padded, ws, stream)
         ra1.record(stream)
         pm.moe_paged_forward(c["h"], dev.x, bm, rt.topk_ids, rt.topk_w, rt.sorted_ids, rt.block_expert,
-                             rt.num_padded, 0, y, ws, flags, stream)
+                             rt.num_padded, 0, y, ws, flags | pm.MOE_FLAG_DEFER_READ_DONE, stream)
         ra1.synchronize()
         route_ms += ra0.elapsed_time(ra1)
     torch.cuda.synchronize()

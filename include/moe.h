@@ -69,6 +69,13 @@ extern "C" {
 #define MOE_FLAG_ATOMIC_COMBINE 1u /* combine the k partial outputs with fp32 atomics
                                       (faster, summation order not reproducible);
                                       default: fixed slot order, bit-reproducible */
+#define MOE_FLAG_DEFER_READ_DONE 2u /* moe_paged_forward: record no "buffer read"
+                                       event on the stream (a stream marker costs
+                                       the GPU ~2 us between forwards); the stream
+                                       is remembered instead, and the next fill of
+                                       that buffer (or moe_pool_destroy) marks it
+                                       there.  The stream must stay alive until
+                                       then.  Default: an event after each forward */
 
 typedef struct moe_pool moe_pool; /* opaque handle: one MoE layer's view of the pool */
 
@@ -119,7 +126,8 @@ typedef struct {
  */
 int moe_pool_create(const moe_pool_desc *desc, moe_pool **out);
 
-/* Release the handle's state.  Waits for the handle's own pending work. NULL is a no-op. */
+/* Release the handle's state.  Waits for the handle's own pending work, and for
+ * the work of streams that ran forwards with MOE_FLAG_DEFER_READ_DONE. NULL is a no-op. */
 int moe_pool_destroy(moe_pool *pool);
 
 /*
@@ -182,7 +190,9 @@ int moe_route(moe_pool *pool, const float *logits, int64_t T, int32_t block_m,
  *   active_buf   0 or 1: the load buffer the MOE_LOC_LOADBUF experts are read
  *                from.  The forward waits (on `stream`, via an event) for the
  *                last moe_loadbuf_fill of that buffer, and marks the buffer
- *                consumed when its last read is done; it fails with
+ *                consumed when its last read is done (with
+ *                MOE_FLAG_DEFER_READ_DONE: when the next fill of the buffer is
+ *                enqueued, by an event on `stream` then); it fails with
  *                MOE_ERR_STATE if the table names load-buffer experts and that
  *                buffer was never filled.
  *   y            device bf16 [T][d] out.
@@ -191,7 +201,7 @@ int moe_route(moe_pool *pool, const float *logits, int64_t T, int32_t block_m,
  *                combine buffer (bf16 weighted partial rows [T*(k+S)][d], or an
  *                fp32 [T][d] accumulator with MOE_FLAG_ATOMIC_COMBINE).  Not kept
  *                between calls.
- *   flags        0 or MOE_FLAG_ATOMIC_COMBINE.
+ *   flags        0, MOE_FLAG_ATOMIC_COMBINE, MOE_FLAG_DEFER_READ_DONE, or both.
  * Gate/up GEMM: each output tile resolves its W1 and W3 page bases once and
  * fuses silu(gate) * up into its epilogue; down GEMM: each tile resolves its
  * W2 page once and scales by the routing weight; each weighted partial row is
@@ -227,6 +237,9 @@ int moe_contiguous_forward(const moe_pool *pool, const void *w13, const void *w2
  * The copies wait for the last forward that read `buf` (write-after-read) and
  * for earlier fills of `buf`; the buffer's "filled" event is recorded after
  * them, and the next forward reading `buf` waits for it (read-after-write).
+ * Forwards of `buf` run with MOE_FLAG_DEFER_READ_DONE are waited for by an
+ * event recorded now on each stream they ran on, which covers everything
+ * enqueued on that stream so far (never less than those forwards).
  */
 int moe_loadbuf_fill(moe_pool *pool, int32_t buf, int32_t n, const int32_t *slots,
                      const void *const *host_src, void *copy_stream);

@@ -32,6 +32,7 @@ MOE_ERR_NO_SPACE = -10
 MOE_LOC_POOL = 0
 MOE_LOC_LOADBUF = 1
 MOE_FLAG_ATOMIC_COMBINE = 1
+MOE_FLAG_DEFER_READ_DONE = 2
 MOE_FORM_TILES = 0
 MOE_FORM_DECODE = 1
 MOE_PAGE_KV = 0

@@ -28,6 +28,9 @@ struct moe_pool {
     hipEvent_t consumed[2] = {nullptr, nullptr}; // last forward reading buffer b done (write-after-read)
     bool ever_filled[2] = {false, false};
     bool consumed_rec[2] = {false, false};
+    // streams of forwards that read buffer b with MOE_FLAG_DEFER_READ_DONE and
+    // have not been marked yet (by the next fill of b or by destroy)
+    std::vector<hipStream_t> deferred_readers[2];
     // stage timing (measurement only): one set of 4 events per recorded forward
     bool timing = false;
     std::vector<std::array<hipEvent_t, 4>> tev;
@@ -365,6 +368,9 @@ int moe_pool_destroy(moe_pool *p)
         if (p->consumed[b]) {
             if (p->consumed_rec[b])
                 (void)hipEventSynchronize(p->consumed[b]);
+            for (hipStream_t r : p->deferred_readers[b]) // forwards whose reads were not marked yet
+                if (hipEventRecord(p->consumed[b], r) == hipSuccess)
+                    (void)hipEventSynchronize(p->consumed[b]);
             (void)hipEventDestroy(p->consumed[b]);
         }
     }
@@ -416,7 +422,7 @@ int moe_workspace_bytes(const moe_pool *p, int64_t T, int32_t block_m, uint32_t 
 {
     if (!p || !bytes)
         return fail(MOE_ERR_INVALID_ARG, "null argument");
-    if (flags & ~MOE_FLAG_ATOMIC_COMBINE)
+    if (flags & ~(MOE_FLAG_ATOMIC_COMBINE | MOE_FLAG_DEFER_READ_DONE))
         return fail(MOE_ERR_INVALID_ARG, "unknown flag bits");
     CHECK(check_tokens(p, T, block_m));
     *bytes = sizes_for(p, T, block_m, flags).total;
@@ -476,6 +482,8 @@ int moe_paged_forward(moe_pool *p, const void *x, int64_t T, int32_t block_m, co
         return fail(MOE_ERR_INVALID_ARG, "active_buf must be 0 or 1");
     if (!p->locs_set)
         return fail(MOE_ERR_STATE, "no location table: call moe_set_expert_locs first");
+    if (flags & ~(MOE_FLAG_ATOMIC_COMBINE | MOE_FLAG_DEFER_READ_DONE))
+        return fail(MOE_ERR_INVALID_ARG, "unknown flag bits");
     if (p->uses_loadbuf && !p->ever_filled[active_buf])
         return fail(MOE_ERR_STATE, "load buffer " + std::to_string(active_buf) +
                                        " was never filled but the table reads from it");
@@ -492,10 +500,17 @@ int moe_paged_forward(moe_pool *p, const void *x, int64_t T, int32_t block_m, co
         }
     }
     CHECK(forward_common(p, nullptr, nullptr, true, x, T, block_m, topk_ids, topk_w, sorted_ids, block_expert,
-                         num_padded, active_buf, y, ws, ws_bytes, flags, s, T > 0 ? next_timing_events(p) : nullptr));
+                         num_padded, active_buf, y, ws, ws_bytes, flags & MOE_FLAG_ATOMIC_COMBINE, s,
+                         T > 0 ? next_timing_events(p) : nullptr));
     if (T > 0 && p->uses_loadbuf) {
-        HIP_TRY(hipEventRecord(p->consumed[active_buf], s));
-        p->consumed_rec[active_buf] = true;
+        if (flags & MOE_FLAG_DEFER_READ_DONE) {
+            auto &rd = p->deferred_readers[active_buf];
+            if (std::find(rd.begin(), rd.end(), s) == rd.end())
+                rd.push_back(s);
+        } else {
+            HIP_TRY(hipEventRecord(p->consumed[active_buf], s));
+            p->consumed_rec[active_buf] = true;
+        }
     }
     return MOE_OK;
 }
@@ -545,6 +560,16 @@ int moe_loadbuf_fill(moe_pool *p, int32_t buf, int32_t n, const int32_t *slots, 
     hipStream_t s = (hipStream_t)copy_stream;
     if (p->consumed_rec[buf])
         HIP_TRY(hipStreamWaitEvent(s, p->consumed[buf], 0));
+    // deferred readers: mark each stream now (the wait takes the event as
+    // recorded at the time of the call, so one event serves them in turn)
+    for (hipStream_t r : p->deferred_readers[buf]) {
+        if (r == s)
+            continue; // same stream: already ordered
+        HIP_TRY(hipEventRecord(p->consumed[buf], r));
+        p->consumed_rec[buf] = true;
+        HIP_TRY(hipStreamWaitEvent(s, p->consumed[buf], 0));
+    }
+    p->deferred_readers[buf].clear();
     if (p->ever_filled[buf])
         HIP_TRY(hipStreamWaitEvent(s, p->filled[buf], 0));
     const size_t bytes = (size_t)3 * p->desc.f * p->desc.d * 2;

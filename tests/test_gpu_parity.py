@@ -361,6 +361,44 @@ def test_double_buffer_alternation():
     pool.close()
 
 
+@pytest.mark.parametrize("flags", [0, pm.MOE_FLAG_DEFER_READ_DONE])
+def test_fill_waits_for_a_queued_forward_of_its_buffer(flags):
+    """A forward reading load buffer 0 is held back on its stream behind a
+    sleep kernel; a fill of buffer 0 with NaN pages is enqueued after it on a
+    copy stream.  The fill must wait for that forward (write after read), so
+    y matches the oracle; a forward after the fill reads the NaN pages.  With
+    the deferred flag the forward records nothing on its stream, and the fill
+    marks the stream instead; destroy waits for a deferred forward too."""
+    c = Case(host_layer("tiny"))
+    s = c.s
+    comp, copy = torch.cuda.Stream(), torch.cuda.Stream()
+    ws = pm.workspace(c.pool, s.T, 16)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(comp):
+        torch.cuda._sleep(50_000_000)
+        r = pm.route(c.pool, c.dev.logits, 16, ws, stream=comp)
+        y = torch.empty_like(c.dev.x)
+        pm.moe_paged_forward(c.pool, c.dev.x, 16, r.topk_ids, r.topk_w, r.sorted_ids, r.block_expert, r.num_padded,
+                             0, y, ws, flags, comp)
+    held = not comp.query()
+    slots = sorted(c.dev.host_blobs)
+    nan = torch.full((3 * s.f * s.d,), float("nan"), dtype=torch.bfloat16).pin_memory()
+    pm.moe_loadbuf_fill(c.pool, 0, slots, [nan] * len(slots), copy)
+    torch.cuda.synchronize()
+    assert held, "the forward had finished before the fill was enqueued; the test shows nothing"
+    ids, w = _oracle_routing(c)
+    ref = oracle.moe(c.layer.x, c.layer.w13, c.layer.w2, ids, w)
+    got = y_f64(y)
+    assert np.all(np.isfinite(got)) and max_rel_err(got, ref) <= TOL
+    picks_loadbuf = np.isin(ids, synth.loadbuf_experts(s)).any()
+    with torch.cuda.stream(comp):
+        y2 = torch.empty_like(c.dev.x)
+        pm.moe_paged_forward(c.pool, c.dev.x, 16, r.topk_ids, r.topk_w, r.sorted_ids, r.block_expert,
+                             r.num_padded, 0, y2, ws, flags, comp)
+    c.pool.close()  # waits for the forward above, also when it was deferred
+    assert picks_loadbuf and np.isnan(y_f64(y2)).any()
+
+
 def test_state_errors():
     c = case("tiny")
     s = c.s
