@@ -1,9 +1,11 @@
 // Top-k softmax routing and token alignment (gfx950, wave64).
 //
-// Routing: one wave per token.  Lane L holds logits L, L+64, ...; each of the k
-// rounds takes a lane-local best, then a butterfly max over the wave (DPP and
-// lane-swap steps, no LDS) with a strict total order (larger logit first, equal
-// logits to the lower id), so all lanes agree on the winner.  Lane j keeps pick j; the weights are the softmax
+// Routing: one wave per token.  Lane L holds logits L, L+64, ..., sorted once
+// into pick order (larger logit first, equal logits by lower id); each of the k
+// rounds takes a butterfly max of the lanes' first entries and a butterfly min
+// of the ids of the lanes whose first entry equals it (DPP and lane-swap steps,
+// no LDS), so all lanes agree on the winner, whose lane then moves on to its
+// next entry.  Lane j keeps pick j; the weights are the softmax
 // of the k picks renormalised over them, exp(l_j - l_0) / sum_i exp(l_i - l_0),
 // in fp32.  A shared expert (id E, weight 1) is appended as pick k.  The pages
 // do not print a routing rule; this is the top-k softmax router of the MoE layer
@@ -96,27 +98,6 @@ __device__ __forceinline__ float xor32(float v, int lane)
     return __builtin_bit_cast(float, xor32(__builtin_bit_cast(int, v), lane));
 }
 
-// (value, id) of the best pick over the wave (beats order), in every lane.
-__device__ __forceinline__ void wave_best(float &bv, int &bi, int lane)
-{
-#define PMOE_BEST_STEP(GETV, GETI)                                                                 \
-    {                                                                                              \
-        const float ov = GETV;                                                                     \
-        const int oi = GETI;                                                                       \
-        if (beats(ov, oi, bv, bi)) {                                                               \
-            bv = ov;                                                                               \
-            bi = oi;                                                                               \
-        }                                                                                          \
-    }
-    PMOE_BEST_STEP(dpp<kDppXor1>(bv), dpp<kDppXor1>(bi))
-    PMOE_BEST_STEP(dpp<kDppXor2>(bv), dpp<kDppXor2>(bi))
-    PMOE_BEST_STEP(dpp<kDppHalfMirror>(bv), dpp<kDppHalfMirror>(bi))
-    PMOE_BEST_STEP(dpp<kDppMirror>(bv), dpp<kDppMirror>(bi))
-    PMOE_BEST_STEP(xor16(bv, lane), xor16(bi, lane))
-    PMOE_BEST_STEP(xor32(bv, lane), xor32(bi, lane))
-#undef PMOE_BEST_STEP
-}
-
 __device__ __forceinline__ float wave_sum(float x, int lane)
 {
     x += dpp<kDppXor1>(x);
@@ -139,37 +120,120 @@ __device__ __forceinline__ void load_logits(const float *row, int E, int lane, f
     }
 }
 
+// Wave-wide max / min of an int, returned as a wave-uniform value.  Each step
+// combines with a DPP-permuted copy whose disabled lanes read the operation's
+// identity, so the move folds into the max / min: two in-quad swaps, the
+// half-row and row mirrors (every row of 16 then uniform), then lane 15 of a
+// row into the next row and lane 31 into rows 2 and 3, which leaves the
+// result in lane 63.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ int dpp_or(int ident, int v)
+{
+    return __builtin_amdgcn_update_dpp(ident, v, CTRL, ROWS, 0xF, false);
+}
+constexpr int kDppRowBcast15 = 0x142, kDppRowBcast31 = 0x143;
+
+__device__ __forceinline__ int wave_max(int x)
+{
+    constexpr int I = (int)0x80000000;
+    x = max(x, dpp_or<kDppXor1, 0xF>(I, x));
+    x = max(x, dpp_or<kDppXor2, 0xF>(I, x));
+    x = max(x, dpp_or<kDppHalfMirror, 0xF>(I, x));
+    x = max(x, dpp_or<kDppMirror, 0xF>(I, x));
+    x = max(x, dpp_or<kDppRowBcast15, 0xA>(I, x));
+    x = max(x, dpp_or<kDppRowBcast31, 0xC>(I, x));
+    return __builtin_amdgcn_readlane(x, 63);
+}
+
+__device__ __forceinline__ int wave_min(int x)
+{
+    constexpr int I = 0x7fffffff;
+    x = min(x, dpp_or<kDppXor1, 0xF>(I, x));
+    x = min(x, dpp_or<kDppXor2, 0xF>(I, x));
+    x = min(x, dpp_or<kDppHalfMirror, 0xF>(I, x));
+    x = min(x, dpp_or<kDppMirror, 0xF>(I, x));
+    x = min(x, dpp_or<kDppRowBcast15, 0xA>(I, x));
+    x = min(x, dpp_or<kDppRowBcast31, 0xC>(I, x));
+    return __builtin_amdgcn_readlane(x, 63);
+}
+
+// A finite fp32 logit as an int whose order is the float order: -0 and +0
+// both map to 0 (they compare equal as floats), negatives to -1 - |bits|.
+__device__ __forceinline__ int order_key(float v)
+{
+    int b = __builtin_bit_cast(int, v);
+    b = b == (int)0x80000000 ? 0 : b;
+    return b < 0 ? b ^ 0x7fffffff : b;
+}
+
+__device__ __forceinline__ float key_value(int k)
+{
+    return __builtin_bit_cast(float, k < 0 ? k ^ 0x7fffffff : k);
+}
+
+// Compare-exchange of lane-local entries a, b so that a comes first in the
+// pick order (larger logit first, equal logits by lower id).
+__device__ __forceinline__ void order_pair(int &ka, int &ia, int &kb, int &ib)
+{
+    const bool sw = kb > ka || (kb == ka && ib < ia);
+    const int tk = ka, ti = ia;
+    ka = sw ? kb : ka;
+    ia = sw ? ib : ia;
+    kb = sw ? tk : kb;
+    ib = sw ? ti : ib;
+}
+
+// Sort a lane's NV entries into pick order (odd-even transposition network).
+template <int NV>
+__device__ __forceinline__ void sort_lane(int (&sk)[NV], int (&si)[NV])
+{
+#pragma unroll
+    for (int round = 0; round < NV; round++)
+#pragma unroll
+        for (int t = round & 1; t + 1 < NV; t += 2)
+            order_pair(sk[t], si[t], sk[t + 1], si[t + 1]);
+}
+
 // Route one token with one wave from its loaded logits.  Writes ids/w[0 .. k+S)
-// and, when lds_ids is not null, the ids into LDS as well.
+// and, when lds_ids is not null, the ids into LDS as well.  Each lane sorts its
+// logits (lane, lane+64, ...) once into pick order; every pick is then the wave
+// maximum of the lanes' first entries, and among the lanes whose first entry
+// equals it the lowest expert id (the same order as comparing (logit, id)
+// pairs); the lane that holds it moves on to its next entry.
 template <int NV>
 __device__ void route_token(const float (&v)[NV], int E, int k, int S, int lane, int32_t *ids, float *w,
                             int32_t *lds_ids)
 {
-    uint32_t taken = 0;
+    constexpr int kNone = 0x7fffffff, kEmpty = (int)0x80000000; // id / key of a lane's used-up entries
+    int sk[NV], si[NV];
 #pragma unroll
-    for (int i = 0; i < NV; i++)
-        if (lane + 64 * i >= E)
-            taken |= 1u << i;
-    float my_v = 0.f;
-    int my_id = 0;
+    for (int i = 0; i < NV; i++) {
+        const int e = lane + 64 * i;
+        sk[i] = e < E ? order_key(v[i]) : kEmpty;
+        si[i] = e < E ? e : kNone;
+    }
+    sort_lane<NV>(sk, si);
+    int my_k = 0, my_id = 0;
     for (int j = 0; j < k; j++) {
-        float bv = 0.f;
-        int bi = -1;
-#pragma unroll
-        for (int i = 0; i < NV; i++) {
-            if (!((taken >> i) & 1u) && beats(v[i], lane + 64 * i, bv, bi)) {
-                bv = v[i];
-                bi = lane + 64 * i;
-            }
-        }
-        wave_best(bv, bi, lane);
-        if (bi >= 0 && (bi & 63) == lane)
-            taken |= 1u << (bi >> 6);
+        const int m = wave_max(sk[0]);
+        const int bi = wave_min(sk[0] == m ? si[0] : kNone);
         if (lane == j) {
-            my_v = bv;
+            my_k = m;
             my_id = bi;
         }
+        // the lane holding the pick drops it: its entries move up by one.  A
+        // bitwise blend, not a select between neighbours (which the compiler
+        // turns into an indexed access and then into compare chains)
+        const int msk = -(int)(si[0] == bi);
+#pragma unroll
+        for (int t = 0; t + 1 < NV; t++) {
+            sk[t] ^= (sk[t] ^ sk[t + 1]) & msk;
+            si[t] ^= (si[t] ^ si[t + 1]) & msk;
+        }
+        sk[NV - 1] ^= (sk[NV - 1] ^ kEmpty) & msk;
+        si[NV - 1] ^= (si[NV - 1] ^ kNone) & msk;
     }
+    const float my_v = key_value(my_k);
     const float lmax = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, my_v)));
     const float ex = lane < k ? expf(my_v - lmax) : 0.f;
     const float sum = wave_sum(ex, lane); // commutative pairs: every lane ends with the same sum
@@ -323,13 +387,11 @@ __device__ int wg_exclusive_scan(int v, int *s_tmp, int *total)
 }
 
 // Given per-expert token counts cnt(e): each expert's padded segment start in
-// seg_start[e] (and its count in seg_cnt[e]), num_padded, then the block->expert
-// map and the sentinel padding, one wave per expert run with its lanes on
-// consecutive positions.  Thread t owns expert t for the scan
-// (E_tot <= kAlignThreads).
+// seg_start[e] (and its count in seg_cnt[e]) and num_padded.  Thread t owns
+// expert t (E_tot <= kAlignThreads).
 template <class CountFn>
-__device__ void scan_experts(CountFn cnt, int E_tot, int BM, int n, int *seg_start, int *seg_cnt, int *s_tmp,
-                             const RouteArgs &a)
+__device__ void scan_segments(CountFn cnt, int E_tot, int BM, int *seg_start, int *seg_cnt, int *s_tmp,
+                              const RouteArgs &a)
 {
     const int e = threadIdx.x;
     const int c = e < E_tot ? cnt(e) : 0;
@@ -342,17 +404,33 @@ __device__ void scan_experts(CountFn cnt, int E_tot, int BM, int n, int *seg_sta
     }
     if (threadIdx.x == 0)
         *a.num_padded = total;
-    lds_sync();
-    // each wave takes whole experts; its lanes write consecutive positions
+}
+
+// The sentinel padding and block->expert map of experts [e0, e1), one wave per
+// expert run with its lanes on consecutive positions.
+template <class SegFn>
+__device__ void pad_segments(SegFn seg, int e0, int e1, int BM, int n, const RouteArgs &a)
+{
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    for (int x = w; x < E_tot; x += kAlignWaves) {
-        const int ox = seg_start[x], cx = seg_cnt[x];
+    for (int x = e0 + w; x < e1; x += kAlignWaves) {
+        int ox, cx;
+        seg(x, ox, cx);
         const int px = (cx + BM - 1) / BM * BM;
         for (int i = lane; i < px - cx; i += 64)
             a.sorted_ids[ox + cx + i] = n;
         for (int i = lane; i < px / BM; i += 64)
             a.block_expert[ox / BM + i] = x;
     }
+}
+
+// Both, for a batch aligned by one workgroup.
+template <class CountFn>
+__device__ void scan_experts(CountFn cnt, int E_tot, int BM, int n, int *seg_start, int *seg_cnt, int *s_tmp,
+                             const RouteArgs &a)
+{
+    scan_segments(cnt, E_tot, BM, seg_start, seg_cnt, s_tmp, a);
+    lds_sync();
+    pad_segments([&](int x, int &ox, int &cx) { ox = seg_start[x]; cx = seg_cnt[x]; }, 0, E_tot, BM, n, a);
 }
 
 // Turn per-wave counts s_cnt[w][e] into per-wave cursors starting at start(e).
@@ -540,6 +618,14 @@ __global__ __launch_bounds__(kAlignThreads) void k_align_single(const RouteArgs 
     align_in_one_wg(sm, n, a);
 }
 
+// Per-chunk counts are stored expert-major, counts[e][ch] with a row stride of
+// the chunk count rounded up to 4, so one expert's column is contiguous.
+__host__ __device__ __forceinline__ int count_stride(int64_t n)
+{
+    const int nch = (int)((n + kMultiChunk - 1) / kMultiChunk);
+    return (nch + 3) & ~3;
+}
+
 __global__ __launch_bounds__(kAlignThreads) void k_align_hist(const RouteArgs a)
 {
     __shared__ int hist[kMaxExpertsTotal];
@@ -561,48 +647,70 @@ __global__ __launch_bounds__(kAlignThreads) void k_align_hist(const RouteArgs a)
         if (v[r] >= 0)
             atomicAdd(&hist[v[r]], 1);
     lds_sync();
+    const int nchp = count_stride(n);
     for (int e = threadIdx.x; e < a.E_tot; e += kAlignThreads)
-        a.counts[(int64_t)blockIdx.x * a.E_tot + e] = hist[e];
+        a.counts[(int64_t)e * nchp + blockIdx.x] = hist[e];
 }
 
-// One workgroup: segment starts, block map, padding; then counts[ch][e] is
-// replaced in place by the start of chunk ch's run of expert e.
+// One workgroup: segment starts (left after the counts, as (start, count)
+// pairs per expert, for the scatter workgroups), num_padded; then counts[e][ch]
+// is replaced in place by the start of chunk ch's run of expert e.  Thread e
+// holds its expert's column in registers, kScanRegs chunks at a time (16-byte
+// loads, all issued before the first is used); up to kScanRegs chunks
+// (kScanRegs * kMultiChunk flat entries) the column is read once and serves
+// both the total and the cursors.
+constexpr int kScanRegs = 48;
+
 __global__ __launch_bounds__(kAlignThreads) void k_align_scan(const RouteArgs a, int nch)
 {
     __shared__ int seg[kMaxExpertsTotal];
     __shared__ int segc[kMaxExpertsTotal];
     __shared__ int tmp[kAlignWaves];
     const int n = (int)(a.T * a.keff);
-    // column e of counts[nch][E_tot], 8 loads in flight at a time
-    auto count = [&](int e) {
-        int c = 0;
-        for (int ch0 = 0; ch0 < nch; ch0 += 8) {
-            int v[8];
+    const int nchp = count_stride(a.T * a.keff);
+    const int e = threadIdx.x; // E_tot <= kAlignThreads
+    const bool mine = e < a.E_tot;
+    int32_t *col = a.counts + (int64_t)(mine ? e : 0) * nchp;
+    int4 v[kScanRegs / 4];
+    auto load = [&](int ch0) { // chunks ch0 .. ch0 + kScanRegs (ch0 and nchp are multiples of 4)
 #pragma unroll
-            for (int r = 0; r < 8; r++)
-                v[r] = ch0 + r < nch ? a.counts[(int64_t)(ch0 + r) * a.E_tot + e] : 0;
-#pragma unroll
-            for (int r = 0; r < 8; r++)
-                c += v[r];
-        }
-        return c;
+        for (int r = 0; r < kScanRegs / 4; r++)
+            v[r] = (mine && ch0 + 4 * r < nchp) ? *(const int4 *)(col + ch0 + 4 * r) : make_int4(0, 0, 0, 0);
     };
-    scan_experts(count, a.E_tot, a.BM, n, seg, segc, tmp, a);
-    lds_sync();
-    for (int e = threadIdx.x; e < a.E_tot; e += kAlignThreads) {
-        int run = seg[e];
-        for (int ch0 = 0; ch0 < nch; ch0 += 8) {
-            int v[8];
+    // entries past nch (row padding) are never written: count only ch < nch
+    auto at = [&](int ch0, int i) {
+        const int4 q = v[i / 4];
+        const int x = (i & 3) == 0 ? q.x : (i & 3) == 1 ? q.y : (i & 3) == 2 ? q.z : q.w;
+        return ch0 + i < nch ? x : 0;
+    };
+    int c = 0;
+    for (int ch0 = 0; ch0 < nch; ch0 += kScanRegs) {
+        load(ch0);
 #pragma unroll
-            for (int r = 0; r < 8; r++)
-                v[r] = ch0 + r < nch ? a.counts[(int64_t)(ch0 + r) * a.E_tot + e] : 0;
+        for (int i = 0; i < kScanRegs; i++)
+            c += at(ch0, i);
+    }
+    scan_segments([&](int) { return c; }, a.E_tot, a.BM, seg, segc, tmp, a);
+    if (!mine)
+        return;
+    // the segments, for the scatter workgroups that write the padding and block map
+    int32_t *segs = a.counts + (int64_t)a.E_tot * nchp;
+    segs[2 * e] = seg[e];
+    segs[2 * e + 1] = segc[e];
+    int run = seg[e]; // written by this thread in scan_segments
+    for (int ch0 = 0; ch0 < nch; ch0 += kScanRegs) {
+        if (nch > kScanRegs) // v holds the last batch: read this one again
+            load(ch0);
+        int out[kScanRegs];
 #pragma unroll
-            for (int r = 0; r < 8; r++) {
-                if (ch0 + r < nch)
-                    a.counts[(int64_t)(ch0 + r) * a.E_tot + e] = run;
-                run += v[r];
-            }
+        for (int i = 0; i < kScanRegs; i++) {
+            out[i] = run;
+            run += at(ch0, i);
         }
+#pragma unroll
+        for (int r = 0; r < kScanRegs / 4; r++)
+            if (ch0 + 4 * r < nch)
+                *(int4 *)(col + ch0 + 4 * r) = make_int4(out[4 * r], out[4 * r + 1], out[4 * r + 2], out[4 * r + 3]);
     }
 }
 
@@ -617,10 +725,16 @@ __global__ __launch_bounds__(kAlignThreads) void k_align_scatter(const RouteArgs
     lds_sync();
     chunk_hist(sm.ids, cn, a.E_tot, sm.cnt);
     lds_sync();
-    const int32_t *starts = a.counts + (int64_t)blockIdx.x * a.E_tot;
-    wave_cursors([&](int e) { return starts[e]; }, a.E_tot, sm.cnt);
+    const int nchp = count_stride(n);
+    wave_cursors([&](int e) { return a.counts[(int64_t)e * nchp + blockIdx.x]; }, a.E_tot, sm.cnt);
     lds_sync();
     chunk_scatter(sm.ids, cn, (int)lo, a.E_tot, sm.cnt, a.sorted_ids);
+    // this workgroup's share of the experts: their padding and block map (one
+    // workgroup would issue all of these stores alone, at one CU's store rate)
+    const int32_t *segs = a.counts + (int64_t)a.E_tot * nchp;
+    const int e0 = (int)((int64_t)blockIdx.x * a.E_tot / gridDim.x);
+    const int e1 = (int)((int64_t)(blockIdx.x + 1) * a.E_tot / gridDim.x);
+    pad_segments([&](int x, int &ox, int &cx) { ox = segs[2 * x]; cx = segs[2 * x + 1]; }, e0, e1, a.BM, (int)n, a);
 }
 
 template <int NV>
@@ -654,8 +768,8 @@ int64_t route_workspace_bytes(int64_t T, int keff, int E_tot)
     const int64_t n = T * keff;
     if (n <= kChunkElems)
         return 0;
-    const int64_t nch = (n + kMultiChunk - 1) / kMultiChunk;
-    return nch * E_tot * (int64_t)sizeof(int32_t);
+    // counts [E_tot][stride], then (segment start, count) per expert
+    return ((int64_t)count_stride(n) + 2) * E_tot * (int64_t)sizeof(int32_t);
 }
 
 hipError_t launch_route_align(const RouteArgs &a, hipStream_t s)
