@@ -181,18 +181,19 @@ def main():
     y = torch.empty_like(dev.x)
     stream = torch.cuda.current_stream()
 
+    # One step = routing + the layer, in one call (for a decode step the routing runs inside the gate/up
+    # launch).  The load buffer is refilled only by the concurrent-fill measurement (buffer 1): the
+    # "buffer read" mark of buffer 0 is deferred to its next fill instead of a stream marker per step.
     def step(i, contiguous=False):
         c = copies[i % R]
-        pm.moe_route(c["h"], dev.logits, bm, rt.topk_ids, rt.topk_w, rt.sorted_ids, rt.block_expert,
-                     rt.num_padded, ws, stream)
         if contiguous:
-            pm.moe_contiguous_forward(c["h"], c["w13"], c["w2"], dev.x, bm, rt.topk_ids, rt.topk_w, rt.sorted_ids,
-                                      rt.block_expert, rt.num_padded, y, ws, flags, stream)
+            pm.moe_route_contiguous_forward(c["h"], c["w13"], c["w2"], dev.logits, dev.x, bm, rt.topk_ids,
+                                            rt.topk_w, rt.sorted_ids, rt.block_expert, rt.num_padded, y, ws, flags,
+                                            stream)
         else:
-            # the load buffer is refilled only by the concurrent-fill measurement (buffer 1): the
-            # "buffer read" mark of buffer 0 is deferred to its next fill instead of a stream marker per step
-            pm.moe_paged_forward(c["h"], dev.x, bm, rt.topk_ids, rt.topk_w, rt.sorted_ids, rt.block_expert,
-                                 rt.num_padded, 0, y, ws, flags | pm.MOE_FLAG_DEFER_READ_DONE, stream)
+            pm.moe_route_forward(c["h"], dev.logits, dev.x, bm, rt.topk_ids, rt.topk_w, rt.sorted_ids,
+                                 rt.block_expert, rt.num_padded, 0, y, ws, flags | pm.MOE_FLAG_DEFER_READ_DONE,
+                                 stream)
 
     def timed(K, W, contiguous=False):
         for i in range(W):
@@ -224,13 +225,19 @@ def main():
         contig_ms = timed(args.steps, args.warmup, contiguous=True)
         print(f"# contiguous: {contig_ms * 1e3:.1f} us/step", file=sys.stderr, flush=True)
 
-    # ---- per-stage times from HIP events on the launch stream
+    # ---- per-stage times from HIP events on the launch stream (the library's events around its launches;
+    # a decode step's routing is part of its first launch, a larger batch's is timed around moe_route)
+    decode_form = pm.moe_forward_form(h0, T) == pm.MOE_FORM_DECODE
+    routed_form = pm.moe_route_forward_form(h0, T) == pm.MOE_FORM_DECODE_ROUTED
     for c in copies:
         pm.moe_stage_timing(c["h"], True)
     ra0, ra1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     route_ms = 0.0
     for i in range(args.steps):
         c = copies[i % R]
+        if routed_form:
+            step(i)
+            continue
         ra0.record(stream)
         pm.moe_route(c["h"], dev.logits, bm, rt.topk_ids, rt.topk_w, rt.sorted_ids, rt.block_expert,
                      rt.num_padded, ws, stream)
@@ -262,8 +269,9 @@ def main():
                 "unit": "TFLOP/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
     roof["traffic"] = measured_traffic(name, T, bm, args.atomic)
-    decode_form = pm.moe_forward_form(h0, T) == pm.MOE_FORM_DECODE
-    roof["kernel"] = ("k_dec_gate_up (paged gate/up, decode form: weight rows dotted with the picks' x rows + SiLU*mul)"
+    roof["kernel"] = ("k_dec_route_gate_up (routing + paged gate/up, decode form: weight rows dotted with the "
+                      "picks' x rows + SiLU*mul)" if routed_form else
+                      "k_dec_gate_up (paged gate/up, decode form: weight rows dotted with the picks' x rows + SiLU*mul)"
                       if decode_form else "k_gemm1 (paged gate/up GEMM + SiLU*mul)")
     roof["avg_launch_us"] = round(stage_us[0], 2)
     roof["algorithmic_bytes_per_launch"] = int(g1_bytes)
@@ -326,7 +334,9 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": WORKLOAD_TEXT[name], "name": name, "T": T, "block_m": bm,
-                   "placement": args.placement, "gemm_form": "decode" if decode_form else "tiles",
+                   "placement": args.placement,
+                   "gemm_form": "decode, routing in its gate/up launch" if routed_form else
+                   "decode" if decode_form else "tiles",
                    "combine": "atomic" if args.atomic else "ordered", "layer_copies_rotated": R},
         "hbm_gbs": round(gbs, 1),
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),

@@ -214,6 +214,34 @@ int moe_paged_forward(moe_pool *pool, const void *x, int64_t T, int32_t block_m,
                       void *y, void *workspace, size_t ws_bytes, uint32_t flags, void *stream);
 
 /*
+ * Routing and the layer output in one call (moe_route followed by
+ * moe_paged_forward, with the same arguments and the same outputs, bit for
+ * bit).  For the few tokens of a decode step (T <= 4, T <= block_m, and the
+ * shapes of the decode form, see moe_forward_form) the routing runs inside the
+ * gate/up launch: every workgroup of it routes the tokens itself and takes its
+ * expert from the result, so the step needs two launches instead of three.
+ * Larger batches run the routing kernels, then the forward.
+ *   logits       device fp32 [T][E] router logits (finite values).
+ *   topk_ids ... num_padded: out, as moe_route writes them.
+ *   x, active_buf, y, workspace, flags: as moe_paged_forward.
+ */
+int moe_route_forward(moe_pool *pool, const float *logits, const void *x, int64_t T, int32_t block_m,
+                      int32_t *topk_ids, float *topk_w, int32_t *sorted_ids, int32_t *block_expert,
+                      int32_t *num_padded, int32_t active_buf, void *y, void *workspace,
+                      size_t ws_bytes, uint32_t flags, void *stream);
+
+/*
+ * moe_route_forward with the weights in the two dense arrays of
+ * moe_contiguous_forward (the contiguous baseline of the one-call step; same
+ * kernels and launches, only the per-tile base address differs).
+ */
+int moe_route_contiguous_forward(const moe_pool *pool, const void *w13, const void *w2,
+                                 const float *logits, const void *x, int64_t T, int32_t block_m,
+                                 int32_t *topk_ids, float *topk_w, int32_t *sorted_ids,
+                                 int32_t *block_expert, int32_t *num_padded, void *y,
+                                 void *workspace, size_t ws_bytes, uint32_t flags, void *stream);
+
+/*
  * The same layer with the weights in two dense arrays (the contiguous
  * baseline the paged kernel is measured against; same kernels and tile
  * schedule, only the per-tile base address differs, so results are
@@ -283,6 +311,15 @@ int32_t moe_suggest_block_m(const moe_pool *pool, int64_t T);
 #define MOE_FORM_TILES 0
 #define MOE_FORM_DECODE 1
 int32_t moe_forward_form(const moe_pool *pool, int64_t T);
+
+/*
+ * Which launches moe_route_forward makes for T tokens: MOE_FORM_DECODE_ROUTED
+ * when the routing runs inside the decode form's gate/up launch (two launches
+ * in all), else the form of moe_forward_form, after the routing kernels.
+ * MOE_ERR_INVALID_ARG for a NULL pool or T < 0.
+ */
+#define MOE_FORM_DECODE_ROUTED 2
+int32_t moe_route_forward_form(const moe_pool *pool, int64_t T);
 
 /*
  * Stage timing of paged forwards, for measurement.  With enable != 0 every

@@ -35,6 +35,7 @@ MOE_FLAG_ATOMIC_COMBINE = 1
 MOE_FLAG_DEFER_READ_DONE = 2
 MOE_FORM_TILES = 0
 MOE_FORM_DECODE = 1
+MOE_FORM_DECODE_ROUTED = 2
 MOE_PAGE_KV = 0
 MOE_PAGE_CONV = 1
 MOE_ALLOC_NO_PACKING = 1
@@ -42,7 +43,8 @@ MOE_ALLOC_NO_PACKING = 1
 # every function moe.h declares
 EXPORTS = (
     "moe_pool_create", "moe_pool_destroy", "moe_validate_locs", "moe_set_expert_locs",
-    "moe_route_capacity", "moe_workspace_bytes", "moe_route", "moe_paged_forward", "moe_forward_form",
+    "moe_route_capacity", "moe_workspace_bytes", "moe_route", "moe_paged_forward", "moe_route_forward",
+    "moe_route_contiguous_forward", "moe_forward_form", "moe_route_forward_form",
     "moe_contiguous_forward", "moe_loadbuf_fill", "moe_resolve_addrs", "moe_suggest_block_m",
     "moe_stage_timing", "moe_stage_times", "moe_last_error", "moe_version",
     "moe_adjust_amounts", "moe_rank_experts", "moe_adjust_select",
@@ -115,6 +117,8 @@ def lib():
     L.moe_route.argtypes = [P, P, i64, i32, P, P, P, P, P, P, sz, P]
     L.moe_paged_forward.argtypes = [P, P, i64, i32, P, P, P, P, P, i32, P, P, sz, u32, P]
     L.moe_contiguous_forward.argtypes = [P, P, P, P, i64, i32, P, P, P, P, P, P, P, sz, u32, P]
+    L.moe_route_forward.argtypes = [P, P, P, i64, i32, P, P, P, P, P, i32, P, P, sz, u32, P]
+    L.moe_route_contiguous_forward.argtypes = [P, P, P, P, P, i64, i32, P, P, P, P, P, P, P, sz, u32, P]
     L.moe_loadbuf_fill.argtypes = [P, i32, i32, P, P, P]
     L.moe_resolve_addrs.argtypes = [P, i32, i64, P, P, P, P, P, P, P]
     L.moe_stage_timing.argtypes = [P, i32]
@@ -147,9 +151,11 @@ def lib():
     L.moe_suggest_block_m.restype = i32
     L.moe_forward_form.argtypes = [P, i64]
     L.moe_forward_form.restype = i32
+    L.moe_route_forward_form.argtypes = [P, i64]
+    L.moe_route_forward_form.restype = i32
     L.moe_last_error.restype = ctypes.c_char_p
     for name in EXPORTS:
-        if name not in ("moe_last_error", "moe_suggest_block_m", "moe_forward_form"):
+        if name not in ("moe_last_error", "moe_suggest_block_m", "moe_forward_form", "moe_route_forward_form"):
             getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -282,6 +288,23 @@ def moe_contiguous_forward(p: MoePool, w13, w2, x, block_m: int, topk_ids, topk_
                                         _stream(stream)))
 
 
+def moe_route_forward(p: MoePool, logits, x, block_m: int, topk_ids, topk_w, sorted_ids, block_expert, num_padded,
+                      active_buf: int, y, workspace, flags: int = 0, stream=None) -> None:
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().moe_route_forward(p.handle, _ptr(logits), _ptr(x), x.shape[0], block_m, _ptr(topk_ids),
+                                   _ptr(topk_w), _ptr(sorted_ids), _ptr(block_expert), _ptr(num_padded),
+                                   active_buf, _ptr(y), _ptr(workspace), ws_bytes, flags, _stream(stream)))
+
+
+def moe_route_contiguous_forward(p: MoePool, w13, w2, logits, x, block_m: int, topk_ids, topk_w, sorted_ids,
+                                 block_expert, num_padded, y, workspace, flags: int = 0, stream=None) -> None:
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().moe_route_contiguous_forward(p.handle, _ptr(w13), _ptr(w2), _ptr(logits), _ptr(x), x.shape[0],
+                                              block_m, _ptr(topk_ids), _ptr(topk_w), _ptr(sorted_ids),
+                                              _ptr(block_expert), _ptr(num_padded), _ptr(y), _ptr(workspace),
+                                              ws_bytes, flags, _stream(stream)))
+
+
 def moe_loadbuf_fill(p: MoePool, buf: int, slots: Sequence[int], host_src: Sequence, copy_stream=None) -> None:
     n = len(slots)
     s = np.ascontiguousarray(np.asarray(slots, dtype=np.int32))
@@ -377,6 +400,14 @@ def moe_forward_form(p: MoePool, T: int) -> int:
     return v
 
 
+def moe_route_forward_form(p: MoePool, T: int) -> int:
+    """MOE_FORM_DECODE_ROUTED when moe_route_forward routes inside the gate/up launch, else moe_forward_form's."""
+    v = int(lib().moe_route_forward_form(p.handle, T))
+    if v < 0:
+        _check(v)
+    return v
+
+
 def moe_version() -> int:
     return int(lib().moe_version())
 
@@ -416,6 +447,17 @@ def paged_forward(p: MoePool, x, r: RouteOut, active_buf: int, ws, flags: int = 
     moe_paged_forward(p, x, r.block_m, r.topk_ids, r.topk_w, r.sorted_ids, r.block_expert, r.num_padded,
                       active_buf, y, ws, flags, stream)
     return y
+
+
+def route_forward(p: MoePool, logits, x, active_buf: int, ws, block_m: int, flags: int = 0, y=None, stream=None):
+    """Routing and the layer output in one call; returns (y, RouteOut)."""
+    import torch
+    r = RouteOut(p, logits.shape[0], block_m, device=logits.device)
+    if y is None:
+        y = torch.empty_like(x)
+    moe_route_forward(p, logits, x, block_m, r.topk_ids, r.topk_w, r.sorted_ids, r.block_expert, r.num_padded,
+                      active_buf, y, ws, flags, stream)
+    return y, r
 
 
 def contiguous_forward(p: MoePool, w13, w2, x, r: RouteOut, ws, flags: int = 0, y=None, stream=None):

@@ -21,6 +21,7 @@
 // fixed butterfly; the same order for paged and contiguous weights.
 
 #include "internal.h"
+#include "route_token.h"
 
 #include <hip/hip_runtime.h>
 
@@ -33,6 +34,13 @@ constexpr int kDecColsPerGroup = 4; // down: output columns per workgroup
 constexpr int kDecMaxT = 8;         // tokens (hence valid rows of one expert block)
 constexpr int kDecMaxD = 4096;
 constexpr int kDecMaxKeff = 64;   // picks per token (top-k plus the shared expert)
+// Routing inside the gate/up launch pays off up to this many tokens: every
+// workgroup routes all of them before its first weight load, and the rows of
+// workgroups past the chosen experts route too before they can exit.
+// Measured one-step times (Qwen1.5-shaped layer, us, separate routing launch /
+// routing inside): T=1 24.3 / 19.5, 2 34.5 / 30.9, 4 56.7 / 54.0,
+// 6 73.5 / 74.7, 8 87.9 / 91.1.
+constexpr int kDecRoutedMaxT = 4;
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float v)
 {
@@ -87,29 +95,15 @@ __device__ __forceinline__ const uint16_t *matrix_base(const FwdArgs &a, int e, 
     }
 }
 
-// grid: (f / (kDecWaves * kDecRowsPerWave), expert blocks).  Every wave works
-// on its own (no LDS, no barrier): it issues its weight rows first, finds the
-// block's valid picks with a ballot over sorted_ids while those loads are in
-// flight, then reads each pick's x row (shared by all waves, so mostly from
+// Gate/up rows of expert e for the picks pick(0 .. ncand) (flat index or -1,
+// ascending): every wave works on its own (no LDS, no barrier): it issues its
+// weight rows first, finds the valid picks with a ballot while those loads are
+// in flight, then reads each pick's x row (shared by all waves, so mostly from
 // L2) and writes that pick's h values.
-template <bool PAGED, int NCH>
-__global__ __launch_bounds__(64 * kDecWaves) void k_dec_gate_up(const FwdArgs a)
+template <bool PAGED, int NCH, class PickFn>
+__device__ __forceinline__ void dec_gate_up_rows(const FwdArgs &a, int e, int ncand, PickFn pick)
 {
-    const int b = (int)blockIdx.y;
-    const int npad = *a.num_padded;
-    if ((int64_t)b * a.BM >= npad)
-        return;
-    const int e = a.block_expert[b];
-    if (e < 0 || e >= a.E_tot)
-        return;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int64_t nflat = a.T * a.keff;
-    const int32_t *sid = a.sorted_ids + (int64_t)b * a.BM;
-    // the block's slots: BM <= 256, so at most four per lane
-    int s4[4];
-#pragma unroll
-    for (int i = 0; i < 4; i++)
-        s4[i] = (i * 64 + lane < a.BM) ? sid[i * 64 + lane] : -1;
     const int r0 = ((int)blockIdx.x * kDecWaves + wave) * kDecRowsPerWave;
     const uint16_t *w1 = matrix_base<PAGED>(a, e, 0), *w3 = matrix_base<PAGED>(a, e, 1);
     uint4 g[kDecRowsPerWave][NCH], u[kDecRowsPerWave][NCH];
@@ -126,13 +120,13 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_dec_gate_up(const FwdArgs a)
                 u[r][c] = make_uint4(0, 0, 0, 0);
             }
         }
-    for (int i = 0; i < 4; i++) {
-        const bool ok = s4[i] >= 0 && s4[i] < nflat;
-        uint64_t m = __ballot(ok);
+    for (int i0 = 0; i0 < ncand; i0 += 64) {
+        const int cand = i0 + lane < ncand ? pick(i0 + lane) : -1;
+        uint64_t m = __ballot(cand >= 0);
         while (m) {
             const int bit = __builtin_ctzll(m);
             m &= m - 1;
-            const int flat = __shfl(s4[i], bit, 64);
+            const int flat = __shfl(cand, bit, 64);
             const int64_t t = flat / a.keff;
             float sg[kDecRowsPerWave], su[kDecRowsPerWave];
 #pragma unroll
@@ -155,6 +149,133 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_dec_gate_up(const FwdArgs a)
                     a.h[(int64_t)flat * a.f + r0 + r] = f32_to_bf16_rne(gs / (1.f + __expf(-gs)) * us);
             }
         }
+    }
+}
+
+// grid: (f / (kDecWaves * kDecRowsPerWave), expert blocks): the picks of block
+// b are its BM entries of sorted_ids.
+template <bool PAGED, int NCH>
+__global__ __launch_bounds__(64 * kDecWaves) void k_dec_gate_up(const FwdArgs a)
+{
+    const int b = (int)blockIdx.y;
+    const int npad = *a.num_padded;
+    if ((int64_t)b * a.BM >= npad)
+        return;
+    const int e = a.block_expert[b];
+    if (e < 0 || e >= a.E_tot)
+        return;
+    const int64_t nflat = a.T * a.keff;
+    const int32_t *sid = a.sorted_ids + (int64_t)b * a.BM;
+    dec_gate_up_rows<PAGED, NCH>(a, e, a.BM, [&](int i) {
+        const int flat = sid[i];
+        return (flat >= 0 && flat < nflat) ? flat : -1;
+    });
+}
+
+// Routing and the gate/up rows in one launch.  Every workgroup routes the
+// batch's T <= kDecMaxT tokens itself (route_token.h, the routing kernels'
+// code), marks the chosen experts in an LDS bitmap, and takes as its expert
+// the blockIdx.y-th chosen one in ascending id order -- the expert of aligned
+// block blockIdx.y, since with at most T <= block_m picks per expert every
+// expert fills one block.  Workgroup (0, 0) also writes the routing outputs
+// (topk ids and weights, which the down pass reads, and the aligned order, the
+// block map and num_padded, as the routing kernels would).
+template <bool PAGED, int NCH, int NV>
+__global__ __launch_bounds__(64 * kDecWaves) void k_dec_route_gate_up(const FwdArgs a, const DecRouteArgs ra)
+{
+    constexpr int kWords = kMaxExpertsTotal / 32;
+    __shared__ int32_t s_ids[kDecMaxT * kDecMaxKeff];
+    __shared__ float s_w[kDecMaxT * kDecMaxKeff];
+    __shared__ uint32_t s_bits[kWords];
+    __shared__ int s_pre[kWords + 1]; // exclusive prefix popcounts of s_bits, s_pre[nwords] = experts chosen
+    __shared__ int s_e;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    constexpr int NT = 64 * kDecWaves;
+    const int T = (int)a.T, keff = a.keff, n = T * keff;
+    const int nwords = (a.E_tot + 31) / 32;
+    for (int i = tid; i < nwords; i += NT)
+        s_bits[i] = 0;
+    if (tid == 0)
+        s_e = -1;
+    // wave w routes tokens w and w + kDecWaves (T <= 2 * kDecWaves): both
+    // tokens' logits are loaded before either is routed
+    constexpr int TPW = kDecMaxT / kDecWaves;
+    float v[TPW][NV];
+#pragma unroll
+    for (int q = 0; q < TPW; q++) {
+        const int t = wave + q * kDecWaves;
+        if (t < T)
+            rt::load_logits<NV>(ra.logits + (int64_t)t * ra.E, ra.E, lane, v[q]);
+    }
+    __syncthreads(); // the bitmap is cleared
+#pragma unroll
+    for (int q = 0; q < TPW; q++) {
+        const int t = wave + q * kDecWaves;
+        if (t < T) {
+            rt::route_token<NV>(v[q], ra.E, ra.k, ra.S, lane, s_ids + t * keff, s_w + t * keff, nullptr);
+            // lane j < k+S wrote pick j: mark its expert
+            if (lane < keff) {
+                const int id = s_ids[t * keff + lane];
+                atomicOr(&s_bits[id >> 5], 1u << (id & 31));
+            }
+        }
+    }
+    __syncthreads();
+    if (wave == 0) {
+        const uint32_t word = lane < nwords ? s_bits[lane] : 0u;
+        const int c = __popc(word);
+        int incl = c;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int y = __shfl_up(incl, off);
+            if (lane >= off)
+                incl += y;
+        }
+        if (lane < nwords)
+            s_pre[lane] = incl - c;
+        if (lane == nwords - 1)
+            s_pre[nwords] = incl;
+        const int u = (int)blockIdx.y;
+        if (lane < nwords && u >= incl - c && u < incl) {
+            uint32_t wd = word;
+            for (int q = u - (incl - c); q > 0; q--)
+                wd &= wd - 1; // drop the lower set bits
+            s_e = lane * 32 + __builtin_ctz(wd);
+        }
+    }
+    __syncthreads();
+    const int e = __builtin_amdgcn_readfirstlane(s_e); // uniform: the table entry and bases load as scalars
+    if (e >= 0)
+        dec_gate_up_rows<PAGED, NCH>(a, e, n, [&](int i) { return s_ids[i] == e ? i : -1; });
+    if (blockIdx.x != 0 || blockIdx.y != 0)
+        return;
+    // the routing outputs, as the routing kernels write them
+    const int U = s_pre[nwords], BM = a.BM;
+    for (int i = tid; i < n; i += NT) {
+        ra.topk_ids[i] = s_ids[i];
+        ra.topk_w[i] = s_w[i];
+    }
+    for (int i = tid; i < U * BM; i += NT)
+        ra.sorted_ids[i] = n;
+    for (int q = tid; q < U; q += NT) {
+        int wi = 0;
+        while (s_pre[wi + 1] <= q)
+            wi++;
+        uint32_t wd = s_bits[wi];
+        for (int r = q - s_pre[wi]; r > 0; r--)
+            wd &= wd - 1;
+        ra.block_expert[q] = wi * 32 + __builtin_ctz(wd);
+    }
+    if (tid == 0)
+        *ra.num_padded = U * BM;
+    __syncthreads(); // the sentinels are stored before the picks overwrite theirs
+    for (int i = tid; i < n; i += NT) {
+        const int ei = s_ids[i];
+        const int seg = BM * (s_pre[ei >> 5] + __popc(s_bits[ei >> 5] & ((1u << (ei & 31)) - 1u)));
+        int rank = 0;
+        for (int j = 0; j < i; j++)
+            rank += s_ids[j] == ei;
+        ra.sorted_ids[seg + rank] = i;
     }
 }
 
@@ -212,16 +333,51 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_dec_down(const FwdArgs a)
     }
 }
 
+template <int NCH_D>
+struct RoutedGateUp {
+    template <bool PAGED, int NV>
+    static void go(const FwdArgs &a, const DecRouteArgs &r, dim3 g, hipStream_t s)
+    {
+        k_dec_route_gate_up<PAGED, NCH_D, NV><<<g, 64 * kDecWaves, 0, s>>>(a, r);
+    }
+};
+
+template <bool PAGED, int NCH_D>
+void launch_gate_up(const FwdArgs &a, const DecRouteArgs *ra, dim3 g1, hipStream_t s)
+{
+    if (!ra) {
+        k_dec_gate_up<PAGED, NCH_D><<<g1, 64 * kDecWaves, 0, s>>>(a);
+        return;
+    }
+    using R = RoutedGateUp<NCH_D>;
+    if (ra->E <= 64)
+        R::template go<PAGED, 1>(a, *ra, g1, s);
+    else if (ra->E <= 128)
+        R::template go<PAGED, 2>(a, *ra, g1, s);
+    else if (ra->E <= 256)
+        R::template go<PAGED, 4>(a, *ra, g1, s);
+    else if (ra->E <= 512)
+        R::template go<PAGED, 8>(a, *ra, g1, s);
+    else
+        R::template go<PAGED, 16>(a, *ra, g1, s);
+}
+
 template <bool PAGED, int NCH_D, int NCH_F>
-hipError_t launch_t(const FwdArgs &a, hipStream_t s)
+hipError_t launch_t(const FwdArgs &a, const DecRouteArgs *ra, hipStream_t s)
 {
     auto mark = [&](int i) {
         if (a.ev[i])
             (void)hipEventRecord(a.ev[i], s);
     };
     mark(0);
-    const dim3 g1((unsigned)(a.f / (kDecWaves * kDecRowsPerWave)), (unsigned)a.blocks_cap);
-    k_dec_gate_up<PAGED, NCH_D><<<g1, 64 * kDecWaves, 0, s>>>(a);
+    // rows of workgroups: at most n / BM + min(n, E+S) blocks exist (the
+    // capacity bound, which counts every expert's padding, is far larger for a
+    // few tokens, and every surplus workgroup still has to start and exit)
+    const int64_t n = a.T * a.keff;
+    int64_t rows = n / a.BM + (n < a.E_tot ? n : a.E_tot);
+    rows = rows < a.blocks_cap ? rows : a.blocks_cap;
+    const dim3 g1((unsigned)(a.f / (kDecWaves * kDecRowsPerWave)), (unsigned)rows);
+    launch_gate_up<PAGED, NCH_D>(a, ra, g1, s);
     mark(1);
     const dim3 g2((unsigned)(a.d / kDecColsPerGroup), (unsigned)a.T);
     k_dec_down<PAGED, NCH_F><<<g2, 64 * kDecWaves, 0, s>>>(a);
@@ -231,29 +387,29 @@ hipError_t launch_t(const FwdArgs &a, hipStream_t s)
 }
 
 template <bool PAGED, int NCH_D>
-hipError_t launch_f(const FwdArgs &a, hipStream_t s)
+hipError_t launch_f(const FwdArgs &a, const DecRouteArgs *ra, hipStream_t s)
 {
     const int nf = (a.f + 511) / 512;
     if (nf <= 1)
-        return launch_t<PAGED, NCH_D, 1>(a, s);
+        return launch_t<PAGED, NCH_D, 1>(a, ra, s);
     if (nf <= 2)
-        return launch_t<PAGED, NCH_D, 2>(a, s);
+        return launch_t<PAGED, NCH_D, 2>(a, ra, s);
     if (nf <= 3)
-        return launch_t<PAGED, NCH_D, 3>(a, s);
-    return launch_t<PAGED, NCH_D, 4>(a, s);
+        return launch_t<PAGED, NCH_D, 3>(a, ra, s);
+    return launch_t<PAGED, NCH_D, 4>(a, ra, s);
 }
 
 template <bool PAGED>
-hipError_t launch_d(const FwdArgs &a, hipStream_t s)
+hipError_t launch_d(const FwdArgs &a, const DecRouteArgs *ra, hipStream_t s)
 {
     const int nd = (a.d + 511) / 512;
     if (nd <= 1)
-        return launch_f<PAGED, 1>(a, s);
+        return launch_f<PAGED, 1>(a, ra, s);
     if (nd <= 2)
-        return launch_f<PAGED, 2>(a, s);
+        return launch_f<PAGED, 2>(a, ra, s);
     if (nd <= 4)
-        return launch_f<PAGED, 4>(a, s);
-    return launch_f<PAGED, 8>(a, s);
+        return launch_f<PAGED, 4>(a, ra, s);
+    return launch_f<PAGED, 8>(a, ra, s);
 }
 
 } // namespace
@@ -268,7 +424,19 @@ bool decode_fits(const FwdArgs &a)
 
 hipError_t launch_decode(const FwdArgs &a, hipStream_t s)
 {
-    return a.locs ? launch_d<true>(a, s) : launch_d<false>(a, s);
+    return a.locs ? launch_d<true>(a, nullptr, s) : launch_d<false>(a, nullptr, s);
+}
+
+bool decode_routed_fits(const FwdArgs &a, const DecRouteArgs &r)
+{
+    // every chosen expert fills one aligned block: at most T <= block_m picks each
+    return decode_fits(a) && a.T <= kDecRoutedMaxT && a.T <= a.BM && r.E >= 1 && r.E <= 1024 &&
+           a.E_tot <= kMaxExpertsTotal;
+}
+
+hipError_t launch_decode_routed(const FwdArgs &a, const DecRouteArgs &r, hipStream_t s)
+{
+    return a.locs ? launch_d<true>(a, &r, s) : launch_d<false>(a, &r, s);
 }
 
 } // namespace pmoe

@@ -61,6 +61,23 @@ struct FwdArgs {
 
 hipError_t launch_forward(const FwdArgs &a, hipStream_t s);
 
+// Routing done inside the decode form's gate/up launch (route + forward in one
+// call for a few tokens): the router's inputs and the routing outputs the
+// launch writes (the same as the routing kernels').
+struct DecRouteArgs {
+    const float *logits; // [T][E] fp32
+    int E, k, S;
+    int32_t *topk_ids;
+    float *topk_w;
+    int32_t *sorted_ids;
+    int32_t *block_expert;
+    int32_t *num_padded;
+};
+bool decode_fits(const FwdArgs &a);
+bool decode_routed_fits(const FwdArgs &a, const DecRouteArgs &r);
+hipError_t launch_decode(const FwdArgs &a, hipStream_t s);
+hipError_t launch_decode_routed(const FwdArgs &a, const DecRouteArgs &r, hipStream_t s);
+
 struct ResolveArgs {
     const DevLoc *locs;
     const uint16_t *pool;

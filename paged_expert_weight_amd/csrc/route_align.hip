@@ -1,15 +1,11 @@
 // Top-k softmax routing and token alignment (gfx950, wave64).
 //
-// Routing: one wave per token.  Lane L holds logits L, L+64, ..., sorted once
-// into pick order (larger logit first, equal logits by lower id); each of the k
-// rounds takes a butterfly max of the lanes' first entries and a butterfly min
-// of the ids of the lanes whose first entry equals it (DPP and lane-swap steps,
-// no LDS), so all lanes agree on the winner, whose lane then moves on to its
-// next entry.  Lane j keeps pick j; the weights are the softmax
-// of the k picks renormalised over them, exp(l_j - l_0) / sum_i exp(l_i - l_0),
-// in fp32.  A shared expert (id E, weight 1) is appended as pick k.  The pages
-// do not print a routing rule; this is the top-k softmax router of the MoE layer
-// whose fused kernel the Rimuru digest's kernel section rewrites.
+// Routing: one wave per token (route_token.h: each lane sorts its logits into
+// pick order, every pick is a wave max of the lanes' first entries with ties
+// to the lower id; weights are the softmax renormalised over the k picks; a
+// shared expert is appended with weight 1).  The pages do not print a routing
+// rule; this is the top-k softmax router of the MoE layer whose fused kernel
+// the Rimuru digest's kernel section rewrites.
 //
 // Alignment: a stable counting sort of the flat picks i = t*(k+S) + j by expert
 // with each expert's run padded to the GEMM tile height BM, so that every
@@ -29,9 +25,12 @@
 // smallest with a leaner eight-wave form); larger ones route with one wave per token and align in one workgroup up to
 // kChunkElems entries, or with histogram / scan / scatter kernels over chunks.
 #include "internal.h"
+#include "route_token.h"
 
 namespace pmoe {
 namespace {
+
+using namespace rt;
 
 // Workgroup barrier that orders LDS only.  Nothing these kernels store to
 // global memory is read back by another thread of the same launch, so the
@@ -49,207 +48,6 @@ constexpr int kAlignThreads = 64 * kAlignWaves;
 constexpr int kChunkElems = 8192; // flat entries aligned by one workgroup (the one-workgroup forms)
 constexpr int kMultiChunk = 2048;  // flat entries per histogram / scatter workgroup of larger batches
 constexpr int kSmallTokens = 64;  // route + align in one workgroup when T <= this (and T*keff <= kChunkElems)
-
-__device__ __forceinline__ bool beats(float va, int ia, float vb, int ib)
-{
-    if (ia < 0)
-        return false;
-    if (ib < 0)
-        return true;
-    return va > vb || (va == vb && ia < ib);
-}
-
-// Cross-lane exchange without the LDS crossbar.  Within a row of 16 lanes:
-// DPP quad_perm [1,0,3,2] (lane ^ 1), quad_perm [2,3,0,1] (lane ^ 2),
-// row_half_mirror (lane i <-> 7-i of its 8) and row_mirror (i <-> 15-i).
-// Across rows: v_permlane16_swap / v_permlane32_swap, which hand every lane the
-// value of lane ^ 16 / lane ^ 32 in one of their two results.  Applied in this
-// order, each step pairs every lane with a lane of the other half of the group
-// the previous steps made uniform, so a commutative, associative combine ends
-// with the same result in all 64 lanes.
-template <int CTRL>
-__device__ __forceinline__ int dpp(int v)
-{
-    return __builtin_amdgcn_update_dpp(v, v, CTRL, 0xF, 0xF, false);
-}
-template <int CTRL>
-__device__ __forceinline__ float dpp(float v)
-{
-    return __builtin_bit_cast(float, dpp<CTRL>(__builtin_bit_cast(int, v)));
-}
-constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
-
-__device__ __forceinline__ int xor16(int v, int lane)
-{
-    const auto r = __builtin_amdgcn_permlane16_swap((unsigned)v, (unsigned)v, false, false);
-    return (int)(((lane >> 4) & 1) ? r[0] : r[1]);
-}
-__device__ __forceinline__ int xor32(int v, int lane)
-{
-    const auto r = __builtin_amdgcn_permlane32_swap((unsigned)v, (unsigned)v, false, false);
-    return (int)(lane >= 32 ? r[0] : r[1]);
-}
-__device__ __forceinline__ float xor16(float v, int lane)
-{
-    return __builtin_bit_cast(float, xor16(__builtin_bit_cast(int, v), lane));
-}
-__device__ __forceinline__ float xor32(float v, int lane)
-{
-    return __builtin_bit_cast(float, xor32(__builtin_bit_cast(int, v), lane));
-}
-
-__device__ __forceinline__ float wave_sum(float x, int lane)
-{
-    x += dpp<kDppXor1>(x);
-    x += dpp<kDppXor2>(x);
-    x += dpp<kDppHalfMirror>(x);
-    x += dpp<kDppMirror>(x);
-    x += xor16(x, lane);
-    x += xor32(x, lane);
-    return x;
-}
-
-// Lane L's logits L, L+64, ... of one token row.
-template <int NV>
-__device__ __forceinline__ void load_logits(const float *row, int E, int lane, float (&v)[NV])
-{
-#pragma unroll
-    for (int i = 0; i < NV; i++) {
-        const int e = lane + 64 * i;
-        v[i] = e < E ? row[e] : 0.f;
-    }
-}
-
-// Wave-wide max / min of an int, returned as a wave-uniform value.  Each step
-// combines with a DPP-permuted copy whose disabled lanes read the operation's
-// identity, so the move folds into the max / min: two in-quad swaps, the
-// half-row and row mirrors (every row of 16 then uniform), then lane 15 of a
-// row into the next row and lane 31 into rows 2 and 3, which leaves the
-// result in lane 63.
-template <int CTRL, int ROWS>
-__device__ __forceinline__ int dpp_or(int ident, int v)
-{
-    return __builtin_amdgcn_update_dpp(ident, v, CTRL, ROWS, 0xF, false);
-}
-constexpr int kDppRowBcast15 = 0x142, kDppRowBcast31 = 0x143;
-
-__device__ __forceinline__ int wave_max(int x)
-{
-    constexpr int I = (int)0x80000000;
-    x = max(x, dpp_or<kDppXor1, 0xF>(I, x));
-    x = max(x, dpp_or<kDppXor2, 0xF>(I, x));
-    x = max(x, dpp_or<kDppHalfMirror, 0xF>(I, x));
-    x = max(x, dpp_or<kDppMirror, 0xF>(I, x));
-    x = max(x, dpp_or<kDppRowBcast15, 0xA>(I, x));
-    x = max(x, dpp_or<kDppRowBcast31, 0xC>(I, x));
-    return __builtin_amdgcn_readlane(x, 63);
-}
-
-__device__ __forceinline__ int wave_min(int x)
-{
-    constexpr int I = 0x7fffffff;
-    x = min(x, dpp_or<kDppXor1, 0xF>(I, x));
-    x = min(x, dpp_or<kDppXor2, 0xF>(I, x));
-    x = min(x, dpp_or<kDppHalfMirror, 0xF>(I, x));
-    x = min(x, dpp_or<kDppMirror, 0xF>(I, x));
-    x = min(x, dpp_or<kDppRowBcast15, 0xA>(I, x));
-    x = min(x, dpp_or<kDppRowBcast31, 0xC>(I, x));
-    return __builtin_amdgcn_readlane(x, 63);
-}
-
-// A finite fp32 logit as an int whose order is the float order: -0 and +0
-// both map to 0 (they compare equal as floats), negatives to -1 - |bits|.
-__device__ __forceinline__ int order_key(float v)
-{
-    int b = __builtin_bit_cast(int, v);
-    b = b == (int)0x80000000 ? 0 : b;
-    return b < 0 ? b ^ 0x7fffffff : b;
-}
-
-__device__ __forceinline__ float key_value(int k)
-{
-    return __builtin_bit_cast(float, k < 0 ? k ^ 0x7fffffff : k);
-}
-
-// Compare-exchange of lane-local entries a, b so that a comes first in the
-// pick order (larger logit first, equal logits by lower id).
-__device__ __forceinline__ void order_pair(int &ka, int &ia, int &kb, int &ib)
-{
-    const bool sw = kb > ka || (kb == ka && ib < ia);
-    const int tk = ka, ti = ia;
-    ka = sw ? kb : ka;
-    ia = sw ? ib : ia;
-    kb = sw ? tk : kb;
-    ib = sw ? ti : ib;
-}
-
-// Sort a lane's NV entries into pick order (odd-even transposition network).
-template <int NV>
-__device__ __forceinline__ void sort_lane(int (&sk)[NV], int (&si)[NV])
-{
-#pragma unroll
-    for (int round = 0; round < NV; round++)
-#pragma unroll
-        for (int t = round & 1; t + 1 < NV; t += 2)
-            order_pair(sk[t], si[t], sk[t + 1], si[t + 1]);
-}
-
-// Route one token with one wave from its loaded logits.  Writes ids/w[0 .. k+S)
-// and, when lds_ids is not null, the ids into LDS as well.  Each lane sorts its
-// logits (lane, lane+64, ...) once into pick order; every pick is then the wave
-// maximum of the lanes' first entries, and among the lanes whose first entry
-// equals it the lowest expert id (the same order as comparing (logit, id)
-// pairs); the lane that holds it moves on to its next entry.
-template <int NV>
-__device__ void route_token(const float (&v)[NV], int E, int k, int S, int lane, int32_t *ids, float *w,
-                            int32_t *lds_ids)
-{
-    constexpr int kNone = 0x7fffffff, kEmpty = (int)0x80000000; // id / key of a lane's used-up entries
-    int sk[NV], si[NV];
-#pragma unroll
-    for (int i = 0; i < NV; i++) {
-        const int e = lane + 64 * i;
-        sk[i] = e < E ? order_key(v[i]) : kEmpty;
-        si[i] = e < E ? e : kNone;
-    }
-    sort_lane<NV>(sk, si);
-    int my_k = 0, my_id = 0;
-    for (int j = 0; j < k; j++) {
-        const int m = wave_max(sk[0]);
-        const int bi = wave_min(sk[0] == m ? si[0] : kNone);
-        if (lane == j) {
-            my_k = m;
-            my_id = bi;
-        }
-        // the lane holding the pick drops it: its entries move up by one.  A
-        // bitwise blend, not a select between neighbours (which the compiler
-        // turns into an indexed access and then into compare chains)
-        const int msk = -(int)(si[0] == bi);
-#pragma unroll
-        for (int t = 0; t + 1 < NV; t++) {
-            sk[t] ^= (sk[t] ^ sk[t + 1]) & msk;
-            si[t] ^= (si[t] ^ si[t + 1]) & msk;
-        }
-        sk[NV - 1] ^= (sk[NV - 1] ^ kEmpty) & msk;
-        si[NV - 1] ^= (si[NV - 1] ^ kNone) & msk;
-    }
-    const float my_v = key_value(my_k);
-    const float lmax = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, my_v)));
-    const float ex = lane < k ? expf(my_v - lmax) : 0.f;
-    const float sum = wave_sum(ex, lane); // commutative pairs: every lane ends with the same sum
-    if (lane < k) {
-        ids[lane] = my_id;
-        w[lane] = ex / sum;
-        if (lds_ids)
-            lds_ids[lane] = my_id;
-    }
-    if (S && lane == k) {
-        ids[k] = E;
-        w[k] = 1.f;
-        if (lds_ids)
-            lds_ids[k] = E;
-    }
-}
 
 template <int NV>
 __global__ __launch_bounds__(256) void k_route(const RouteArgs a)

@@ -45,13 +45,6 @@ constexpr size_t kMaxTimedForwards = 1024;
 // invalidate the caches after every forward.
 constexpr unsigned kReadDoneEvent = hipEventDisableTiming | hipEventDisableSystemFence;
 
-namespace pmoe {
-// Decode form of the two GEMMs for a few tokens (vector-ALU dot products,
-// down projection and combine in one pass); used when decode_fits holds.
-bool decode_fits(const FwdArgs &a);
-hipError_t launch_decode(const FwdArgs &a, hipStream_t s);
-} // namespace pmoe
-
 namespace {
 
 thread_local std::string g_err;
@@ -184,10 +177,37 @@ int check_dev(const void *ptr, size_t align, const char *name)
             return rc_;                                                                            \
     } while (0)
 
+pmoe::RouteArgs route_args(const moe_pool *p, const float *logits, int64_t T, int32_t bm, int32_t *ids, float *w,
+                           int32_t *sorted, int32_t *blk, int32_t *npad, void *ws, const Sizes &sz)
+{
+    pmoe::RouteArgs a{};
+    a.logits = logits;
+    a.T = T;
+    a.E = p->desc.num_experts;
+    a.k = p->desc.top_k;
+    a.S = p->desc.num_shared;
+    a.keff = p->keff;
+    a.E_tot = p->E_tot;
+    a.BM = bm;
+    a.topk_ids = ids;
+    a.topk_w = w;
+    a.sorted_ids = sorted;
+    a.block_expert = blk;
+    a.num_padded = npad;
+    a.sorted_cap = sz.sorted_cap;
+    a.blocks_cap = sz.blocks_cap;
+    a.counts = (int32_t *)((char *)ws + sz.off_counts);
+    return a;
+}
+
+// The forward on routing outputs (ids ... npad).  With logits (route + forward
+// in one call) the routing is computed first: inside the decode form's gate/up
+// launch when decode_routed_fits holds, else by the routing kernels.
 int forward_common(const moe_pool *p, const void *w13, const void *w2, bool paged, const void *x,
                    int64_t T, int32_t bm, const int32_t *ids, const float *w, const int32_t *sorted,
                    const int32_t *blk, const int32_t *npad, int32_t active_buf, void *y, void *ws,
-                   size_t ws_bytes, uint32_t flags, hipStream_t s, hipEvent_t *ev)
+                   size_t ws_bytes, uint32_t flags, hipStream_t s, hipEvent_t *ev,
+                   const float *logits = nullptr)
 {
     if (flags & ~MOE_FLAG_ATOMIC_COMBINE)
         return fail(MOE_ERR_INVALID_ARG, "unknown flag bits");
@@ -237,6 +257,26 @@ int forward_common(const moe_pool *p, const void *w13, const void *w2, bool page
     if (ev)
         for (int i = 0; i < 4; i++)
             a.ev[i] = ev[i];
+    if (logits) {
+        CHECK(check_dev(logits, 4, "logits"));
+        pmoe::DecRouteArgs dr{};
+        dr.logits = logits;
+        dr.E = p->desc.num_experts;
+        dr.k = p->desc.top_k;
+        dr.S = p->desc.num_shared;
+        dr.topk_ids = const_cast<int32_t *>(ids);
+        dr.topk_w = const_cast<float *>(w);
+        dr.sorted_ids = const_cast<int32_t *>(sorted);
+        dr.block_expert = const_cast<int32_t *>(blk);
+        dr.num_padded = const_cast<int32_t *>(npad);
+        if (pmoe::decode_routed_fits(a, dr)) {
+            HIP_TRY(pmoe::launch_decode_routed(a, dr, s));
+            return MOE_OK;
+        }
+        const pmoe::RouteArgs ra = route_args(p, logits, T, bm, dr.topk_ids, dr.topk_w, dr.sorted_ids,
+                                              dr.block_expert, dr.num_padded, ws, sz);
+        HIP_TRY(pmoe::launch_route_align(ra, s));
+    }
     if (pmoe::decode_fits(a))
         HIP_TRY(pmoe::launch_decode(a, s));
     else
@@ -277,7 +317,7 @@ extern "C" {
 
 const char *moe_last_error(void) { return g_err.c_str(); }
 
-int moe_version(void) { return 102; }
+int moe_version(void) { return 103; }
 
 int moe_validate_locs(const moe_pool_desc *desc, const moe_expert_loc *locs, int32_t n)
 {
@@ -450,31 +490,17 @@ int moe_route(moe_pool *p, const float *logits, int64_t T, int32_t block_m, int3
         if (ws_bytes < sz.off_h)
             return fail(MOE_ERR_WORKSPACE, "workspace too small for routing");
     }
-    pmoe::RouteArgs a{};
-    a.logits = logits;
-    a.T = T;
-    a.E = p->desc.num_experts;
-    a.k = p->desc.top_k;
-    a.S = p->desc.num_shared;
-    a.keff = p->keff;
-    a.E_tot = p->E_tot;
-    a.BM = block_m;
-    a.topk_ids = topk_ids;
-    a.topk_w = topk_w;
-    a.sorted_ids = sorted_ids;
-    a.block_expert = block_expert;
-    a.num_padded = num_padded;
-    a.sorted_cap = sz.sorted_cap;
-    a.blocks_cap = sz.blocks_cap;
-    a.counts = (int32_t *)((char *)ws + sz.off_counts);
+    const pmoe::RouteArgs a =
+        route_args(p, logits, T, block_m, topk_ids, topk_w, sorted_ids, block_expert, num_padded, ws, sz);
     HIP_TRY(pmoe::launch_route_align(a, (hipStream_t)stream));
     return MOE_OK;
 }
 
-int moe_paged_forward(moe_pool *p, const void *x, int64_t T, int32_t block_m, const int32_t *topk_ids,
-                      const float *topk_w, const int32_t *sorted_ids, const int32_t *block_expert,
-                      const int32_t *num_padded, int32_t active_buf, void *y, void *ws, size_t ws_bytes,
-                      uint32_t flags, void *stream)
+namespace {
+
+// Checks of a paged forward, and its wait for the last fill of the load
+// buffer it reads (read after write).
+int paged_begin(moe_pool *p, int64_t T, int32_t active_buf, uint32_t flags, hipStream_t s)
 {
     if (!p)
         return fail(MOE_ERR_INVALID_ARG, "pool is null");
@@ -487,7 +513,6 @@ int moe_paged_forward(moe_pool *p, const void *x, int64_t T, int32_t block_m, co
     if (p->uses_loadbuf && !p->ever_filled[active_buf])
         return fail(MOE_ERR_STATE, "load buffer " + std::to_string(active_buf) +
                                        " was never filled but the table reads from it");
-    hipStream_t s = (hipStream_t)stream;
     if (T > 0 && p->uses_loadbuf) {
         // a fill that has already completed needs no wait on the stream (the
         // wait would still cost a queue round trip before the first kernel)
@@ -499,9 +524,13 @@ int moe_paged_forward(moe_pool *p, const void *x, int64_t T, int32_t block_m, co
             return hip_fail(q, "hipEventQuery");
         }
     }
-    CHECK(forward_common(p, nullptr, nullptr, true, x, T, block_m, topk_ids, topk_w, sorted_ids, block_expert,
-                         num_padded, active_buf, y, ws, ws_bytes, flags & MOE_FLAG_ATOMIC_COMBINE, s,
-                         T > 0 ? next_timing_events(p) : nullptr));
+    return MOE_OK;
+}
+
+// After a paged forward: mark its load buffer read (write after read), now
+// or (MOE_FLAG_DEFER_READ_DONE) at the buffer's next fill.
+int paged_end(moe_pool *p, int64_t T, int32_t active_buf, uint32_t flags, hipStream_t s)
+{
     if (T > 0 && p->uses_loadbuf) {
         if (flags & MOE_FLAG_DEFER_READ_DONE) {
             auto &rd = p->deferred_readers[active_buf];
@@ -513,6 +542,51 @@ int moe_paged_forward(moe_pool *p, const void *x, int64_t T, int32_t block_m, co
         }
     }
     return MOE_OK;
+}
+
+} // namespace
+
+int moe_paged_forward(moe_pool *p, const void *x, int64_t T, int32_t block_m, const int32_t *topk_ids,
+                      const float *topk_w, const int32_t *sorted_ids, const int32_t *block_expert,
+                      const int32_t *num_padded, int32_t active_buf, void *y, void *ws, size_t ws_bytes,
+                      uint32_t flags, void *stream)
+{
+    hipStream_t s = (hipStream_t)stream;
+    CHECK(paged_begin(p, T, active_buf, flags, s));
+    CHECK(forward_common(p, nullptr, nullptr, true, x, T, block_m, topk_ids, topk_w, sorted_ids, block_expert,
+                         num_padded, active_buf, y, ws, ws_bytes, flags & MOE_FLAG_ATOMIC_COMBINE, s,
+                         T > 0 ? next_timing_events(p) : nullptr));
+    return paged_end(p, T, active_buf, flags, s);
+}
+
+int moe_route_forward(moe_pool *p, const float *logits, const void *x, int64_t T, int32_t block_m,
+                      int32_t *topk_ids, float *topk_w, int32_t *sorted_ids, int32_t *block_expert,
+                      int32_t *num_padded, int32_t active_buf, void *y, void *ws, size_t ws_bytes,
+                      uint32_t flags, void *stream)
+{
+    hipStream_t s = (hipStream_t)stream;
+    CHECK(paged_begin(p, T, active_buf, flags, s));
+    if (T > 0 && !logits)
+        return fail(MOE_ERR_INVALID_ARG, "logits is null");
+    CHECK(forward_common(p, nullptr, nullptr, true, x, T, block_m, topk_ids, topk_w, sorted_ids, block_expert,
+                         num_padded, active_buf, y, ws, ws_bytes, flags & MOE_FLAG_ATOMIC_COMBINE, s,
+                         T > 0 ? next_timing_events(p) : nullptr, logits));
+    return paged_end(p, T, active_buf, flags, s);
+}
+
+int moe_route_contiguous_forward(const moe_pool *p, const void *w13, const void *w2, const float *logits,
+                                 const void *x, int64_t T, int32_t block_m, int32_t *topk_ids, float *topk_w,
+                                 int32_t *sorted_ids, int32_t *block_expert, int32_t *num_padded, void *y,
+                                 void *ws, size_t ws_bytes, uint32_t flags, void *stream)
+{
+    if (!p)
+        return fail(MOE_ERR_INVALID_ARG, "pool is null");
+    if (T > 0 && !logits)
+        return fail(MOE_ERR_INVALID_ARG, "logits is null");
+    CHECK(check_dev(w13, 16, "w13"));
+    CHECK(check_dev(w2, 16, "w2"));
+    return forward_common(p, w13, w2, false, x, T, block_m, topk_ids, topk_w, sorted_ids, block_expert,
+                          num_padded, 0, y, ws, ws_bytes, flags, (hipStream_t)stream, nullptr, logits);
 }
 
 int moe_contiguous_forward(const moe_pool *p, const void *w13, const void *w2, const void *x, int64_t T,
@@ -658,6 +732,23 @@ int32_t moe_forward_form(const moe_pool *p, int64_t T)
     a.f = p->desc.f;
     a.keff = p->keff;
     return pmoe::decode_fits(a) ? MOE_FORM_DECODE : MOE_FORM_TILES;
+}
+
+int32_t moe_route_forward_form(const moe_pool *p, int64_t T)
+{
+    const int32_t form = moe_forward_form(p, T);
+    if (form != MOE_FORM_DECODE)
+        return form;
+    pmoe::FwdArgs a{};
+    a.T = T;
+    a.d = p->desc.d;
+    a.f = p->desc.f;
+    a.keff = p->keff;
+    a.E_tot = p->E_tot;
+    a.BM = 16; // the smallest block height; the routed form needs T <= block_m
+    pmoe::DecRouteArgs r{};
+    r.E = p->desc.num_experts;
+    return pmoe::decode_routed_fits(a, r) ? MOE_FORM_DECODE_ROUTED : form;
 }
 
 int32_t moe_suggest_block_m(const moe_pool *p, int64_t T)

@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol(lib):
     for name in sorted(declared):
         assert hasattr(lib, name), f"{name} declared in include/ but not exported"
     assert declared == set(pm.EXPORTS)
-    assert lib.moe_version() == 102
+    assert lib.moe_version() == 103
 
 
 def _desc(**kw):
@@ -119,6 +119,10 @@ def test_null_handles_rejected(lib):
     assert lib.moe_workspace_bytes(None, 4, 16, 0, ctypes.byref(n)) == pm.MOE_ERR_INVALID_ARG
     assert lib.moe_paged_forward(None, None, 1, 16, None, None, None, None, None, 0, None, None, 0, 0,
                                  None) == pm.MOE_ERR_INVALID_ARG
+    assert lib.moe_route_forward(None, None, None, 1, 16, None, None, None, None, None, 0, None, None, 0, 0,
+                                 None) == pm.MOE_ERR_INVALID_ARG
+    assert lib.moe_route_contiguous_forward(None, None, None, None, None, 1, 16, None, None, None, None, None,
+                                            None, None, 0, 0, None) == pm.MOE_ERR_INVALID_ARG
     assert lib.moe_pool_destroy(None) == pm.MOE_OK
 
 
