@@ -741,6 +741,8 @@ using Tiles128 = Tiles<128, Gemm<128, 64, 2, 2, 1, 64, 2, true>, Gemm<128, 128, 
 using Down128w = Gemm<128, 256, 2, 4, 1, 64, 3, false>;
 using Tiles128w = Tiles<128, Gemm<128, 256, 2, 4, 1, 64, 2, true>, Down128w>;
 using Tiles128d = Tiles<128, Gemm<128, 64, 2, 2, 1, 64, 2, true>, Down128w>;
+// when d is not a multiple of 128 (d and f are multiples of 64)
+using Tiles128n = Tiles<128, Gemm<128, 64, 2, 2, 1, 64, 2, true>, Gemm<128, 64, 2, 2, 1, 64, 2, false>>;
 // large blocks (MFMA-bound shapes): 8 waves, two per SIMD, each with a 64x128
 // accumulator tile (gate/up: 64 x (64 gate + 64 up)); 256x256 down tiles.  K
 // steps of 64: every staged row is a 128-byte segment, which L2 feeds into LDS
@@ -857,7 +859,7 @@ hipError_t launch_paged(const FwdArgs &a, hipStream_t s)
     case 128:
         if (a.d % 256 == 0)
             return a.f % 256 == 0 ? launch_tiles<Tiles128w, PAGED>(a, s) : launch_tiles<Tiles128d, PAGED>(a, s);
-        return launch_tiles<Tiles128, PAGED>(a, s);
+        return a.d % 128 == 0 ? launch_tiles<Tiles128, PAGED>(a, s) : launch_tiles<Tiles128n, PAGED>(a, s);
     case 256:
         if (a.f % Tiles256::K1::BN_ == 0 && a.d % Tiles256::K2::BN_ == 0)
             return launch_tiles<Tiles256, PAGED>(a, s);

@@ -1,0 +1,111 @@
+"""Degenerate and extreme layers on the GPU, through the C ABI, against the
+oracle: one expert with k = 1, k = E, every token on one expert (one expert
+owning many blocks at every tile height), the smallest shapes (d = f = 64, and
+d not a multiple of 128), a ragged token count, a shared expert beside two
+routed ones, and the largest expert count (E + S = 1024).  Routing ids,
+aligned order and block map are compared bit for bit, y within the bar, and
+paged against contiguous weights bit for bit."""
+import dataclasses
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle
+import paged_expert_weight_amd as pm
+from workloads import synth
+
+from gpu_cases import Case, max_rel_err, y_f64
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-2
+BLOCK_MS = (16, 32, 64, 128, 256)
+
+
+def _spec(name, **kw):
+    return dataclasses.replace(synth.SPECS["tiny"], name=name, **kw)
+
+
+EDGE = {
+    "one_expert": _spec("one_expert", T=37, E=1, k=1, S=0, pool_pages=4, loadbuf_experts=(), loadbuf_slots=0,
+                        seed=4001),
+    "k_equals_E": _spec("k_equals_E", T=29, E=4, k=4, pool_pages=16, loadbuf_experts=(3,), loadbuf_slots=1,
+                        seed=4002),
+    "shared_beside_two": _spec("shared_beside_two", T=45, E=2, k=1, S=1, pool_pages=12, loadbuf_experts=(1,),
+                               loadbuf_slots=1, seed=4003),
+    "d64_f64": _spec("d64_f64", T=19, d=64, f=64, seed=4004),
+    "d192_ragged": _spec("d192_ragged", T=1000, d=192, f=192, E=16, k=3, pool_pages=64,
+                         loadbuf_experts=(13, 14, 15), loadbuf_slots=4, seed=4005),
+    "max_experts": _spec("max_experts", T=40, d=64, f=64, E=1023, k=8, S=1, pool_pages=3 * 1024 + 8,
+                         loadbuf_experts=tuple(range(1000, 1023)), loadbuf_slots=24, seed=4006),
+}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    pm.lib()
+
+
+def _check_layer(layer, block_ms=BLOCK_MS):
+    c = Case(layer)
+    s = c.s
+    ids, w = oracle.route(layer.logits, s.k, s.S)
+    ref = oracle.moe(layer.x, layer.w13, layer.w2, ids, w)
+    for bm in block_ms:
+        y, r = c.forward(bm)
+        yc, _ = c.contiguous(bm)
+        torch.cuda.synchronize()
+        assert np.array_equal(r.topk_ids.cpu().numpy(), ids), f"block_m {bm}: routing ids"
+        np.testing.assert_allclose(r.topk_w.cpu().numpy(), w, rtol=1e-6, atol=0)
+        s_ids, blk, npad = oracle.align(ids, s.E_tot, bm)
+        assert int(r.num_padded.item()) == npad
+        assert np.array_equal(r.sorted_ids[:npad].cpu().numpy(), s_ids), f"block_m {bm}: sorted order"
+        assert np.array_equal(r.block_expert[: npad // bm].cpu().numpy(), blk), f"block_m {bm}: block map"
+        got = y_f64(y)
+        assert np.all(np.isfinite(got)), f"block_m {bm}: non-finite output"
+        assert max_rel_err(got, ref) <= TOL, f"block_m {bm}: y off the oracle"
+        assert torch.equal(y, yc), f"block_m {bm}: paged and contiguous differ"
+    c.pool.close()
+
+
+@pytest.mark.parametrize("name", sorted(EDGE))
+def test_edge_layer_matches_oracle(name):
+    _check_layer(synth.make_layer(EDGE[name]))
+
+
+def test_every_token_on_one_expert():
+    """Expert 0 wins every token's first pick: it owns T rows, many blocks at
+    every tile height (and the 256-row launch's split last wave)."""
+    spec = _spec("one_hot_expert", T=700, E=8, k=2, pool_pages=32, seed=4007)
+    layer = synth.make_layer(spec)
+    # +8 puts expert 0 first for all 700 tokens (the other logits are N(0, 1))
+    # while the second picks' exp arguments stay near -10: an fp32 exp through
+    # 2^(x log2 e) loses about |x log2 e| half-ulps of relative accuracy, which
+    # at a gap of 50 would exceed the 1e-6 weight bar
+    layer.logits[:, 0] += 8.0
+    ids, _ = oracle.route(layer.logits, spec.k, spec.S)
+    assert np.all(ids[:, 0] == 0)
+    _check_layer(layer)
+
+
+@pytest.mark.parametrize("T", [1, 3])
+def test_edge_decode_steps(T):
+    """The decode forms on the degenerate layers (one expert, k = E, shared beside two)."""
+    for name in ("one_expert", "k_equals_E", "shared_beside_two", "max_experts"):
+        layer = synth.make_layer(EDGE[name], T)
+        c = Case(layer)
+        s = c.s
+        assert pm.moe_forward_form(c.pool, T) == pm.MOE_FORM_DECODE
+        ids, w = oracle.route(layer.logits, s.k, s.S)
+        ref = oracle.moe(layer.x, layer.w13, layer.w2, ids, w)
+        y1, _ = c.forward(16)
+        ws = pm.workspace(c.pool, T, 16)
+        y2, r2 = pm.route_forward(c.pool, c.dev.logits, c.dev.x, c.active, ws, 16)
+        torch.cuda.synchronize()
+        assert np.array_equal(r2.topk_ids.cpu().numpy(), ids), name
+        assert torch.equal(y1, y2), name
+        assert max_rel_err(y_f64(y1), ref) <= TOL, name
+        c.pool.close()
