@@ -94,6 +94,31 @@ def test_decode_step_512_experts_and_shared(T):
     c.pool.close()
 
 
+@pytest.mark.parametrize("T", [1, 2, 4])
+def test_decode_steps_reuse_one_workspace(T):
+    """Back-to-back one-call steps on one workspace that starts as 0xFF bytes,
+    with the routing changing from step to step: nothing left in the workspace
+    by the previous step (or garbage) may leak into the next one."""
+    c = Case(host_layer("decode", T))
+    bm = 16
+    assert pm.moe_route_forward_form(c.pool, T) == pm.MOE_FORM_DECODE_ROUTED
+    ws = torch.full((pm.moe_workspace_bytes(c.pool, T, bm, 0),), 255, dtype=torch.uint8, device="cuda")
+    steps = []
+    for rep in range(5):
+        logits = torch.roll(c.dev.logits, shifts=7 * rep, dims=1).contiguous()
+        y, _ = pm.route_forward(c.pool, logits, c.dev.x, c.active, ws, bm, 0,
+                                y=torch.full_like(c.dev.x, float("nan")))
+        steps.append((logits, y))
+    torch.cuda.synchronize()
+    for logits, y in steps:
+        ws2 = torch.zeros(pm.moe_workspace_bytes(c.pool, T, bm, 0), dtype=torch.uint8, device="cuda")
+        r2 = pm.route(c.pool, logits, bm, ws2)
+        y2 = pm.paged_forward(c.pool, c.dev.x, r2, c.active, ws2, 0)
+        torch.cuda.synchronize()
+        assert torch.equal(y, y2)
+    c.pool.close()
+
+
 @pytest.mark.parametrize("name,T", [("tiny", None), ("decode", 32)])
 def test_larger_batches_take_the_two_call_path(name, T):
     c = Case(host_layer(name, T))
