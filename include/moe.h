@@ -198,15 +198,17 @@ int moe_route(moe_pool *pool, const float *logits, int64_t T, int32_t block_m,
  *   y            device bf16 [T][d] out.
  *   workspace    device, >= moe_workspace_bytes(pool, T, block_m, flags) bytes;
  *                holds the SiLU-gated activations [sorted_cap][f] (bf16) and the
- *                combine buffer (bf16 weighted partial rows [T*(k+S)][d], or an
+ *                combine buffer (bf16 expert output rows [T*(k+S)][d], or an
  *                fp32 [T][d] accumulator with MOE_FLAG_ATOMIC_COMBINE).  Not kept
  *                between calls.
  *   flags        0, MOE_FLAG_ATOMIC_COMBINE, MOE_FLAG_DEFER_READ_DONE, or both.
  * Gate/up GEMM: each output tile resolves its W1 and W3 page bases once and
  * fuses silu(gate) * up into its epilogue; down GEMM: each tile resolves its
- * W2 page once and scales by the routing weight; each weighted partial row is
- * rounded to bf16, and the k+S rows of a token are added in fp32 in slot order
- * (bit-reproducible) before the sum is rounded to bf16.
+ * W2 page once; each expert output row is rounded to bf16, and the k+S rows of
+ * a token are scaled by their routing weights and added in fp32 in slot order
+ * (bit-reproducible) before the sum is rounded to bf16.  With
+ * MOE_FLAG_ATOMIC_COMBINE the down tiles add weighted fp32 rows into the
+ * accumulator instead (order not fixed).
  */
 int moe_paged_forward(moe_pool *pool, const void *x, int64_t T, int32_t block_m,
                       const int32_t *topk_ids, const float *topk_w, const int32_t *sorted_ids,

@@ -84,10 +84,12 @@ __device__ __forceinline__ const uint16_t *matrix_base(const FwdArgs &a, int e, 
 {
     const int64_t fd = (int64_t)a.f * a.d;
     if constexpr (PAGED) {
-        const DevLoc L = a.locs[e];
-        if (L.kind == 0)
-            return a.pool + (int64_t)L.idx[m] * fd;
-        return a.loadbuf + ((int64_t)L.idx[0] * 3 + m) * fd;
+        // the whole 16-byte entry in one load (the table is 16-byte aligned)
+        const int4 L = *(const int4 *)(a.locs + e); // kind, idx[0..2]
+        const bool in_pool = L.x == 0;               // selects: no field is loaded late
+        const int64_t o = in_pool ? (int64_t)(m == 0 ? L.y : m == 1 ? L.z : L.w) * fd
+                                  : ((int64_t)L.y * 3 + m) * fd;
+        return (in_pool ? a.pool : a.loadbuf) + o;
     } else {
         if (m < 2)
             return a.w13 + (int64_t)e * 2 * fd + m * fd;

@@ -51,7 +51,7 @@ struct FwdArgs {
     int64_t sorted_cap, blocks_cap;
     uint16_t *y;
     uint16_t *h;  // workspace [sorted_cap][f] bf16
-    void *comb;   // workspace: bf16 [T*keff][d] weighted partials (ordered) or fp32 [T][d] (atomic)
+    void *comb;   // workspace: bf16 [T*keff][d] expert output rows (ordered) or fp32 [T][d] (atomic)
     float *part;  // workspace: fp32 K-split partial tiles of the last partial wave (large tiles only)
     int64_t part_bytes;
     int slots[2]; // resident workgroups of the gate/up and down kernels when the last wave is split (0: never)

@@ -59,20 +59,31 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float v)
 }
 
 // Page bases of expert e: the per-tile resolver shared by the GEMMs and moe_resolve_addrs.
+// The whole 16-byte entry in one load (the table is 16-byte aligned), so that
+// the page bases follow one memory round trip after the expert is known.
+__device__ __forceinline__ int4 load_loc(const DevLoc *locs, int e)
+{
+    const int4 L = *(const int4 *)(locs + e);
+    // every field is needed here: the compiler would otherwise load the
+    // second index only after testing the kind, one more round trip
+    asm volatile("" ::"v"(L.x), "v"(L.y), "v"(L.z), "v"(L.w));
+    return L;
+}
+
 template <bool PAGED>
 __device__ __forceinline__ void gate_up_bases(const FwdArgs &a, int e, const uint16_t *&w1,
                                               const uint16_t *&w3)
 {
     const int64_t fd = (int64_t)a.f * a.d;
     if constexpr (PAGED) {
-        const DevLoc L = a.locs[e];
-        if (L.kind == 0) {
-            w1 = a.pool + L.idx[0] * fd;
-            w3 = a.pool + L.idx[1] * fd;
-        } else {
-            w1 = a.loadbuf + (int64_t)L.idx[0] * 3 * fd;
-            w3 = w1 + fd;
-        }
+        const int4 L = load_loc(a.locs, e); // kind, idx[0..2]
+        // selects, not branches: every field is used, so none is loaded late
+        const bool in_pool = L.x == 0;
+        const int64_t o1 = in_pool ? (int64_t)L.y * fd : (int64_t)L.y * 3 * fd;
+        const int64_t o3 = in_pool ? (int64_t)L.z * fd : o1 + fd;
+        const uint16_t *base = in_pool ? a.pool : a.loadbuf;
+        w1 = base + o1;
+        w3 = base + o3;
     } else {
         w1 = a.w13 + (int64_t)e * 2 * fd;
         w3 = w1 + fd;
@@ -84,8 +95,10 @@ __device__ __forceinline__ const uint16_t *down_base(const FwdArgs &a, int e)
 {
     const int64_t fd = (int64_t)a.f * a.d;
     if constexpr (PAGED) {
-        const DevLoc L = a.locs[e];
-        return L.kind == 0 ? a.pool + L.idx[2] * fd : a.loadbuf + ((int64_t)L.idx[0] * 3 + 2) * fd;
+        const int4 L = load_loc(a.locs, e);
+        const bool in_pool = L.x == 0;
+        const int64_t o2 = in_pool ? (int64_t)L.w * fd : ((int64_t)L.y * 3 + 2) * fd;
+        return (in_pool ? a.pool : a.loadbuf) + o2;
     } else {
         return a.w2 + (int64_t)e * fd;
     }
@@ -126,15 +139,89 @@ __device__ __forceinline__ void tile_at(const TileSpace &t, int ntiles, int u, i
     b = g * GM + r % gm;
 }
 
-// One tile per workgroup: workgroup i takes tile (i mod 8) * per_xcd + i / 8.
+// Expert-aligned groups: the blocks of one expert's segment are grouped GM at
+// a time from the segment's first block, so a group never spans two experts
+// (a group that did would stream two experts' weight tiles for the blocks of
+// one L2).  Groups still partition the blocks in order, so the group of tile u
+// is that of block u / ntiles: its segment is found with two 64-entry reads of
+// block_expert around that block (more only for segments longer than 64
+// blocks).  Used by the long tiles, where these reads are a negligible part
+// of a tile.
+__device__ __forceinline__ int expert_segment(const FwdArgs &a, int nblocks, int q, int &lo, int &hi)
+{
+    const int lane = threadIdx.x & 63;
+    // the expert of block q and the 64 blocks on either side, loaded together
+    const int il = q - 64 + lane, ih = q + 1 + lane;
+    const int e = a.block_expert[q];
+    const int vl = a.block_expert[il > 0 ? il : 0];
+    const int vh = a.block_expert[ih < nblocks ? ih : nblocks - 1];
+    uint64_t other = __ballot(il >= 0 && vl != e);
+    lo = 0;
+    for (int base = q - 64;; base -= 64) { // other: blocks base .. base+63 that are not e's
+        if (other) {
+            lo = base + (63 - __builtin_clzll(other)) + 1;
+            break;
+        }
+        if (base <= 0)
+            break;
+        const int i = base - 64 + lane;
+        other = __ballot(i >= 0 && a.block_expert[i] != e);
+    }
+    other = __ballot(ih < nblocks && vh != e);
+    hi = nblocks;
+    for (int base = q + 1;; base += 64) {
+        if (other) {
+            hi = base + __builtin_ctzll(other);
+            break;
+        }
+        if (base + 64 >= nblocks)
+            break;
+        const int i = base + 64 + lane;
+        other = __ballot(i < nblocks && a.block_expert[i] != e);
+    }
+    return e;
+}
+
+// Returns the expert of the tile's block (known from the segment search).
 template <int GM>
-__device__ __forceinline__ bool tile_of(const FwdArgs &a, int BM, int ntiles, int &b, int &nt)
+__device__ __forceinline__ int tile_at_aligned(const FwdArgs &a, const TileSpace &t, int ntiles, int u, int &b,
+                                               int &nt)
+{
+    const int q = u / ntiles;
+    int lo, hi;
+    const int e = expert_segment(a, t.blocks, q, lo, hi);
+    const int s = lo + (q - lo) / GM * GM;
+    const int m = min(GM, hi - s);
+    const int r = u - s * ntiles;
+    nt = r / m;
+    b = s + r % m;
+    return e;
+}
+
+// Tile u -> (block, column tile); returns the block's expert when the mapping
+// read it (ALIGNED), else kExpertUnknown.
+constexpr int kExpertUnknown = -2;
+
+template <int GM, bool ALIGNED>
+__device__ __forceinline__ int tile_pick(const FwdArgs &a, const TileSpace &t, int ntiles, int u, int &b, int &nt)
+{
+    if constexpr (ALIGNED) {
+        return tile_at_aligned<GM>(a, t, ntiles, u, b, nt);
+    } else {
+        tile_at<GM>(t, ntiles, u, b, nt);
+        return kExpertUnknown;
+    }
+}
+
+// One tile per workgroup: workgroup i takes tile (i mod 8) * per_xcd + i / 8.
+template <int GM, bool ALIGNED>
+__device__ __forceinline__ bool tile_of(const FwdArgs &a, int BM, int ntiles, int &b, int &nt, int &e)
 {
     const TileSpace t = tile_space(a, BM, ntiles);
     const int u = (int)(blockIdx.x % 8) * t.per_xcd + (int)(blockIdx.x / 8);
     if ((int)(blockIdx.x / 8) >= t.per_xcd || u >= t.total)
         return false;
-    tile_at<GM>(t, ntiles, u, b, nt);
+    e = tile_pick<GM, ALIGNED>(a, t, ntiles, u, b, nt);
     return true;
 }
 
@@ -335,7 +422,13 @@ struct Gemm {
         }
     }
 
-    // K-steps [kb, ke)
+    // K-steps [kb, ke): begin() issues the first S-1 stages, then the caller
+    // may issue loads of its own, then run() does the rest.
+    __device__ __forceinline__ void begin(int kb, int ke)
+    {
+        this->template prologue<0>(kb, ke);
+    }
+
     __device__ __forceinline__ void run(int kb, int ke)
     {
 #pragma unroll
@@ -345,7 +438,6 @@ struct Gemm {
                 acc0[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
                 acc1[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
             }
-        this->template prologue<0>(kb, ke);
         for (int kt0 = kb; kt0 < ke; kt0 += S)
             this->template steps<0>(kt0, ke);
         wait_vm_lgkm0(Int<0>{}); // no DMA may still be writing this workgroup's LDS when it exits
@@ -395,15 +487,28 @@ struct Gemm {
 };
 
 // One output tile (block b, column tile nt) of a grouped GEMM.
-template <class G, bool G1, bool PAGED, bool ATOMIC>
-__device__ __forceinline__ void gemm_tile(const FwdArgs &a, G &g, int b, int nt, int ks = 0, int nks = 1,
-                                          float *part = nullptr)
+template <class G, bool G1, bool PAGED, bool ATOMIC, bool E_KNOWN>
+__device__ __forceinline__ void gemm_tile(const FwdArgs &a, G &g, int b, int nt, int e_known, int ks = 0,
+                                          int nks = 1, float *part = nullptr)
 {
     constexpr int BM = G::BM_, BN = G::BN_, WK = G::WK_;
     constexpr int BK = G::Geo::ROWB / 2;
     using Geo = typename G::Geo;
+    // DMA instructions i < IA of a wave stage A rows, the others B rows
+    constexpr int IA = BM / Geo::ROWS_PER_LD / G::NT;
+    static_assert(IA * Geo::ROWS_PER_LD * G::NT == BM, "A rows split evenly over the waves");
     const int lane = threadIdx.x & 63;
-    const int e = block_owner(a, b);
+    const int lrow = lane / Geo::CH, lpos = lane % Geo::CH;
+    // The tile's first loads are issued together so that their latencies
+    // overlap: the flat picks of this wave's A rows (gate/up), the block's
+    // expert unless the tile mapping read it, then the page table entry.
+    int flat_a[G1 ? IA : 1];
+    if constexpr (G1) {
+#pragma unroll
+        for (int i = 0; i < IA; i++)
+            flat_a[i] = a.sorted_ids[b * BM + (g.wt + G::NT * i) * Geo::ROWS_PER_LD + lrow];
+    }
+    const int e = E_KNOWN ? (e_known >= 0 && e_known < a.E_tot ? e_known : -1) : block_owner(a, b);
     if (e < 0)
         return;
     const int d = a.d, f = a.f, K = G1 ? d : f;
@@ -423,16 +528,15 @@ __device__ __forceinline__ void gemm_tile(const FwdArgs &a, G &g, int b, int nt,
     }
 
     // per-lane source offset of each DMA instruction this wave issues
-    const int lrow = lane / Geo::CH, lpos = lane % Geo::CH;
 #pragma unroll
     for (int i = 0; i < G::IPW; i++) {
         const int q = g.wt + G::NT * i;                // instruction index within the stage
         const int row = q * Geo::ROWS_PER_LD + lrow;  // row within the stage
         const int chunk = lpos ^ Geo::swz(row);
         uint32_t off;
-        if (row < BM) {
+        if (i < IA) {
             if constexpr (G1) {
-                const int flat = a.sorted_ids[b * BM + row];
+                const int flat = flat_a[i];
                 off = (flat >= 0 && flat < nflat) ? (uint32_t)(flat / a.keff) * (uint32_t)d * 2u : kOOB;
             } else {
                 off = (uint32_t)(b * BM + row) * (uint32_t)f * 2u;
@@ -444,13 +548,14 @@ __device__ __forceinline__ void gemm_tile(const FwdArgs &a, G &g, int b, int nt,
         g.voff[i] = off + chunk * 16u;
     }
 
-    // G2: the flat pick and routing weight of every output row this lane
-    // stores.  Small wave tiles fetch them before the K loop so their latency
-    // overlaps it; large ones (whose accumulators fill the register file, and
-    // whose K loop is long) fetch them after it.
+    // G2: the flat pick (and, for the atomic combine, the routing weight) of
+    // every output row this lane stores.  Small wave tiles fetch the picks
+    // before the first stages are issued, so their latency overlaps the K
+    // loop; large ones (whose accumulators fill the register file, and whose
+    // K loop is long) fetch them after it.
     int eflat[G::FM][4];
     float ewt[G::FM][4];
-    auto epilogue_rows = [&]() {
+    auto epilogue_picks = [&]() {
 #pragma unroll
         for (int i = 0; i < G::FM; i++)
 #pragma unroll
@@ -459,6 +564,8 @@ __device__ __forceinline__ void gemm_tile(const FwdArgs &a, G &g, int b, int nt,
                 const int flat = a.sorted_ids[b * BM + row];
                 eflat[i][r] = (flat >= 0 && flat < nflat) ? flat : -1;
             }
+    };
+    auto epilogue_weights = [&]() {
 #pragma unroll
         for (int i = 0; i < G::FM; i++)
 #pragma unroll
@@ -466,14 +573,19 @@ __device__ __forceinline__ void gemm_tile(const FwdArgs &a, G &g, int b, int nt,
                 ewt[i][r] = eflat[i][r] >= 0 ? a.topk_w[eflat[i][r]] : 0.f;
     };
     constexpr bool kPrefetchRows = !G1 && G::FM <= 4;
+    // the picks are read before the first stages are issued (nothing waits
+    // for them until the epilogue); the ordered combine applies the routing
+    // weights itself, the atomic one reads them after the K loop
     if constexpr (kPrefetchRows)
-        epilogue_rows();
+        epilogue_picks();
 
     // K-steps [kb, ke): range ks of nks (the whole contraction unless the tile
     // is split), divided again over the WK waves of a split-K tile
     const int KT = K / BK;
     const int kb = ks * KT / nks, ke = (ks + 1) * KT / nks;
-    g.run(kb + g.kg * (ke - kb) / WK, kb + (g.kg + 1) * (ke - kb) / WK);
+    const int wkb = kb + g.kg * (ke - kb) / WK, wke = kb + (g.kg + 1) * (ke - kb) / WK;
+    g.begin(wkb, wke);
+    g.run(wkb, wke);
     if (!g.reduce_k())
         return;
     const int lg = g.lg, l16 = g.l16;
@@ -495,7 +607,9 @@ __device__ __forceinline__ void gemm_tile(const FwdArgs &a, G &g, int b, int nt,
         return;
     }
     if constexpr (!G1 && !kPrefetchRows)
-        epilogue_rows();
+        epilogue_picks();
+    if constexpr (!G1 && ATOMIC)
+        epilogue_weights();
 
     if constexpr (G1) {
         uint16_t *hb = a.h + (int64_t)b * BM * f + n0;
@@ -518,15 +632,14 @@ __device__ __forceinline__ void gemm_tile(const FwdArgs &a, G &g, int b, int nt,
                 const int flat = eflat[i][r];
                 if (flat < 0)
                     continue;
-                const float wt = ewt[i][r];
 #pragma unroll
                 for (int j = 0; j < G::FN; j++) {
                     const int col = n0 + g.wn * G::WN + j * 16 + l16;
-                    const float v = g.acc0[i][j][r] * wt;
                     if constexpr (ATOMIC)
-                        unsafeAtomicAdd(&((float *)a.comb)[(int64_t)(flat / a.keff) * d + col], v);
+                        unsafeAtomicAdd(&((float *)a.comb)[(int64_t)(flat / a.keff) * d + col],
+                                        g.acc0[i][j][r] * ewt[i][r]);
                     else
-                        ((uint16_t *)a.comb)[(int64_t)flat * d + col] = f32_to_bf16(v);
+                        ((uint16_t *)a.comb)[(int64_t)flat * d + col] = f32_to_bf16(g.acc0[i][j][r]);
                 }
             }
     }
@@ -558,21 +671,21 @@ __global__ __launch_bounds__(64 * G::NW) void k_gemm(const FwdArgs a)
         if (tp.tail > 0) {
             const int i = (int)blockIdx.x;
             if (i < tp.full) { // whole tiles, dealt to the XCDs as in tile_of (full is a multiple of 8)
-                tile_at<GM>(ts, ntiles, (i & 7) * (tp.full >> 3) + (i >> 3), b, nt);
-                gemm_tile<G, G1, PAGED, ATOMIC>(a, g, b, nt);
+                const int e = tile_pick<GM, TAIL>(a, ts, ntiles, (i & 7) * (tp.full >> 3) + (i >> 3), b, nt);
+                gemm_tile<G, G1, PAGED, ATOMIC, TAIL>(a, g, b, nt, e);
             } else if (i - tp.full < tp.tail * tp.ks) {
                 const int v = i - tp.full;
-                tile_at<GM>(ts, ntiles, tp.full + v / tp.ks, b, nt);
+                const int e = tile_pick<GM, TAIL>(a, ts, ntiles, tp.full + v / tp.ks, b, nt);
                 constexpr int BNE = G1 ? 2 * BN : BN;
-                gemm_tile<G, G1, PAGED, ATOMIC>(a, g, b, nt, v % tp.ks, tp.ks,
-                                                                                a.part + (int64_t)v * BM * BNE);
+                gemm_tile<G, G1, PAGED, ATOMIC, TAIL>(a, g, b, nt, e, v % tp.ks, tp.ks, a.part + (int64_t)v * BM * BNE);
             }
             return;
         }
     }
-    if (!tile_of<GM>(a, BM, ntiles, b, nt))
+    int e;
+    if (!tile_of<GM, TAIL>(a, BM, ntiles, b, nt, e))
         return;
-    gemm_tile<G, G1, PAGED, ATOMIC>(a, g, b, nt);
+    gemm_tile<G, G1, PAGED, ATOMIC, TAIL>(a, g, b, nt, e);
 #endif
 }
 
@@ -593,7 +706,7 @@ __global__ __launch_bounds__(256) void k_tail_fixup(const FwdArgs a)
     if (t >= tp.tail)
         return;
     int b, nt;
-    tile_at<GM>(ts, ntiles, tp.full + t, b, nt);
+    tile_pick<GM, true>(a, ts, ntiles, tp.full + t, b, nt); // the split tiles' (256-row) order
     if (block_owner(a, b) < 0)
         return;
     constexpr int BNE = G1 ? 2 * BN : BN;
@@ -620,28 +733,30 @@ __global__ __launch_bounds__(256) void k_tail_fixup(const FwdArgs a)
         const int flat = a.sorted_ids[b * BM + row];
         if (flat < 0 || flat >= a.T * a.keff)
             return;
-        const float w = a.topk_w[flat];
         if constexpr (ATOMIC) {
+            const float w = a.topk_w[flat];
             float *y32 = (float *)a.comb + (int64_t)(flat / a.keff) * a.d + n0 + col;
             unsafeAtomicAdd(y32 + 0, s0.x * w);
             unsafeAtomicAdd(y32 + 1, s0.y * w);
             unsafeAtomicAdd(y32 + 2, s0.z * w);
             unsafeAtomicAdd(y32 + 3, s0.w * w);
         } else {
-            o.x = (uint32_t)f32_to_bf16(s0.x * w) | ((uint32_t)f32_to_bf16(s0.y * w) << 16);
-            o.y = (uint32_t)f32_to_bf16(s0.z * w) | ((uint32_t)f32_to_bf16(s0.w * w) << 16);
+            o.x = (uint32_t)f32_to_bf16(s0.x) | ((uint32_t)f32_to_bf16(s0.y) << 16);
+            o.y = (uint32_t)f32_to_bf16(s0.z) | ((uint32_t)f32_to_bf16(s0.w) << 16);
             *(uint2 *)&((uint16_t *)a.comb)[(int64_t)flat * a.d + n0 + col] = o;
         }
     }
 }
 
 // ---------------------------------------------------------------------------- combine / convert
-// Ordered: y[t][c] = bf16( sum_{j < keff} part[t*keff + j][c] ), the weighted
-// bf16 partial rows added in fp32 in slot order.  Atomic: y = bf16(y32).
+// Ordered: y[t][c] = bf16( sum_{j < keff} w[t][j] * part[t*keff + j][c] ), the
+// bf16 expert output rows weighted and added in fp32 in slot order.  Atomic:
+// y = bf16(y32).
 // Four columns per thread.
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 
-__global__ __launch_bounds__(256) void k_combine(const uint16_t *part, int64_t T, int d, int keff, uint16_t *y)
+__global__ __launch_bounds__(256) void k_combine(const uint16_t *part, const float *w, int64_t T, int d, int keff,
+                                                 uint16_t *y)
 {
     const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const int q = d / 4;
@@ -652,15 +767,19 @@ __global__ __launch_bounds__(256) void k_combine(const uint16_t *part, int64_t T
     float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
     for (int j0 = 0; j0 < keff; j0 += 4) {
         uint2 v[4];
+        float wj[4];
 #pragma unroll
-        for (int r = 0; r < 4; r++)
-            v[r] = j0 + r < keff ? *(const uint2 *)&part[(t * keff + j0 + r) * d + c] : make_uint2(0u, 0u);
+        for (int r = 0; r < 4; r++) {
+            const bool in = j0 + r < keff;
+            v[r] = in ? *(const uint2 *)&part[(t * keff + j0 + r) * d + c] : make_uint2(0u, 0u);
+            wj[r] = in ? w[t * keff + j0 + r] : 0.f;
+        }
 #pragma unroll
         for (int r = 0; r < 4; r++) { // slot order; a missing slot adds +0
-            s0 += bf16_to_f32(v[r].x & 0xffffu);
-            s1 += bf16_to_f32(v[r].x >> 16);
-            s2 += bf16_to_f32(v[r].y & 0xffffu);
-            s3 += bf16_to_f32(v[r].y >> 16);
+            s0 += wj[r] * bf16_to_f32(v[r].x & 0xffffu);
+            s1 += wj[r] * bf16_to_f32(v[r].x >> 16);
+            s2 += wj[r] * bf16_to_f32(v[r].y & 0xffffu);
+            s3 += wj[r] * bf16_to_f32(v[r].y >> 16);
         }
     }
     uint2 o;
@@ -752,6 +871,7 @@ using Tiles256 = Tiles<256, Gemm<256, 128, 4, 2, 1, 64, 2, true>, Gemm<256, 256,
 using Tiles256n = Tiles<256, Gemm<256, 64, 4, 2, 1, 32, 4, true>, Gemm<256, 64, 4, 1, 1, 32, 4, false>>;
 
 constexpr int kGroupM = 4;
+constexpr int kGroupMLong = 8; // 256-row tiles (expert-aligned groups)
 
 // Workgroups of a kernel that fit on the current device at once (a multiple of
 // 8), or 0 if the runtime cannot tell.  Cached per kernel and device.
@@ -802,8 +922,9 @@ hipError_t launch_tiles_t(const FwdArgs &a_in, hipStream_t s)
     if (a.f % BN1 || a.d % BN2)
         return hipErrorInvalidValue;
     constexpr int T1 = 64 * G1T::NW, T2 = 64 * G2T::NW;
-    auto k1 = k_gemm<G1T, kGroupM, true, PAGED, false, TAIL>;
-    auto k2 = k_gemm<G2T, kGroupM, false, PAGED, ATOMIC, TAIL>;
+    constexpr int GM = TAIL ? kGroupMLong : kGroupM;
+    auto k1 = k_gemm<G1T, GM, true, PAGED, false, TAIL>;
+    auto k2 = k_gemm<G2T, GM, false, PAGED, ATOMIC, TAIL>;
     a.slots[0] = a.slots[1] = 0;
     if constexpr (TAIL) {
         const int p1 = resident_slots((const void *)k1, T1), p2 = resident_slots((const void *)k2, T2);
@@ -825,20 +946,21 @@ hipError_t launch_tiles_t(const FwdArgs &a_in, hipStream_t s)
     k1<<<grid(a.f / BN1, a.slots[0]), T1, 0, s>>>(a);
     if constexpr (TAIL)
         if (a.slots[0])
-            k_tail_fixup<BM, BN1, kGroupM, true, false>
+            k_tail_fixup<BM, BN1, GM, true, false>
                 <<<(unsigned)(a.slots[0] / 2 * fixup_chunks(BM, BN1)), 256, 0, s>>>(a);
     mark(1);
     k2<<<grid(a.d / BN2, a.slots[1]), T2, 0, s>>>(a);
     if constexpr (TAIL)
         if (a.slots[1])
-            k_tail_fixup<BM, BN2, kGroupM, false, ATOMIC>
+            k_tail_fixup<BM, BN2, GM, false, ATOMIC>
                 <<<(unsigned)(a.slots[1] / 2 * fixup_chunks(BM, BN2)), 256, 0, s>>>(a);
     mark(2);
     const int64_t nq = a.T * a.d / 4;
     if (ATOMIC)
         k_convert<<<(unsigned)((nq + 255) / 256), 256, 0, s>>>((const float *)a.comb, a.T, a.d, a.y);
     else
-        k_combine<<<(unsigned)((nq + 255) / 256), 256, 0, s>>>((const uint16_t *)a.comb, a.T, a.d, a.keff, a.y);
+        k_combine<<<(unsigned)((nq + 255) / 256), 256, 0, s>>>((const uint16_t *)a.comb, a.topk_w, a.T, a.d, a.keff,
+                                                               a.y);
     mark(3);
     return hipGetLastError();
 }
