@@ -29,6 +29,7 @@
 #include "internal.h"
 
 #include <mutex>
+#include <type_traits>
 
 namespace pmoe {
 namespace {
@@ -182,10 +183,16 @@ __device__ __forceinline__ int expert_segment(const FwdArgs &a, int nblocks, int
     return e;
 }
 
-// Returns the expert of the tile's block (known from the segment search).
+// What the tile mapping learnt about a tile's block: its expert (or
+// kExpertUnknown) and whether that expert has no other block (-1: unknown).
+constexpr int kExpertUnknown = -2;
+struct BlockInfo {
+    int e, single;
+};
+
 template <int GM>
-__device__ __forceinline__ int tile_at_aligned(const FwdArgs &a, const TileSpace &t, int ntiles, int u, int &b,
-                                               int &nt)
+__device__ __forceinline__ BlockInfo tile_at_aligned(const FwdArgs &a, const TileSpace &t, int ntiles, int u,
+                                                     int &b, int &nt)
 {
     const int q = u / ntiles;
     int lo, hi;
@@ -195,33 +202,33 @@ __device__ __forceinline__ int tile_at_aligned(const FwdArgs &a, const TileSpace
     const int r = u - s * ntiles;
     nt = r / m;
     b = s + r % m;
-    return e;
+    return BlockInfo{e, hi - lo == 1 ? 1 : 0};
 }
 
-// Tile u -> (block, column tile); returns the block's expert when the mapping
-// read it (ALIGNED), else kExpertUnknown.
-constexpr int kExpertUnknown = -2;
-
+// Tile u -> (block, column tile), and what the mapping learnt of the block.
 template <int GM, bool ALIGNED>
-__device__ __forceinline__ int tile_pick(const FwdArgs &a, const TileSpace &t, int ntiles, int u, int &b, int &nt)
+__device__ __forceinline__ BlockInfo tile_pick(const FwdArgs &a, const TileSpace &t, int ntiles, int u, int &b,
+                                               int &nt)
 {
     if constexpr (ALIGNED) {
         return tile_at_aligned<GM>(a, t, ntiles, u, b, nt);
     } else {
         tile_at<GM>(t, ntiles, u, b, nt);
-        return kExpertUnknown;
+        return BlockInfo{kExpertUnknown, -1};
     }
 }
 
 // One tile per workgroup: workgroup i takes tile (i mod 8) * per_xcd + i / 8.
 template <int GM, bool ALIGNED>
-__device__ __forceinline__ bool tile_of(const FwdArgs &a, int BM, int ntiles, int &b, int &nt, int &e)
+__device__ __forceinline__ bool tile_of(const FwdArgs &a, int BM, int ntiles, int &b, int &nt, BlockInfo &bi,
+                                        int &nblocks)
 {
     const TileSpace t = tile_space(a, BM, ntiles);
+    nblocks = t.blocks;
     const int u = (int)(blockIdx.x % 8) * t.per_xcd + (int)(blockIdx.x / 8);
     if ((int)(blockIdx.x / 8) >= t.per_xcd || u >= t.total)
         return false;
-    e = tile_pick<GM, ALIGNED>(a, t, ntiles, u, b, nt);
+    bi = tile_pick<GM, ALIGNED>(a, t, ntiles, u, b, nt);
     return true;
 }
 
@@ -274,6 +281,15 @@ struct StageGeom {
     static constexpr int ROWS_PER_LD = 64 / CH;  // rows one DMA instruction covers
     __device__ static __forceinline__ int swz(int r) { return CH >= 8 ? (r & 7) : ((r >> 1) & 3); }
 };
+
+// Cache policy of the stage DMA (the instruction's aux bits).  A streaming
+// read of HBM into LDS measured 7.2 TB/s with non-temporal loads against
+// 5.7 TB/s with plain ones, but a non-temporal line is the first to leave L2:
+// weight tiles go non-temporal only when no other tile reads them (the
+// expert has one block); x and h rows, which other column tiles re-read,
+// never do.
+constexpr int kDmaPlain = 0;
+constexpr int kDmaStream = 2;
 
 template <int N>
 struct Int {
@@ -333,8 +349,8 @@ struct Gemm {
     }
 
     // DMA of K-step kt into stage J: instruction i of this wave reads section
-    // 0 (A), 1 (B gate / W2) or 2 (B up).
-    template <int J>
+    // 0 (A), 1 (B gate / W2) or 2 (B up); STREAM: the B rows non-temporally.
+    template <int J, bool STREAM>
     __device__ __forceinline__ void issue(int kt)
     {
         uint8_t *slot = stage<J>();
@@ -345,11 +361,11 @@ struct Gemm {
             const int row0 = q * Geo::ROWS_PER_LD;
             auto *dst = (__attribute__((address_space(3))) void *)(slot + q * 1024);
             if (row0 < BM)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, dst, 16, voff[i], soff, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, dst, 16, voff[i], soff, 0, kDmaPlain);
             else if (!G1 || row0 - BM < BN)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rb0, dst, 16, voff[i], soff, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rb0, dst, 16, voff[i], soff, 0, STREAM ? kDmaStream : kDmaPlain);
             else
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rb1, dst, 16, voff[i], soff, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rb1, dst, 16, voff[i], soff, 0, STREAM ? kDmaStream : kDmaPlain);
         }
     }
 
@@ -386,18 +402,18 @@ struct Gemm {
         }
     }
 
-    template <int J>
+    template <int J, bool STREAM>
     __device__ __forceinline__ void prologue(int kb, int ke)
     {
         if constexpr (J < S - 1) {
             if (kb + J < ke)
-                this->template issue<J>(kb + J);
-            this->template prologue<J + 1>(kb, ke);
+                this->template issue<J, STREAM>(kb + J);
+            this->template prologue<J + 1, STREAM>(kb, ke);
         }
     }
 
     // one pass over the S stages: K-steps kt0 .. kt0+S-1 (of the range ending at ke)
-    template <int J>
+    template <int J, bool STREAM>
     __device__ __forceinline__ void steps(int kt0, int ke)
     {
         if constexpr (J < S) {
@@ -415,20 +431,22 @@ struct Gemm {
                 __builtin_amdgcn_s_barrier();
             constexpr int NEXT = (J + S - 1) % S;
             if (kt + S - 1 < ke)
-                this->template issue<NEXT>(kt + S - 1);
+                this->template issue<NEXT, STREAM>(kt + S - 1);
             if (kt < ke)
                 this->template compute<J>();
-            this->template steps<J + 1>(kt0, ke);
+            this->template steps<J + 1, STREAM>(kt0, ke);
         }
     }
 
     // K-steps [kb, ke): begin() issues the first S-1 stages, then the caller
     // may issue loads of its own, then run() does the rest.
+    template <bool STREAM>
     __device__ __forceinline__ void begin(int kb, int ke)
     {
-        this->template prologue<0>(kb, ke);
+        this->template prologue<0, STREAM>(kb, ke);
     }
 
+    template <bool STREAM>
     __device__ __forceinline__ void run(int kb, int ke)
     {
 #pragma unroll
@@ -439,7 +457,7 @@ struct Gemm {
                 acc1[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
             }
         for (int kt0 = kb; kt0 < ke; kt0 += S)
-            this->template steps<0>(kt0, ke);
+            this->template steps<0, STREAM>(kt0, ke);
         wait_vm_lgkm0(Int<0>{}); // no DMA may still be writing this workgroup's LDS when it exits
     }
 
@@ -488,8 +506,8 @@ struct Gemm {
 
 // One output tile (block b, column tile nt) of a grouped GEMM.
 template <class G, bool G1, bool PAGED, bool ATOMIC, bool E_KNOWN>
-__device__ __forceinline__ void gemm_tile(const FwdArgs &a, G &g, int b, int nt, int e_known, int ks = 0,
-                                          int nks = 1, float *part = nullptr)
+__device__ __forceinline__ void gemm_tile(const FwdArgs &a, G &g, int b, int nt, BlockInfo bi, int nblocks,
+                                          int ks = 0, int nks = 1, float *part = nullptr)
 {
     constexpr int BM = G::BM_, BN = G::BN_, WK = G::WK_;
     constexpr int BK = G::Geo::ROWB / 2;
@@ -508,7 +526,16 @@ __device__ __forceinline__ void gemm_tile(const FwdArgs &a, G &g, int b, int nt,
         for (int i = 0; i < IA; i++)
             flat_a[i] = a.sorted_ids[b * BM + (g.wt + G::NT * i) * Geo::ROWS_PER_LD + lrow];
     }
-    const int e = E_KNOWN ? (e_known >= 0 && e_known < a.E_tot ? e_known : -1) : block_owner(a, b);
+    int e, single;
+    if constexpr (E_KNOWN) {
+        e = bi.e >= 0 && bi.e < a.E_tot ? bi.e : -1;
+        single = bi.single;
+    } else { // the block's expert and its neighbours' (read together)
+        e = block_owner(a, b);
+        const int ep = b > 0 ? a.block_expert[b - 1] : -1;
+        const int en = b + 1 < nblocks ? a.block_expert[b + 1] : -1;
+        single = ep != e && en != e;
+    }
     if (e < 0)
         return;
     const int d = a.d, f = a.f, K = G1 ? d : f;
@@ -584,8 +611,17 @@ __device__ __forceinline__ void gemm_tile(const FwdArgs &a, G &g, int b, int nt,
     const int KT = K / BK;
     const int kb = ks * KT / nks, ke = (ks + 1) * KT / nks;
     const int wkb = kb + g.kg * (ke - kb) / WK, wke = kb + (g.kg + 1) * (ke - kb) / WK;
-    g.begin(wkb, wke);
-    g.run(wkb, wke);
+    // the weight rows go non-temporal when the expert has no other block
+    // (one copy of the K loop per policy, chosen once per tile)
+    auto pipeline = [&](auto stream) {
+        constexpr bool ST = decltype(stream)::value;
+        g.template begin<ST>(wkb, wke);
+        g.template run<ST>(wkb, wke);
+    };
+    if (single)
+        pipeline(std::true_type{});
+    else
+        pipeline(std::false_type{});
     if (!g.reduce_k())
         return;
     const int lg = g.lg, l16 = g.l16;
@@ -671,21 +707,23 @@ __global__ __launch_bounds__(64 * G::NW) void k_gemm(const FwdArgs a)
         if (tp.tail > 0) {
             const int i = (int)blockIdx.x;
             if (i < tp.full) { // whole tiles, dealt to the XCDs as in tile_of (full is a multiple of 8)
-                const int e = tile_pick<GM, TAIL>(a, ts, ntiles, (i & 7) * (tp.full >> 3) + (i >> 3), b, nt);
-                gemm_tile<G, G1, PAGED, ATOMIC, TAIL>(a, g, b, nt, e);
+                const BlockInfo bi = tile_pick<GM, TAIL>(a, ts, ntiles, (i & 7) * (tp.full >> 3) + (i >> 3), b, nt);
+                gemm_tile<G, G1, PAGED, ATOMIC, TAIL>(a, g, b, nt, bi, ts.blocks);
             } else if (i - tp.full < tp.tail * tp.ks) {
                 const int v = i - tp.full;
-                const int e = tile_pick<GM, TAIL>(a, ts, ntiles, tp.full + v / tp.ks, b, nt);
+                const BlockInfo bi = tile_pick<GM, TAIL>(a, ts, ntiles, tp.full + v / tp.ks, b, nt);
                 constexpr int BNE = G1 ? 2 * BN : BN;
-                gemm_tile<G, G1, PAGED, ATOMIC, TAIL>(a, g, b, nt, e, v % tp.ks, tp.ks, a.part + (int64_t)v * BM * BNE);
+                gemm_tile<G, G1, PAGED, ATOMIC, TAIL>(a, g, b, nt, bi, ts.blocks, v % tp.ks, tp.ks,
+                                                      a.part + (int64_t)v * BM * BNE);
             }
             return;
         }
     }
-    int e;
-    if (!tile_of<GM, TAIL>(a, BM, ntiles, b, nt, e))
+    BlockInfo bi;
+    int nblocks;
+    if (!tile_of<GM, TAIL>(a, BM, ntiles, b, nt, bi, nblocks))
         return;
-    gemm_tile<G, G1, PAGED, ATOMIC, TAIL>(a, g, b, nt, e);
+    gemm_tile<G, G1, PAGED, ATOMIC, TAIL>(a, g, b, nt, bi, nblocks);
 #endif
 }
 
