@@ -674,8 +674,9 @@ __device__ __forceinline__ void gemm_tile(const FwdArgs &a, G &g, int b, int nt,
                     if constexpr (ATOMIC)
                         unsafeAtomicAdd(&((float *)a.comb)[(int64_t)(flat / a.keff) * d + col],
                                         g.acc0[i][j][r] * ewt[i][r]);
-                    else
-                        ((uint16_t *)a.comb)[(int64_t)flat * d + col] = f32_to_bf16(g.acc0[i][j][r]);
+                    else // written once, read once by the combine: non-temporal
+                        __builtin_nontemporal_store(f32_to_bf16(g.acc0[i][j][r]),
+                                                    &((uint16_t *)a.comb)[(int64_t)flat * d + col]);
                 }
             }
     }
@@ -809,7 +810,13 @@ __global__ __launch_bounds__(256) void k_combine(const uint16_t *part, const flo
 #pragma unroll
         for (int r = 0; r < 4; r++) {
             const bool in = j0 + r < keff;
-            v[r] = in ? *(const uint2 *)&part[(t * keff + j0 + r) * d + c] : make_uint2(0u, 0u);
+            if (in) { // each expert output row is read once: non-temporal
+                typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+                const u32x2 pv = __builtin_nontemporal_load((const u32x2 *)&part[(t * keff + j0 + r) * d + c]);
+                v[r] = make_uint2(pv.x, pv.y);
+            } else {
+                v[r] = make_uint2(0u, 0u);
+            }
             wj[r] = in ? w[t * keff + j0 + r] : 0.f;
         }
 #pragma unroll
