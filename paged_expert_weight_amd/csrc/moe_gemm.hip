@@ -897,6 +897,10 @@ struct Tiles {
 using Tiles16 = Tiles<16, Gemm<16, 16, 1, 1, 4, 64, 3, true>, Gemm<16, 32, 1, 1, 2, 64, 4, false>>;
 using Tiles32 = Tiles<32, Gemm<32, 32, 1, 2, 1, 64, 2, true>, Gemm<32, 32, 1, 2, 1, 64, 2, false>>;
 using Tiles64 = Tiles<64, Gemm<64, 64, 2, 2, 1, 64, 2, true>, Gemm<64, 64, 2, 2, 1, 64, 2, false>>;
+// when d is a multiple of 256: 256-column down tiles, 8 waves of 32x64 (a
+// block's h rows are re-read by 4x fewer column tiles; 63 against 77 us for the
+// down GEMM of a 512-token Qwen1.5-shaped layer)
+using Tiles64w = Tiles<64, Gemm<64, 64, 2, 2, 1, 64, 2, true>, Gemm<64, 256, 2, 4, 1, 64, 2, false>>;
 using Tiles128 = Tiles<128, Gemm<128, 64, 2, 2, 1, 64, 2, true>, Gemm<128, 128, 2, 2, 1, 64, 2, false>>;
 // 128-row blocks of layers with many small experts (a block's x or h rows are
 // re-read once per column tile): 256-column tiles, 8 waves of 64x64
@@ -1022,7 +1026,7 @@ hipError_t launch_paged(const FwdArgs &a, hipStream_t s)
     switch (a.BM) {
     case 16: return launch_tiles<Tiles16, PAGED>(a, s);
     case 32: return launch_tiles<Tiles32, PAGED>(a, s);
-    case 64: return launch_tiles<Tiles64, PAGED>(a, s);
+    case 64: return a.d % 256 == 0 ? launch_tiles<Tiles64w, PAGED>(a, s) : launch_tiles<Tiles64, PAGED>(a, s);
     case 128:
         if (a.d % 256 == 0)
             return a.f % 256 == 0 ? launch_tiles<Tiles128w, PAGED>(a, s) : launch_tiles<Tiles128d, PAGED>(a, s);
