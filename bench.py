@@ -34,10 +34,10 @@ HBM_PEAK_GBS = 8000.0
 # 1 GiB copy reads back, plus WRITE_SIZE), keyed by workload, T, block_m, atomic combine and a
 # hash of the GEMM sources the counters were taken on.  Reported only while that hash matches.
 MEASURED_TRAFFIC = {
-    ("qwen15", 1024, 128, False, "4e969b57c6d92005"): 750133099,
-    ("qwen3n", 8192, 128, False, "4e969b57c6d92005"): 2842344005,
-    ("decode", 1, 16, False, "4e969b57c6d92005"): 46304693,
-    ("mixtral", 4096, 256, False, "4e969b57c6d92005"): 4076791110,
+    ("qwen15", 1024, 128, False, "fdb2ca354ab3970d"): 734954234,
+    ("qwen3n", 8192, 128, False, "fdb2ca354ab3970d"): 2880516130,
+    ("decode", 1, 16, False, "fdb2ca354ab3970d"): 46304749,
+    ("mixtral", 4096, 256, False, "fdb2ca354ab3970d"): 4082357855,
 }
 GEMM_SOURCES = ("paged_expert_weight_amd/csrc/moe_gemm.hip", "paged_expert_weight_amd/csrc/decode.hip",
                 "paged_expert_weight_amd/csrc/internal.h")
