@@ -91,6 +91,22 @@ def test_every_token_on_one_expert():
     _check_layer(layer)
 
 
+def test_expert_segment_longer_than_64_blocks():
+    """256-row tiles group an expert's blocks from its first block, found by
+    reading the block map 64 entries at a time around a tile's block: with
+    every token's first pick on expert 0 (40000 rows, 157 blocks) the search
+    must walk several windows in both directions for the blocks in the middle
+    of that segment.  d = 256 and f = 128 select the 256 x 256 tiles; the 314
+    tiles of each GEMM are one full wave and a split last wave on 256 CUs."""
+    spec = _spec("long_segment", T=40000, d=256, f=128, E=4, k=2, pool_pages=16, loadbuf_experts=(3,),
+                 loadbuf_slots=1, seed=4008)
+    layer = synth.make_layer(spec)
+    layer.logits[:, 0] += 8.0  # see test_every_token_on_one_expert for the size of the bias
+    ids, _ = oracle.route(layer.logits, spec.k, spec.S)
+    assert np.all(ids[:, 0] == 0)
+    _check_layer(layer, block_ms=(256,))
+
+
 @pytest.mark.parametrize("T", [1, 3])
 def test_edge_decode_steps(T):
     """The decode forms on the degenerate layers (one expert, k = E, shared beside two)."""
