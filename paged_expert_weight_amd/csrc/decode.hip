@@ -29,8 +29,13 @@ namespace pmoe {
 namespace {
 
 constexpr int kDecWaves = 4;
+// Granularity: intermediate rows per gate/up wave and output columns per down
+// workgroup.  Batches of 2+ tokens run 2 rows / 4 columns; a one-token step runs
+// 1 row / 2 columns (twice the workgroups, each with half the loads: 17.1
+// against 17.8 us per Qwen1.5-shaped step; at 4 tokens it is 4 % slower).
 constexpr int kDecRowsPerWave = 2;  // gate/up: intermediate rows per wave
 constexpr int kDecColsPerGroup = 4; // down: output columns per workgroup
+constexpr int kDecRowsPerWave1 = 1, kDecColsPerGroup1 = 2; // T = 1
 constexpr int kDecMaxT = 8;         // tokens (hence valid rows of one expert block)
 constexpr int kDecMaxD = 4096;
 constexpr int kDecMaxKeff = 64;   // picks per token (top-k plus the shared expert)
@@ -111,15 +116,15 @@ __device__ __forceinline__ const uint16_t *matrix_base(const FwdArgs &a, int e, 
 // weight rows first, finds the valid picks with a ballot while those loads are
 // in flight, then reads each pick's x row (shared by all waves, so mostly from
 // L2) and writes that pick's h values.
-template <bool PAGED, int NCH, class PickFn>
+template <bool PAGED, int NCH, int RPW, class PickFn>
 __device__ __forceinline__ void dec_gate_up_rows(const FwdArgs &a, int e, int ncand, PickFn pick)
 {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int r0 = ((int)blockIdx.x * kDecWaves + wave) * kDecRowsPerWave;
+    const int r0 = ((int)blockIdx.x * kDecWaves + wave) * RPW;
     const uint16_t *w1 = matrix_base<PAGED>(a, e, 0), *w3 = matrix_base<PAGED>(a, e, 1);
-    uint4 g[kDecRowsPerWave][NCH], u[kDecRowsPerWave][NCH];
+    uint4 g[RPW][NCH], u[RPW][NCH];
 #pragma unroll
-    for (int r = 0; r < kDecRowsPerWave; r++)
+    for (int r = 0; r < RPW; r++)
 #pragma unroll
         for (int c = 0; c < NCH; c++) {
             const int o = c * 512 + lane * 8;
@@ -139,22 +144,22 @@ __device__ __forceinline__ void dec_gate_up_rows(const FwdArgs &a, int e, int nc
             m &= m - 1;
             const int flat = __shfl(cand, bit, 64);
             const int64_t t = flat / a.keff;
-            float sg[kDecRowsPerWave], su[kDecRowsPerWave];
+            float sg[RPW], su[RPW];
 #pragma unroll
-            for (int r = 0; r < kDecRowsPerWave; r++)
+            for (int r = 0; r < RPW; r++)
                 sg[r] = su[r] = 0.f;
 #pragma unroll
             for (int c = 0; c < NCH; c++) {
                 const int o = c * 512 + lane * 8;
                 const uint4 xv = o < a.d ? *(const uint4 *)&a.x[t * a.d + o] : make_uint4(0, 0, 0, 0);
 #pragma unroll
-                for (int r = 0; r < kDecRowsPerWave; r++) {
+                for (int r = 0; r < RPW; r++) {
                     sg[r] = dot8(g[r][c], xv, sg[r]);
                     su[r] = dot8(u[r][c], xv, su[r]);
                 }
             }
 #pragma unroll
-            for (int r = 0; r < kDecRowsPerWave; r++) {
+            for (int r = 0; r < RPW; r++) {
                 const float gs = wave_sum(sg[r]), us = wave_sum(su[r]);
                 if (lane == r)
                     a.h[(int64_t)flat * a.f + r0 + r] = f32_to_bf16_rne(gs / (1.f + __expf(-gs)) * us);
@@ -163,9 +168,9 @@ __device__ __forceinline__ void dec_gate_up_rows(const FwdArgs &a, int e, int nc
     }
 }
 
-// grid: (f / (kDecWaves * kDecRowsPerWave), expert blocks): the picks of block
-// b are its BM entries of sorted_ids.
-template <bool PAGED, int NCH>
+// grid: (f / (kDecWaves * RPW), expert blocks): the picks of block b are its BM
+// entries of sorted_ids.
+template <bool PAGED, int NCH, int RPW>
 __global__ __launch_bounds__(64 * kDecWaves) void k_dec_gate_up(const FwdArgs a)
 {
     const int b = (int)blockIdx.y;
@@ -177,7 +182,7 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_dec_gate_up(const FwdArgs a)
         return;
     const int64_t nflat = a.T * a.keff;
     const int32_t *sid = a.sorted_ids + (int64_t)b * a.BM;
-    dec_gate_up_rows<PAGED, NCH>(a, e, a.BM, [&](int i) {
+    dec_gate_up_rows<PAGED, NCH, RPW>(a, e, a.BM, [&](int i) {
         const int flat = sid[i];
         return (flat >= 0 && flat < nflat) ? flat : -1;
     });
@@ -191,7 +196,7 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_dec_gate_up(const FwdArgs a)
 // expert fills one block.  Workgroup (0, 0) also writes the routing outputs
 // (topk ids and weights, which the down pass reads, and the aligned order, the
 // block map and num_padded, as the routing kernels would).
-template <bool PAGED, int NCH, int NV>
+template <bool PAGED, int NCH, int NV, int RPW>
 __global__ __launch_bounds__(64 * kDecWaves) void k_dec_route_gate_up(const FwdArgs a, const DecRouteArgs ra)
 {
     constexpr int kWords = kMaxExpertsTotal / 32;
@@ -257,7 +262,7 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_dec_route_gate_up(const FwdA
     __syncthreads();
     const int e = __builtin_amdgcn_readfirstlane(s_e); // uniform: the table entry and bases load as scalars
     if (e >= 0)
-        dec_gate_up_rows<PAGED, NCH>(a, e, n, [&](int i) { return s_ids[i] == e ? i : -1; });
+        dec_gate_up_rows<PAGED, NCH, RPW>(a, e, n, [&](int i) { return s_ids[i] == e ? i : -1; });
     if (blockIdx.x != 0 || blockIdx.y != 0)
         return;
     // the routing outputs, as the routing kernels write them
@@ -290,29 +295,29 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_dec_route_gate_up(const FwdA
     }
 }
 
-// grid: (d / kDecColsPerGroup, T).  Wave w takes the token's picks w, w + 4,
+// grid: (d / CPG, T).  Wave w takes the token's picks w, w + 4,
 // ...: it issues the four W2 rows of its pick, reads the pick's h row (from
 // L2), and leaves w_tj * dot per column in LDS; after the one barrier the sums
 // over the picks are taken in slot order.
-template <bool PAGED, int NCH>
+template <bool PAGED, int NCH, int CPG>
 __global__ __launch_bounds__(64 * kDecWaves) void k_dec_down(const FwdArgs a)
 {
-    __shared__ float res[kDecMaxKeff * kDecColsPerGroup];
+    __shared__ float res[kDecMaxKeff * CPG];
     const int t = (int)blockIdx.y;
-    const int c0 = (int)blockIdx.x * kDecColsPerGroup;
+    const int c0 = (int)blockIdx.x * CPG;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     for (int j = wave; j < a.keff; j += kDecWaves) {
         const int e = a.topk_ids[(int64_t)t * a.keff + j];
         const float w = a.topk_w[(int64_t)t * a.keff + j];
-        float s[kDecColsPerGroup];
+        float s[CPG];
 #pragma unroll
-        for (int c = 0; c < kDecColsPerGroup; c++)
+        for (int c = 0; c < CPG; c++)
             s[c] = 0.f;
         if (e >= 0 && e < a.E_tot) {
             const uint16_t *w2 = matrix_base<PAGED>(a, e, 2);
-            uint4 wv[kDecColsPerGroup][NCH];
+            uint4 wv[CPG][NCH];
 #pragma unroll
-            for (int c = 0; c < kDecColsPerGroup; c++)
+            for (int c = 0; c < CPG; c++)
 #pragma unroll
                 for (int k = 0; k < NCH; k++) {
                     const int o = k * 512 + lane * 8;
@@ -324,43 +329,43 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_dec_down(const FwdArgs a)
                 const int o = k * 512 + lane * 8;
                 const uint4 hv = o < a.f ? *(const uint4 *)&hrow[o] : make_uint4(0, 0, 0, 0);
 #pragma unroll
-                for (int c = 0; c < kDecColsPerGroup; c++)
+                for (int c = 0; c < CPG; c++)
                     s[c] = dot8(wv[c][k], hv, s[c]);
             }
         }
 #pragma unroll
-        for (int c = 0; c < kDecColsPerGroup; c++) {
+        for (int c = 0; c < CPG; c++) {
             const float v = wave_sum(s[c]);
             if (lane == c)
-                res[j * kDecColsPerGroup + c] = w * v;
+                res[j * CPG + c] = w * v;
         }
     }
     __syncthreads();
-    if (tid < kDecColsPerGroup) {
+    if (tid < CPG) {
         float acc = 0.f;
         for (int j = 0; j < a.keff; j++)
-            acc += res[j * kDecColsPerGroup + tid];
+            acc += res[j * CPG + tid];
         a.y[(int64_t)t * a.d + c0 + tid] = f32_to_bf16_rne(acc);
     }
 }
 
-template <int NCH_D>
+template <int NCH_D, int RPW>
 struct RoutedGateUp {
     template <bool PAGED, int NV>
     static void go(const FwdArgs &a, const DecRouteArgs &r, dim3 g, hipStream_t s)
     {
-        k_dec_route_gate_up<PAGED, NCH_D, NV><<<g, 64 * kDecWaves, 0, s>>>(a, r);
+        k_dec_route_gate_up<PAGED, NCH_D, NV, RPW><<<g, 64 * kDecWaves, 0, s>>>(a, r);
     }
 };
 
-template <bool PAGED, int NCH_D>
+template <bool PAGED, int NCH_D, int RPW>
 void launch_gate_up(const FwdArgs &a, const DecRouteArgs *ra, dim3 g1, hipStream_t s)
 {
     if (!ra) {
-        k_dec_gate_up<PAGED, NCH_D><<<g1, 64 * kDecWaves, 0, s>>>(a);
+        k_dec_gate_up<PAGED, NCH_D, RPW><<<g1, 64 * kDecWaves, 0, s>>>(a);
         return;
     }
-    using R = RoutedGateUp<NCH_D>;
+    using R = RoutedGateUp<NCH_D, RPW>;
     if (ra->E <= 64)
         R::template go<PAGED, 1>(a, *ra, g1, s);
     else if (ra->E <= 128)
@@ -373,8 +378,8 @@ void launch_gate_up(const FwdArgs &a, const DecRouteArgs *ra, dim3 g1, hipStream
         R::template go<PAGED, 16>(a, *ra, g1, s);
 }
 
-template <bool PAGED, int NCH_D, int NCH_F>
-hipError_t launch_t(const FwdArgs &a, const DecRouteArgs *ra, hipStream_t s)
+template <bool PAGED, int NCH_D, int NCH_F, int RPW, int CPG>
+hipError_t launch_g(const FwdArgs &a, const DecRouteArgs *ra, hipStream_t s)
 {
     auto mark = [&](int i) {
         if (a.ev[i])
@@ -387,14 +392,22 @@ hipError_t launch_t(const FwdArgs &a, const DecRouteArgs *ra, hipStream_t s)
     const int64_t n = a.T * a.keff;
     int64_t rows = n / a.BM + (n < a.E_tot ? n : a.E_tot);
     rows = rows < a.blocks_cap ? rows : a.blocks_cap;
-    const dim3 g1((unsigned)(a.f / (kDecWaves * kDecRowsPerWave)), (unsigned)rows);
-    launch_gate_up<PAGED, NCH_D>(a, ra, g1, s);
+    const dim3 g1((unsigned)(a.f / (kDecWaves * RPW)), (unsigned)rows);
+    launch_gate_up<PAGED, NCH_D, RPW>(a, ra, g1, s);
     mark(1);
-    const dim3 g2((unsigned)(a.d / kDecColsPerGroup), (unsigned)a.T);
-    k_dec_down<PAGED, NCH_F><<<g2, 64 * kDecWaves, 0, s>>>(a);
+    const dim3 g2((unsigned)(a.d / CPG), (unsigned)a.T);
+    k_dec_down<PAGED, NCH_F, CPG><<<g2, 64 * kDecWaves, 0, s>>>(a);
     mark(2);
     mark(3);
     return hipGetLastError();
+}
+
+template <bool PAGED, int NCH_D, int NCH_F>
+hipError_t launch_t(const FwdArgs &a, const DecRouteArgs *ra, hipStream_t s)
+{
+    if (a.T == 1)
+        return launch_g<PAGED, NCH_D, NCH_F, kDecRowsPerWave1, kDecColsPerGroup1>(a, ra, s);
+    return launch_g<PAGED, NCH_D, NCH_F, kDecRowsPerWave, kDecColsPerGroup>(a, ra, s);
 }
 
 template <bool PAGED, int NCH_D>
