@@ -518,14 +518,13 @@ __device__ __forceinline__ void gemm_tile(const FwdArgs &a, G &g, int b, int nt,
     const int lane = threadIdx.x & 63;
     const int lrow = lane / Geo::CH, lpos = lane % Geo::CH;
     // The tile's first loads are issued together so that their latencies
-    // overlap: the flat picks of this wave's A rows (gate/up), the block's
-    // expert unless the tile mapping read it, then the page table entry.
-    int flat_a[G1 ? IA : 1];
-    if constexpr (G1) {
+    // overlap: the flat picks of this wave's A rows, the block's expert unless
+    // the tile mapping read it, then the page table entry.  A padding row (no
+    // pick) is staged from an out-of-range offset: zeros, no memory traffic.
+    int flat_a[IA];
 #pragma unroll
-        for (int i = 0; i < IA; i++)
-            flat_a[i] = a.sorted_ids[b * BM + (g.wt + G::NT * i) * Geo::ROWS_PER_LD + lrow];
-    }
+    for (int i = 0; i < IA; i++)
+        flat_a[i] = a.sorted_ids[b * BM + (g.wt + G::NT * i) * Geo::ROWS_PER_LD + lrow];
     int e, single;
     if constexpr (E_KNOWN) {
         e = bi.e >= 0 && bi.e < a.E_tot ? bi.e : -1;
@@ -562,12 +561,12 @@ __device__ __forceinline__ void gemm_tile(const FwdArgs &a, G &g, int b, int nt,
         const int chunk = lpos ^ Geo::swz(row);
         uint32_t off;
         if (i < IA) {
-            if constexpr (G1) {
-                const int flat = flat_a[i];
-                off = (flat >= 0 && flat < nflat) ? (uint32_t)(flat / a.keff) * (uint32_t)d * 2u : kOOB;
-            } else {
-                off = (uint32_t)(b * BM + row) * (uint32_t)f * 2u;
-            }
+            const int flat = flat_a[i];
+            const bool pick = flat >= 0 && flat < nflat;
+            if constexpr (G1) // the token's x row
+                off = pick ? (uint32_t)(flat / a.keff) * (uint32_t)d * 2u : kOOB;
+            else // the block's h row
+                off = pick ? (uint32_t)(b * BM + row) * (uint32_t)f * 2u : kOOB;
         } else {
             const int br = (row - BM) % BN;
             off = (uint32_t)(n0 + br) * (uint32_t)K * 2u;
