@@ -574,8 +574,8 @@ __device__ __forceinline__ void gemm_tile(const FwdArgs &a, G &g, int b, int nt,
         g.voff[i] = off + chunk * 16u;
     }
 
-    // G2: the flat pick (and, for the atomic combine, the routing weight) of
-    // every output row this lane stores.  Small wave tiles fetch the picks
+    // The flat pick of every output row this lane stores (and, for the atomic
+    // combine, its routing weight).  Small wave tiles fetch the picks
     // before the first stages are issued, so their latency overlaps the K
     // loop; large ones (whose accumulators fill the register file, and whose
     // K loop is long) fetch them after it.
@@ -598,7 +598,7 @@ __device__ __forceinline__ void gemm_tile(const FwdArgs &a, G &g, int b, int nt,
             for (int r = 0; r < 4; r++)
                 ewt[i][r] = eflat[i][r] >= 0 ? a.topk_w[eflat[i][r]] : 0.f;
     };
-    constexpr bool kPrefetchRows = !G1 && G::FM <= 4;
+    constexpr bool kPrefetchRows = G::FM <= 4;
     // the picks are read before the first stages are issued (nothing waits
     // for them until the epilogue); the ordered combine applies the routing
     // weights itself, the atomic one reads them after the K loop
@@ -641,24 +641,27 @@ __device__ __forceinline__ void gemm_tile(const FwdArgs &a, G &g, int b, int nt,
                 }
         return;
     }
-    if constexpr (!G1 && !kPrefetchRows)
+    if constexpr (!kPrefetchRows)
         epilogue_picks();
     if constexpr (!G1 && ATOMIC)
         epilogue_weights();
 
-    if constexpr (G1) {
+    if constexpr (G1) { // rows without a pick (padding) are not stored: the down GEMM never reads them
         uint16_t *hb = a.h + (int64_t)b * BM * f + n0;
 #pragma unroll
         for (int i = 0; i < G::FM; i++)
 #pragma unroll
-            for (int j = 0; j < G::FN; j++)
+            for (int r = 0; r < 4; r++) {
+                if (eflat[i][r] < 0)
+                    continue;
+                const int row = g.wm * G::WM + i * 16 + 4 * lg + r;
 #pragma unroll
-                for (int r = 0; r < 4; r++) {
-                    const int row = g.wm * G::WM + i * 16 + 4 * lg + r;
+                for (int j = 0; j < G::FN; j++) {
                     const int col = g.wn * G::WN + j * 16 + l16;
                     const float gt = g.acc0[i][j][r], up = g.acc1[i][j][r];
                     hb[(int64_t)row * f + col] = f32_to_bf16(gt / (1.f + __expf(-gt)) * up);
                 }
+            }
     } else {
 #pragma unroll
         for (int i = 0; i < G::FM; i++)
