@@ -793,46 +793,48 @@ __global__ __launch_bounds__(256) void k_tail_fixup(const FwdArgs a)
 // Ordered: y[t][c] = bf16( sum_{j < keff} w[t][j] * part[t*keff + j][c] ), the
 // bf16 expert output rows weighted and added in fp32 in slot order.  Atomic:
 // y = bf16(y32).
-// Four columns per thread.
+// Eight columns per thread (combine), four (convert).
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 
 __global__ __launch_bounds__(256) void k_combine(const uint16_t *part, const float *w, int64_t T, int d, int keff,
                                                  uint16_t *y)
 {
     const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int q = d / 4;
+    const int q = d / 8;
     if (idx >= T * q)
         return;
     const int64_t t = idx / q;
-    const int c = (int)(idx % q) * 4;
-    float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+    const int c = (int)(idx % q) * 8;
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    float acc[8];
+#pragma unroll
+    for (int k = 0; k < 8; k++)
+        acc[k] = 0.f;
     for (int j0 = 0; j0 < keff; j0 += 4) {
-        uint2 v[4];
+        u32x4 v[4];
         float wj[4];
 #pragma unroll
         for (int r = 0; r < 4; r++) {
             const bool in = j0 + r < keff;
-            if (in) { // each expert output row is read once: non-temporal
-                typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-                const u32x2 pv = __builtin_nontemporal_load((const u32x2 *)&part[(t * keff + j0 + r) * d + c]);
-                v[r] = make_uint2(pv.x, pv.y);
-            } else {
-                v[r] = make_uint2(0u, 0u);
-            }
+            // each expert output row is read once: non-temporal
+            v[r] = in ? __builtin_nontemporal_load((const u32x4 *)&part[(t * keff + j0 + r) * d + c])
+                      : u32x4{0u, 0u, 0u, 0u};
             wj[r] = in ? w[t * keff + j0 + r] : 0.f;
         }
 #pragma unroll
-        for (int r = 0; r < 4; r++) { // slot order; a missing slot adds +0
-            s0 += wj[r] * bf16_to_f32(v[r].x & 0xffffu);
-            s1 += wj[r] * bf16_to_f32(v[r].x >> 16);
-            s2 += wj[r] * bf16_to_f32(v[r].y & 0xffffu);
-            s3 += wj[r] * bf16_to_f32(v[r].y >> 16);
-        }
+        for (int r = 0; r < 4; r++) // slot order; a missing slot adds +0
+#pragma unroll
+            for (int k = 0; k < 4; k++) {
+                acc[2 * k] += wj[r] * bf16_to_f32(v[r][k] & 0xffffu);
+                acc[2 * k + 1] += wj[r] * bf16_to_f32(v[r][k] >> 16);
+            }
     }
-    uint2 o;
-    o.x = (uint32_t)f32_to_bf16(s0) | ((uint32_t)f32_to_bf16(s1) << 16);
-    o.y = (uint32_t)f32_to_bf16(s2) | ((uint32_t)f32_to_bf16(s3) << 16);
-    *(uint2 *)&y[t * d + c] = o;
+    uint4 o;
+    o.x = (uint32_t)f32_to_bf16(acc[0]) | ((uint32_t)f32_to_bf16(acc[1]) << 16);
+    o.y = (uint32_t)f32_to_bf16(acc[2]) | ((uint32_t)f32_to_bf16(acc[3]) << 16);
+    o.z = (uint32_t)f32_to_bf16(acc[4]) | ((uint32_t)f32_to_bf16(acc[5]) << 16);
+    o.w = (uint32_t)f32_to_bf16(acc[6]) | ((uint32_t)f32_to_bf16(acc[7]) << 16);
+    *(uint4 *)&y[t * d + c] = o;
 }
 
 __global__ __launch_bounds__(256) void k_convert(const float *y32, int64_t T, int d, uint16_t *y)
@@ -1010,7 +1012,7 @@ hipError_t launch_tiles_t(const FwdArgs &a_in, hipStream_t s)
     if (ATOMIC)
         k_convert<<<(unsigned)((nq + 255) / 256), 256, 0, s>>>((const float *)a.comb, a.T, a.d, a.y);
     else
-        k_combine<<<(unsigned)((nq + 255) / 256), 256, 0, s>>>((const uint16_t *)a.comb, a.topk_w, a.T, a.d, a.keff,
+        k_combine<<<(unsigned)((nq / 2 + 255) / 256), 256, 0, s>>>((const uint16_t *)a.comb, a.topk_w, a.T, a.d, a.keff,
                                                                a.y);
     mark(3);
     return hipGetLastError();
