@@ -923,7 +923,7 @@ using Tiles256 = Tiles<256, Gemm<256, 128, 4, 2, 1, 64, 2, true>, Gemm<256, 256,
 // when f or d is not a multiple of 128 / 256
 using Tiles256n = Tiles<256, Gemm<256, 64, 4, 2, 1, 32, 4, true>, Gemm<256, 64, 4, 1, 1, 32, 4, false>>;
 
-constexpr int kGroupM = 4;
+constexpr int kGroupM = 2;
 constexpr int kGroupMLong = 8; // 256-row tiles (expert-aligned groups)
 
 // Workgroups of a kernel that fit on the current device at once (a multiple of
