@@ -923,7 +923,12 @@ using Tiles256 = Tiles<256, Gemm<256, 128, 4, 2, 1, 64, 2, true>, Gemm<256, 256,
 // when f or d is not a multiple of 128 / 256
 using Tiles256n = Tiles<256, Gemm<256, 64, 4, 2, 1, 32, 4, true>, Gemm<256, 64, 4, 1, 1, 32, 4, false>>;
 
-constexpr int kGroupM = 2;
+// Blocks per group.  Up to 128-row blocks, one: a block's column tiles run
+// together, reading its x (or h) rows from L2 (these layers have few blocks
+// per expert, so weight tiles are rarely shared; against groups of 4, a
+// 1024-token Qwen1.5-shaped step took 223.8 against 231.6 us).  256-row tiles
+// of experts with many blocks: up to 8, starting at each expert's first block.
+constexpr int kGroupM = 1;
 constexpr int kGroupMLong = 8; // 256-row tiles (expert-aligned groups)
 
 // Workgroups of a kernel that fit on the current device at once (a multiple of
