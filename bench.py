@@ -353,7 +353,9 @@ def main():
         "contig_ms_per_step": round(contig_ms, 5) if contig_ms else None,
         "overhead_vs_contiguous_pct": round((paged_alt_ms / contig_ms - 1) * 100, 3) if contig_ms else None,
         "stages_us": {"route_align": round(route_us, 2), "gate_up": round(stage_us[0], 2),
-                      "down": round(stage_us[1], 2), "combine": round(stage_us[2], 2)},
+                      "down": round(stage_us[1], 2),
+                      # the decode form combines inside its down launch: no stage of its own
+                      "combine": None if decode_form else round(stage_us[2], 2)},
         "step_us_spread": spread,
         "roofline": roof,
         "loadbuf": loadbuf,
