@@ -114,22 +114,16 @@ __device__ __forceinline__ uint64_t lanes_below()
     return lane == 0 ? 0ull : (~0ull >> (64 - lane));
 }
 
-// Per-wave histogram of the chunk s_ids[0..n): s_cnt[w*E_tot + e] (must start at zero).
+// Per-wave histogram of the chunk s_ids[0..n): s_cnt[w*E_tot + e] (must start
+// at zero).  Counts do not depend on order, so each entry is one LDS atomic add
+// (the id matching of the scatter costs a ballot per id bit).
 __device__ void chunk_hist(const int32_t *s_ids, int n, int E_tot, int *s_cnt)
 {
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int nbits = id_bits(E_tot);
-    const uint64_t below = lanes_below();
     int lo, hi;
     wave_range(n, w, lo, hi);
-    for (int g = lo; g < hi; g += 64) {
-        const int i = g + lane;
-        const bool valid = i < hi;
-        const int e = valid ? s_ids[i] : 0;
-        const uint64_t m = same_id_lanes(e, valid, nbits);
-        if (valid && (m & below) == 0)
-            s_cnt[w * E_tot + e] += __popcll(m);
-    }
+    for (int i = lo + lane; i < hi; i += 64)
+        atomicAdd(&s_cnt[w * E_tot + s_ids[i]], 1);
 }
 
 // In-order scatter of the chunk s_ids[0..n) whose first flat index is elem0.
