@@ -7,8 +7,8 @@
 // first entry equals it (DPP and lane-swap steps, no LDS), so all lanes agree
 // on the winner, whose lane then moves on to its next entry.  Lane j keeps pick
 // j; the weights are the softmax of the k picks renormalised over them,
-// exp(l_j - l_0) / sum_i exp(l_i - l_0), in fp32.  A shared expert (id E,
-// weight 1) is appended as pick k.
+// exp(l_j - l_0) / sum_i exp(l_i - l_0), computed in fp64 and stored as fp32.
+// A shared expert (id E, weight 1) is appended as pick k.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -30,11 +30,6 @@ __device__ __forceinline__ int dpp(int v)
 {
     return __builtin_amdgcn_update_dpp(v, v, CTRL, 0xF, 0xF, false);
 }
-template <int CTRL>
-__device__ __forceinline__ float dpp(float v)
-{
-    return __builtin_bit_cast(float, dpp<CTRL>(__builtin_bit_cast(int, v)));
-}
 constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
 
 __device__ __forceinline__ int xor16(int v, int lane)
@@ -47,16 +42,28 @@ __device__ __forceinline__ int xor32(int v, int lane)
     const auto r = __builtin_amdgcn_permlane32_swap((unsigned)v, (unsigned)v, false, false);
     return (int)(lane >= 32 ? r[0] : r[1]);
 }
-__device__ __forceinline__ float xor16(float v, int lane)
+// Wave-wide fp64 sum, each exchange on the two 32-bit halves.
+template <int CTRL>
+__device__ __forceinline__ double dpp(double v)
 {
-    return __builtin_bit_cast(float, xor16(__builtin_bit_cast(int, v), lane));
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const int lo = dpp<CTRL>((int)(uint32_t)u), hi = dpp<CTRL>((int)(uint32_t)(u >> 32));
+    return __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
 }
-__device__ __forceinline__ float xor32(float v, int lane)
+__device__ __forceinline__ double xor16(double v, int lane)
 {
-    return __builtin_bit_cast(float, xor32(__builtin_bit_cast(int, v), lane));
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const int lo = xor16((int)(uint32_t)u, lane), hi = xor16((int)(uint32_t)(u >> 32), lane);
+    return __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+__device__ __forceinline__ double xor32(double v, int lane)
+{
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const int lo = xor32((int)(uint32_t)u, lane), hi = xor32((int)(uint32_t)(u >> 32), lane);
+    return __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
 }
 
-__device__ __forceinline__ float wave_sum(float x, int lane)
+__device__ __forceinline__ double wave_sum(double x, int lane)
 {
     x += dpp<kDppXor1>(x);
     x += dpp<kDppXor2>(x);
@@ -191,13 +198,17 @@ __device__ void route_token(const float (&v)[NV], int E, int k, int S, int lane,
         sk[NV - 1] ^= (sk[NV - 1] ^ kEmpty) & msk;
         si[NV - 1] ^= (si[NV - 1] ^ kNone) & msk;
     }
+    // The weights in fp64, rounded once to fp32: the difference of two fp32
+    // logits is exact in fp64, so exp of it keeps its relative accuracy at any
+    // logit gap (in fp32 the rounding of l_j - l_0 alone is |l_j - l_0| * 2^-24
+    // relative after exp, 3e-6 at a gap of 50).
     const float my_v = key_value(my_k);
     const float lmax = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, my_v)));
-    const float ex = lane < k ? expf(my_v - lmax) : 0.f;
-    const float sum = wave_sum(ex, lane); // commutative pairs: every lane ends with the same sum
+    const double ex = lane < k ? exp((double)my_v - (double)lmax) : 0.0;
+    const double sum = wave_sum(ex, lane); // commutative pairs: every lane ends with the same sum
     if (lane < k) {
         ids[lane] = my_id;
-        w[lane] = ex / sum;
+        w[lane] = (float)(ex / sum);
         if (lds_ids)
             lds_ids[lane] = my_id;
     }

@@ -81,11 +81,10 @@ def test_every_token_on_one_expert():
     every tile height (and the 256-row launch's split last wave)."""
     spec = _spec("one_hot_expert", T=700, E=8, k=2, pool_pages=32, seed=4007)
     layer = synth.make_layer(spec)
-    # +8 puts expert 0 first for all 700 tokens (the other logits are N(0, 1))
-    # while the second picks' exp arguments stay near -10: an fp32 exp through
-    # 2^(x log2 e) loses about |x log2 e| half-ulps of relative accuracy, which
-    # at a gap of 50 would exceed the 1e-6 weight bar
-    layer.logits[:, 0] += 8.0
+    # +50 puts expert 0 first for all 700 tokens (the other logits are N(0, 1)),
+    # so every second pick's weight is about exp(-50): the routing weights must
+    # keep the 1e-6 relative bar at that gap
+    layer.logits[:, 0] += 50.0
     ids, _ = oracle.route(layer.logits, spec.k, spec.S)
     assert np.all(ids[:, 0] == 0)
     _check_layer(layer)
@@ -101,7 +100,7 @@ def test_expert_segment_longer_than_64_blocks():
     spec = _spec("long_segment", T=40000, d=256, f=128, E=4, k=2, pool_pages=16, loadbuf_experts=(3,),
                  loadbuf_slots=1, seed=4008)
     layer = synth.make_layer(spec)
-    layer.logits[:, 0] += 8.0  # see test_every_token_on_one_expert for the size of the bias
+    layer.logits[:, 0] += 50.0  # second picks at weights near exp(-50), as in test_every_token_on_one_expert
     ids, _ = oracle.route(layer.logits, spec.k, spec.S)
     assert np.all(ids[:, 0] == 0)
     _check_layer(layer, block_ms=(256,))
