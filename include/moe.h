@@ -116,7 +116,12 @@ typedef struct {
 } moe_expert_loc;
 
 /*
- * Create a layer handle.  Validates desc (MOE_ERR_INVALID_ARG /
+ * Create a layer handle.  Defined by the Rimuru digest, "One pool for data
+ * whose sizes differ by orders of magnitude" (one contiguous pool in which an
+ * expert matrix fills one page) and "Expert weights are scattered across
+ * pages. How does the kernel read them?" (the kernel is told where each expert
+ * sits: a page number when it is cached, a slot of one of the two alternating
+ * loading buffers when it was just copied in).  Validates desc (MOE_ERR_INVALID_ARG /
  * MOE_ERR_UNSUPPORTED / MOE_ERR_ALIGN), then allocates the handle's own small
  * state on the current device: the device copy of the location table
  * (E + S entries), a pinned staging copy, and four hipEvents (filled and
@@ -164,6 +169,12 @@ int moe_workspace_bytes(const moe_pool *pool, int64_t T, int32_t block_m, uint32
 
 /*
  * Routing and token alignment, all on the device, no host synchronisation.
+ * The digest's "The pipeline: what happens in one scheduling round" (step 5)
+ * has the actual routing choose the experts a layer computes; it prints no
+ * routing rule, so this is top-k softmax routing renormalised over the picks,
+ * and the alignment is the grouping of picks by expert into GEMM-tile blocks
+ * of the fused MoE kernel that "Expert weights are scattered across pages. How
+ * does the kernel read them?" says the paged kernel is rewritten from.
  *   logits       device fp32 [T][E] router logits (finite values).
  *   topk_ids     device int32 [T][k+S] out: per token the k experts with the
  *                largest logits, largest first, equal logits to the lower id;
@@ -185,6 +196,13 @@ int moe_route(moe_pool *pool, const float *logits, int64_t T, int32_t block_m,
 
 /*
  * The layer output from the routing above, reading the weights in place.
+ * Defined by the digest's "Expert weights are scattered across pages. How does
+ * the kernel read them?": the weight of output column n, offset t of expert e
+ * is at addr_e(n,t) = B_P + p_e(n)*f*d + (n mod f)*d + t, W1 (gate) for the
+ * first half of the fused columns and W3 (up) for the second, W2 (down) as the
+ * expert's third page ("The adjuster: when to evict an expert, and which
+ * one?"); the page is found once per output tile, then read with fixed
+ * strides; an expert just copied in is read from its load-buffer slot.
  *   x            device bf16 [T][d] hidden states.
  *   topk_ids ... num_padded: as produced by moe_route with the same block_m.
  *   active_buf   0 or 1: the load buffer the MOE_LOC_LOADBUF experts are read
@@ -245,7 +263,9 @@ int moe_route_contiguous_forward(const moe_pool *pool, const void *w13, const vo
 
 /*
  * The same layer with the weights in two dense arrays (the contiguous
- * baseline the paged kernel is measured against; same kernels and tile
+ * baseline the paged kernel is measured against, as in the last paragraph of
+ * the digest's "Expert weights are scattered across pages. How does the
+ * kernel read them?": the same inputs and routing through both kernels; same kernels and tile
  * schedule, only the per-tile base address differs, so results are
  * bit-identical to moe_paged_forward for the same weights).
  *   w13  device bf16 [E+S][2f][d]: rows [0,f) W1, rows [f,2f) W3 of each expert.
@@ -276,7 +296,11 @@ int moe_loadbuf_fill(moe_pool *pool, int32_t buf, int32_t n, const int32_t *slot
 
 /*
  * Resolve weight addresses on the device with the same per-tile resolver the
- * GEMM kernels use, for checking against the address formula.
+ * GEMM kernels use, for checking against the address formula of the digest's
+ * "Expert weights are scattered across pages. How does the kernel read them?",
+ * addr_e(n,t) = B_P + p_e(n)*f*d + (n mod f)*d + t, p_e(n) the W1 page for
+ * n < f and the W3 page otherwise (W2: the reading stated at moe_pool_desc;
+ * load-buffer slots: the same formula from the buffer base with page 3s + m).
  *   e, which, row, col  device int32/int32/int64/int64 [n] queries:
  *       which 0: gate/up operand, row = output column n in [0, 2f), col = t in [0, d)
  *       which 1: down projection, row in [0, d), col in [0, f)
@@ -579,8 +603,16 @@ int moe_vmm_map_experts(moe_vmm *vmm, const moe_expert_loc *locs, int32_t n, int
 
 /* The contiguous forward over the expert views (arguments as
  * moe_contiguous_forward).  MOE_ERR_STATE until the views are fully mapped;
- * MOE_ERR_INVALID_ARG if the layer handle's E + S or f*d*2 differ. */
-int moe_vmm_forward(const moe_vmm *vmm, const moe_pool *pool, const void *x, int64_t T, int32_t block_m,
+ * MOE_ERR_INVALID_ARG if the layer handle's E + S or f*d*2 differ.
+ * When the mapped table places experts in load buffer b (the active_buf of the
+ * last moe_vmm_map_experts), `pool` must be the layer handle whose load buffers
+ * are this object's views (its fills write them, MOE_ERR_INVALID_ARG
+ * otherwise), and the forward keeps that handle's double-buffer protocol as
+ * moe_paged_forward does: it waits on `stream` for the last moe_loadbuf_fill
+ * of buffer b (MOE_ERR_STATE if b was never filled) and marks b read after its
+ * kernels, so the next fill of b waits for it; flags as moe_paged_forward
+ * (MOE_FLAG_ATOMIC_COMBINE, MOE_FLAG_DEFER_READ_DONE). */
+int moe_vmm_forward(const moe_vmm *vmm, moe_pool *pool, const void *x, int64_t T, int32_t block_m,
                     const int32_t *topk_ids, const float *topk_w, const int32_t *sorted_ids,
                     const int32_t *block_expert, const int32_t *num_padded, void *y, void *ws,
                     size_t ws_bytes, uint32_t flags, void *stream);

@@ -311,6 +311,47 @@ bool pool_shape(const moe_pool *p, int32_t *E_tot, int64_t *page_bytes)
     *page_bytes = (int64_t)p->desc.f * p->desc.d * 2;
     return true;
 }
+void pool_loadbufs(const moe_pool *p, void *bases[2])
+{
+    const bool has = p->desc.loadbuf_slots > 0;
+    bases[0] = has ? p->desc.loadbuf_base[0] : nullptr;
+    bases[1] = has ? p->desc.loadbuf_base[1] : nullptr;
+}
+
+// A forward about to read load buffer buf on stream s waits for the buffer's
+// last fill (read after write).  MOE_ERR_STATE if the buffer was never filled.
+int loadbuf_read_begin(moe_pool *p, int32_t buf, hipStream_t s)
+{
+    if (!p->ever_filled[buf])
+        return fail(MOE_ERR_STATE, "load buffer " + std::to_string(buf) +
+                                       " was never filled but the table reads from it");
+    // a fill that has already completed needs no wait on the stream (the
+    // wait would still cost a queue round trip before the first kernel)
+    const hipError_t q = hipEventQuery(p->filled[buf]);
+    if (q == hipErrorNotReady) {
+        (void)hipGetLastError();
+        HIP_TRY(hipStreamWaitEvent(s, p->filled[buf], 0));
+    } else if (q != hipSuccess) {
+        return hip_fail(q, "hipEventQuery");
+    }
+    return MOE_OK;
+}
+
+// After a forward that read load buffer buf on stream s: mark the buffer read
+// (write after read), now or (MOE_FLAG_DEFER_READ_DONE) at its next fill.
+int loadbuf_read_end(moe_pool *p, int32_t buf, uint32_t flags, hipStream_t s)
+{
+    if (flags & MOE_FLAG_DEFER_READ_DONE) {
+        auto &rd = p->deferred_readers[buf];
+        if (std::find(rd.begin(), rd.end(), s) == rd.end())
+            rd.push_back(s);
+    } else {
+        HIP_TRY(hipEventRecord(p->consumed[buf], s));
+        p->consumed_rec[buf] = true;
+    }
+    return MOE_OK;
+}
+
 } // namespace pmoe
 
 extern "C" {
@@ -496,6 +537,7 @@ int moe_route(moe_pool *p, const float *logits, int64_t T, int32_t block_m, int3
     return MOE_OK;
 }
 
+
 namespace {
 
 // Checks of a paged forward, and its wait for the last fill of the load
@@ -513,17 +555,8 @@ int paged_begin(moe_pool *p, int64_t T, int32_t active_buf, uint32_t flags, hipS
     if (p->uses_loadbuf && !p->ever_filled[active_buf])
         return fail(MOE_ERR_STATE, "load buffer " + std::to_string(active_buf) +
                                        " was never filled but the table reads from it");
-    if (T > 0 && p->uses_loadbuf) {
-        // a fill that has already completed needs no wait on the stream (the
-        // wait would still cost a queue round trip before the first kernel)
-        const hipError_t q = hipEventQuery(p->filled[active_buf]);
-        if (q == hipErrorNotReady) {
-            (void)hipGetLastError();
-            HIP_TRY(hipStreamWaitEvent(s, p->filled[active_buf], 0));
-        } else if (q != hipSuccess) {
-            return hip_fail(q, "hipEventQuery");
-        }
-    }
+    if (T > 0 && p->uses_loadbuf)
+        return pmoe::loadbuf_read_begin(p, active_buf, s);
     return MOE_OK;
 }
 
@@ -531,16 +564,8 @@ int paged_begin(moe_pool *p, int64_t T, int32_t active_buf, uint32_t flags, hipS
 // or (MOE_FLAG_DEFER_READ_DONE) at the buffer's next fill.
 int paged_end(moe_pool *p, int64_t T, int32_t active_buf, uint32_t flags, hipStream_t s)
 {
-    if (T > 0 && p->uses_loadbuf) {
-        if (flags & MOE_FLAG_DEFER_READ_DONE) {
-            auto &rd = p->deferred_readers[active_buf];
-            if (std::find(rd.begin(), rd.end(), s) == rd.end())
-                rd.push_back(s);
-        } else {
-            HIP_TRY(hipEventRecord(p->consumed[active_buf], s));
-            p->consumed_rec[active_buf] = true;
-        }
-    }
+    if (T > 0 && p->uses_loadbuf)
+        return pmoe::loadbuf_read_end(p, active_buf, flags, s);
     return MOE_OK;
 }
 

@@ -24,6 +24,11 @@
 namespace pmoe {
 // experts (E + S) and expert-page bytes (f*d*2) of a layer handle; false for NULL
 bool pool_shape(const moe_pool *p, int32_t *E_tot, int64_t *page_bytes);
+// the layer handle's load-buffer events around a forward that reads buffer buf
+int loadbuf_read_begin(moe_pool *p, int32_t buf, hipStream_t s);
+int loadbuf_read_end(moe_pool *p, int32_t buf, uint32_t flags, hipStream_t s);
+// the layer handle's load-buffer base addresses
+void pool_loadbufs(const moe_pool *p, void *bases[2]);
 } // namespace pmoe
 
 struct moe_vmm {
@@ -37,6 +42,10 @@ struct moe_vmm {
     std::vector<char> base_mapped; // per handle: mapped into its pool / load-buffer view
     int64_t gran = 0, align = 0; // minimum and recommended mapping granularity
     bool all_mapped = false, broken = false;
+    // the mapped table places experts in load buffer active_buf (whose fills
+    // and readers are ordered by the layer handle's events)
+    bool uses_loadbuf = false;
+    int32_t active_buf = 0;
 };
 
 namespace {
@@ -275,12 +284,16 @@ int moe_vmm_map_experts(moe_vmm *v, const moe_expert_loc *locs, int32_t n, int32
         changed++;
     }
     v->all_mapped = true;
+    v->active_buf = active_buf;
+    v->uses_loadbuf = false;
+    for (int32_t e = 0; e < n; e++)
+        v->uses_loadbuf |= locs[e].kind == MOE_LOC_LOADBUF;
     if (n_remapped)
         *n_remapped = changed;
     return MOE_OK;
 }
 
-int moe_vmm_forward(const moe_vmm *v, const moe_pool *pool, const void *x, int64_t T, int32_t block_m,
+int moe_vmm_forward(const moe_vmm *v, moe_pool *pool, const void *x, int64_t T, int32_t block_m,
                     const int32_t *topk_ids, const float *topk_w, const int32_t *sorted_ids,
                     const int32_t *block_expert, const int32_t *num_padded, void *y, void *ws, size_t ws_bytes,
                     uint32_t flags, void *stream)
@@ -289,14 +302,34 @@ int moe_vmm_forward(const moe_vmm *v, const moe_pool *pool, const void *x, int64
         return err(MOE_ERR_INVALID_ARG, "vmm is null");
     if (!v->all_mapped || v->broken)
         return err(MOE_ERR_STATE, "the expert views are not fully mapped");
+    if (flags & ~(MOE_FLAG_ATOMIC_COMBINE | MOE_FLAG_DEFER_READ_DONE))
+        return err(MOE_ERR_INVALID_ARG, "unknown flag bits");
     int32_t E_tot = 0;
     int64_t page = 0;
     if (!pmoe::pool_shape(pool, &E_tot, &page))
         return err(MOE_ERR_INVALID_ARG, "pool is null");
     if (E_tot != v->E_tot || page != v->page)
         return err(MOE_ERR_INVALID_ARG, "the layer handle's experts or page size differ from the views'");
-    return moe_contiguous_forward(pool, v->w13_va, v->w2_va, x, T, block_m, topk_ids, topk_w, sorted_ids,
-                                  block_expert, num_padded, y, ws, ws_bytes, flags, stream);
+    // expert views onto a load buffer: the forward waits for that buffer's last
+    // fill and marks it read afterwards, through the layer handle whose fills
+    // write it (the same events as a paged forward of that buffer)
+    const bool lb = T > 0 && v->uses_loadbuf;
+    hipStream_t s = (hipStream_t)stream;
+    if (lb) {
+        void *bases[2] = {nullptr, nullptr};
+        pmoe::pool_loadbufs(pool, bases);
+        if (bases[v->active_buf] != v->lb_va[v->active_buf])
+            return err(MOE_ERR_INVALID_ARG, "the layer handle's load buffers are not these views'");
+        const int rc = pmoe::loadbuf_read_begin(pool, v->active_buf, s);
+        if (rc != MOE_OK)
+            return rc;
+    }
+    const int rc = moe_contiguous_forward(pool, v->w13_va, v->w2_va, x, T, block_m, topk_ids, topk_w, sorted_ids,
+                                          block_expert, num_padded, y, ws, ws_bytes,
+                                          flags & MOE_FLAG_ATOMIC_COMBINE, stream);
+    if (rc != MOE_OK || !lb)
+        return rc;
+    return pmoe::loadbuf_read_end(pool, v->active_buf, flags, s);
 }
 
 } // extern "C"

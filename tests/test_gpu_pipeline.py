@@ -27,7 +27,9 @@ D, F, E, K, T = 512, 256, 16, 4, 96
 SLOTS = 8   # slots per load buffer
 N_LB = 4    # experts each layer starts with in the load buffer
 SPARE = 36  # pages no table names at the start
-DUMMY_BYTES = 512 << 20
+# cycles of the sleep kernel that holds the copy stream (a bounded spin that
+# ends on its own, some hundreds of milliseconds: far longer than enqueuing a pass)
+HOLD_CYCLES = 400_000_000
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -179,22 +181,20 @@ def test_pipeline_passes_copy_before_switch(block_m):
     b1 = [_bits(y) for y in y1]
 
     new, copies, dropped, free = change_list(st)
-    host_dummy = torch.empty(DUMMY_BYTES, dtype=torch.uint8, pin_memory=True)
-    dev_dummy = torch.empty(DUMMY_BYTES, dtype=torch.uint8, device="cuda")
-    ev_dummy = torch.cuda.Event()
+    ev_hold = torch.cuda.Event()
 
     def stage():
         # hold the copy stream so that the page copies land long after layer 0 could start
         with torch.cuda.stream(copy):
-            dev_dummy.copy_(host_dummy, non_blocking=True)
-            ev_dummy.record(copy)
+            torch.cuda._sleep(HOLD_CYCLES)
+            ev_hold.record(copy)
         for l in range(L):
             pipe.stage_table(l, new[l], copies[l])
 
     y2 = run_pass(pipe, st, new, after_first_fill=stage)
-    pending = not ev_dummy.query()
-    print(f"copies still in flight after the pass was enqueued: {pending}", flush=True)
+    pending = not ev_hold.query()
     torch.cuda.synchronize()
+    assert pending, "the copy stream was no longer held when the pass had been enqueued; the test shows nothing"
     _check_oracle(st, y2)
     for l in range(L):
         assert np.array_equal(_bits(y2[l]), b1[l]), f"layer {l} differs from the first pass"
@@ -219,12 +219,10 @@ def test_pipeline_reclaim_waits_for_running_pass():
     st = Stack(4200)
     copy = torch.cuda.Stream()
     pipe = pm.MoePipeline(st.handles, copy)
-    host_dummy = torch.empty(DUMMY_BYTES, dtype=torch.uint8, pin_memory=True)
-    dev_dummy = torch.empty(DUMMY_BYTES, dtype=torch.uint8, device="cuda")
-    ev_dummy = torch.cuda.Event()
+    ev_hold = torch.cuda.Event()
     with torch.cuda.stream(copy):
-        dev_dummy.copy_(host_dummy, non_blocking=True)  # pass 1 waits for its fills behind this
-        ev_dummy.record(copy)
+        torch.cuda._sleep(HOLD_CYCLES)  # pass 1 waits for its fills behind this
+        ev_hold.record(copy)
     y1 = run_pass(pipe, st, st.tables)
     new = st.tables[2].copy()
     ev = [e for e in range(E) if new[e]["kind"] == synth.LOC_POOL][0]
@@ -244,10 +242,9 @@ def test_pipeline_reclaim_waits_for_running_pass():
         pipe.stage_table(1, t1, [(e1, st.blobs[1][e1])])
     assert ei.value.code == pm.MOE_ERR_PAGE_ALIAS
     early = pipe.reclaim()
-    still_running = not ev_dummy.query()
-    print(f"pass 1 still held behind the copy stream at the reclaim: {still_running}", flush=True)
-    if still_running:
-        assert early == [], "pages reported while the pass reading them had not finished"
+    still_running = not ev_hold.query()
+    assert still_running, "pass 1 was no longer held at the reclaim; the test shows nothing"
+    assert early == [], "pages reported while the pass reading them had not finished"
     torch.cuda.synchronize()
     got = sorted(early + pipe.reclaim())
     assert got == sorted(dropped)

@@ -210,3 +210,39 @@ def test_forward_rejects_other_layer_shape(vl):
         vl.ev.forward(other, vl.x, r, ws)
     assert ei.value.code == pm.MOE_ERR_INVALID_ARG
     other.close()
+
+
+@pytest.mark.parametrize("flags", [0, pm.MOE_FLAG_DEFER_READ_DONE])
+def test_fill_waits_for_a_queued_vmm_forward(vl, flags):
+    """A forward over the expert views that reads load buffer 0 is held back on
+    its stream behind a sleep kernel; a fill of buffer 0 with NaN pages is
+    enqueued after it on a copy stream.  The fill must wait for that forward
+    (write after read), so y matches the oracle; a forward after the fill
+    reads the NaN pages through the views (read after write)."""
+    s = SPEC
+    vl.fill(0)
+    vl.ev.map_experts(vl.locs, 0)
+    lb = [e for e in range(s.E_tot) if vl.locs[e]["kind"] == synth.LOC_LOADBUF]
+    assert lb, "the table must place experts in the load buffer"
+    comp, copy = torch.cuda.Stream(), torch.cuda.Stream()
+    ws = pm.workspace(vl.pool, s.T, 16)
+    r = pm.route(vl.pool, vl.logits, 16, ws)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(comp):
+        torch.cuda._sleep(50_000_000)
+        y = vl.ev.forward(vl.pool, vl.x, r, ws, flags=flags, stream=comp)
+    held = not comp.query()
+    nan = torch.full((3 * vl.fd,), float("nan"), dtype=torch.bfloat16).pin_memory()
+    slots = [int(vl.locs[e]["idx"][0]) for e in lb]
+    pm.moe_loadbuf_fill(vl.pool, 0, slots, [nan] * len(slots), copy)
+    torch.cuda.synchronize()
+    assert held, "the forward had finished before the fill was enqueued; the test shows nothing"
+    ids, w = oracle.route(vl.L.logits, s.k, s.S)
+    got = y_f64(y)
+    assert np.all(np.isfinite(got)) and max_rel_err(got, oracle.moe(vl.L.x, vl.L.w13, vl.L.w2, ids, w)) <= TOL
+    assert np.isin(ids, lb).any()
+    with torch.cuda.stream(comp):
+        y2 = vl.ev.forward(vl.pool, vl.x, r, ws, flags=flags, stream=comp)
+    torch.cuda.synchronize()
+    assert np.isnan(y_f64(y2)).any(), "the forward after the NaN fill did not read it"
+    vl.fill(0)  # the real experts back in buffer 0
