@@ -12,9 +12,13 @@ Consecutive steps rotate over R copies of the layer's pool and load buffers
 (R large enough that R working sets exceed the 256 MB Infinity Cache), as the
 layers of a model would, so each step streams its weights from HBM.
 
-Prints ONE JSON line.  Default workload: the Qwen1.5-MoE-shaped layer
-(T=1024, d=2048, f=1408, E=60, top-4; 48 experts in a 256-page pool, 12 in the
-load buffer).
+Prints ONE JSON line.  Default workload: the Mixtral-8x7B-shaped layer (T=4096,
+d=4096, f=14336, E=8, top-2, Zipf(1.2) routing; all experts paged in a
+fragmented pool), the largest configuration; every other configuration (the
+tiny, Qwen1.5-MoE-shaped and Qwen3-Next-shaped layers and the decode sweep
+T = 1, 8, 32, 128, 512) is timed in the same run and reported under "configs"
+(step time, fractions of the rooflines, paged vs contiguous, the dominant
+kernel's roofline).
 """
 from __future__ import annotations
 
@@ -75,7 +79,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="qwen15", choices=sorted(WORKLOAD_TEXT))
+    ap.add_argument("--workload", default="mixtral", choices=sorted(WORKLOAD_TEXT))
+    ap.add_argument("--only", action="store_true",
+                    help="time the chosen workload alone (default: also every other configuration, as sub-objects)")
     ap.add_argument("--T", type=int, default=None, help="tokens (default: the workload's own; decode: 1)")
     ap.add_argument("--block-m", type=int, default=0, help="GEMM tile height (default: moe_suggest_block_m)")
     ap.add_argument("--atomic", action="store_true", help="fp32-atomic combine instead of the ordered one")
@@ -133,11 +139,9 @@ def main():
               "implemented here). Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     import paged_expert_weight_amd as pm
-    from workloads import device as wdev
     from workloads import synth
 
     pm.lib()  # fails loudly without the HIP library
@@ -146,15 +150,86 @@ def main():
         sys.exit(1)
 
     name = args.workload
-    s = synth.SPECS[name]
-    T = args.T if args.T is not None else (1 if name == "decode" else s.T)
-    t0 = time.time()
-    layer = synth.make_layer(s, T)
-    if args.placement == "allocator":
-        layer = allocator_placed(layer)
-    dev = wdev.to_device(layer)
-    print(f"# layer {name} T={T} generated and placed in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    T = args.T if args.T is not None else (1 if name == "decode" else synth.SPECS[name].T)
+    layer = make_host_layer(name, T, args.placement)
+    line, extra = bench_layer(layer, args, full=True)
 
+    # every other configuration, timed in the same run: step time, fractions of the rooflines,
+    # paged vs contiguous and the dominant kernel's roofline (one layer resident at a time)
+    if not args.only:
+        subs = {}
+        for sub_name, sub_T in ALL_CONFIGS:
+            if (sub_name, sub_T) == (name, T):
+                continue
+            sub_layer = make_host_layer(sub_name, sub_T, "synth")
+            sub, _ = bench_layer(sub_layer, args, full=False)
+            subs[f"{sub_name}_T{sub_T}"] = sub
+            del sub_layer
+            torch.cuda.empty_cache()
+        line["configs"] = subs
+
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(layer, args.cpu_seconds)
+    line.update(extra)
+    print(json.dumps(line), flush=True)
+
+
+# The configurations every default run times besides the headline one (the decode sweep
+# as one entry per batch size).
+ALL_CONFIGS = (("tiny", 16), ("qwen15", 1024), ("decode", 1), ("decode", 8), ("decode", 32), ("decode", 128),
+               ("decode", 512), ("mixtral", 4096), ("qwen3n", 8192))
+_HOST_LAYERS = {}
+
+
+def make_host_layer(name, T, placement):
+    """The seeded host layer of a workload with its first T tokens (the decode sweep
+    slices one 512-token draw, so its weights are generated once)."""
+    from workloads import synth
+    t0 = time.time()
+    s = synth.SPECS[name]
+    key = (name, placement)
+    if key not in _HOST_LAYERS:
+        _HOST_LAYERS.clear()
+        full = synth.make_layer(s)
+        if placement == "allocator":
+            full = allocator_placed(full)
+        _HOST_LAYERS[key] = full
+    full = _HOST_LAYERS[key]
+    layer = synth.Layer(s, full.x[:T].copy(), full.logits[:T].copy(), full.w13, full.w2, full.placement)
+    print(f"# layer {name} T={T} generated in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    return layer
+
+
+def carve(dev, s, torch):
+    """One device allocation holding a copy of the pool, both load buffers and the
+    contiguous twin's w13 / w2, so that the paged path and its twin read memory of
+    the same placement."""
+    parts = [dev.pool, dev.loadbuf[0], dev.loadbuf[1], dev.w13, dev.w2]
+    n = [t.numel() for t in parts]
+    big = torch.empty(sum(n), dtype=torch.bfloat16, device=dev.pool.device)
+    views, off = [], 0
+    for t, k in zip(parts, n):
+        v = big[off:off + k].view(t.shape)
+        v.copy_(t)
+        views.append(v)
+        off += k
+    return big, views
+
+
+def bench_layer(layer, args, full):
+    """Time one layer: the paged step (routing + forward in one call), its contiguous
+    twin in alternating blocks, per-stage HIP-event times and the dominant kernel's
+    roofline.  full: also the load-buffer fill, the per-step spread and the adjuster's
+    host cost.  Returns (line, extra keys for the top level)."""
+    import numpy as np
+    import torch
+
+    import paged_expert_weight_amd as pm
+    from workloads import device as wdev
+
+    s = layer.spec
+    name, T = s.name, layer.T
+    dev = wdev.to_device(layer)
     fd = s.f * s.d
     # working set of one step (weights of touched experts are at most all experts)
     ws_bytes_est = min(s.E_tot, T * s.k_eff) * 3 * fd * 2
@@ -163,16 +238,16 @@ def main():
     slots = sorted(dev.host_blobs)
     copies = []
     for r in range(R):
-        pool = dev.pool if r == 0 else dev.pool.clone()
-        lbs = tuple(dev.loadbuf) if r == 0 else tuple(b.clone() for b in dev.loadbuf)
-        h = pm.moe_pool_create(pool, s.pool_pages, s.d, s.f, s.E, s.k, s.S, s.loadbuf_slots, lbs)
+        big, (pool, lb0, lb1, w13, w2) = carve(dev, s, torch)
+        h = pm.moe_pool_create(pool, s.pool_pages, s.d, s.f, s.E, s.k, s.S, s.loadbuf_slots, (lb0, lb1))
         pm.moe_set_expert_locs(h, layer.placement.locs)
         if s.loadbuf_slots:
             pm.moe_loadbuf_fill(h, 0, slots, [dev.host_blobs[k] for k in slots])
-        w13 = dev.w13 if r == 0 else dev.w13.clone()
-        w2 = dev.w2 if r == 0 else dev.w2.clone()
-        copies.append(dict(h=h, pool=pool, lbs=lbs, w13=w13, w2=w2))
+        copies.append(dict(h=h, big=big, pool=pool, lbs=(lb0, lb1), w13=w13, w2=w2))
     torch.cuda.synchronize()
+    dev.pool = dev.w13 = dev.w2 = None
+    dev.loadbuf = None
+    torch.cuda.empty_cache()
 
     h0 = copies[0]["h"]
     bm = args.block_m or pm.moe_suggest_block_m(h0, T)
@@ -181,6 +256,9 @@ def main():
     rt = pm.RouteOut(h0, T, bm)
     y = torch.empty_like(dev.x)
     stream = torch.cuda.current_stream()
+    # the headline takes exactly --steps; the short steps of the other configurations take more
+    K = args.steps if full or ws_bytes_est * 8 > 2e9 else max(args.steps, 100)
+    W = args.warmup
 
     # One step = routing + the layer, in one call (for a decode step the routing runs inside the gate/up
     # launch).  The load buffer is refilled only by the concurrent-fill measurement (buffer 1): the
@@ -208,22 +286,23 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / K
 
-    # ---- paging overhead: the contiguous twin (same kernels, dense weight arrays, same inputs and
-    # routing) against the paged path in alternating blocks (contiguous, paged, three times each), so
-    # that both see the same clock and thermal state.  It runs before the timed region.
+    # ---- paging overhead: the contiguous twin (same kernels, dense weight arrays carved from the same
+    # allocation as the pool, same inputs and routing) against the paged path in alternating blocks
+    # (contiguous, paged, three times each), so that both see the same clock and thermal state.  It runs
+    # before the timed region.
     contig_ms = paged_alt_ms = None
     if not args.no_contig:
         c_runs, p_runs = [], []
         for _ in range(3):
-            c_runs.append(timed(args.steps, args.warmup, contiguous=True))
-            p_runs.append(timed(args.steps, args.warmup))
+            c_runs.append(timed(K, W, contiguous=True))
+            p_runs.append(timed(K, W))
         contig_ms, paged_alt_ms = sum(c_runs) / len(c_runs), sum(p_runs) / len(p_runs)
-        print(f"# contiguous: {contig_ms * 1e3:.1f} us/step, paged in the same blocks {paged_alt_ms * 1e3:.1f}",
-              file=sys.stderr, flush=True)
+        print(f"# {name} T={T}: contiguous {contig_ms * 1e3:.1f} us/step, paged in the same blocks "
+              f"{paged_alt_ms * 1e3:.1f}", file=sys.stderr, flush=True)
 
     # ---- the timed region (paged)
-    ms = timed(args.steps, args.warmup)
-    print(f"# paged: {ms * 1e3:.1f} us/step", file=sys.stderr, flush=True)
+    ms = timed(K, W)
+    print(f"# {name} T={T}: paged {ms * 1e3:.1f} us/step", file=sys.stderr, flush=True)
 
     ids = rt.topk_ids.cpu().numpy()
     n = T * s.k_eff
@@ -241,7 +320,7 @@ def main():
         pm.moe_stage_timing(c["h"], True)
     ra0, ra1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     route_ms = 0.0
-    for i in range(args.steps):
+    for i in range(K):
         c = copies[i % R]
         if routed_form:
             step(i)
@@ -263,8 +342,9 @@ def main():
         stage = [a + b for a, b in zip(stage, msv)]
         cnt += k
     stage_us = [v / max(1, cnt) * 1e3 for v in stage]
-    route_us = route_ms / args.steps * 1e3
+    route_us = route_ms / K * 1e3
 
+    # ---- roofline of the dominant kernel (the gate/up launch: 2/3 of the flops and of the weight bytes)
     g1_flops = 4.0 * n * s.f * s.d
     g1_bytes = touched * 2 * fd * 2 + T * s.d * 2 + n * s.f * 2
     g1_ai = g1_flops / g1_bytes
@@ -285,6 +365,44 @@ def main():
     roof["algorithmic_bytes_per_launch"] = int(g1_bytes)
     roof["algorithmic_flops_per_launch"] = int(g1_flops)
 
+    line = {
+        "metric": METRIC,
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD_TEXT[name] if name != "decode" else f"{WORKLOAD_TEXT[name]}; T={T}",
+                   "name": name, "T": T, "block_m": bm, "placement": args.placement if full else "synth",
+                   "gemm_form": "decode, routing in its gate/up launch" if routed_form else
+                   "decode" if decode_form else "tiles",
+                   "combine": "atomic" if args.atomic else "ordered", "layer_copies_rotated": R},
+        "hbm_gbs": round(gbs, 1),
+        "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "mfma_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+        "algorithmic": {"flops": int(flops), "bytes": int(bytes_alg), "experts_touched": touched},
+        "contig_ms_per_step": round(contig_ms, 5) if contig_ms else None,
+        "overhead_vs_contiguous_pct": round((paged_alt_ms / contig_ms - 1) * 100, 3) if contig_ms else None,
+        "stages_us": {"route_align": round(route_us, 2), "gate_up": round(stage_us[0], 2),
+                      "down": round(stage_us[1], 2),
+                      # the decode form combines inside its down launch: no stage of its own
+                      "combine": None if decode_form else round(stage_us[2], 2)},
+        "roofline": roof,
+    }
+    extra = {}
+    if not full:
+        for k in ("metric", "n_gpus", "higher_is_better", "scaling", "vs_baseline", "dtype", "data"):
+            line.pop(k)
+        for c in copies:
+            c["h"].close()
+        return line, extra
+
     # ---- load-buffer fill (host link) and its effect on compute
     loadbuf = None
     if s.loadbuf_slots and not args.no_fill:
@@ -303,15 +421,15 @@ def main():
         copy.synchronize()
         fill_ms = f0.elapsed_time(f1) / reps
         # compute on buffer 0 while buffer 1 keeps filling
-        for _ in range(max(1, int(args.steps * ms / fill_ms) + 1)):
+        for _ in range(max(1, int(K * ms / fill_ms) + 1)):
             pm.moe_loadbuf_fill(hc, 1, slots, blobs, copy)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        for i in range(args.steps):
+        for i in range(K):
             step(0)
         e1.record(stream)
         torch.cuda.synchronize()
-        busy_ms = e0.elapsed_time(e1) / args.steps
+        busy_ms = e0.elapsed_time(e1) / K
         loadbuf = {"experts_per_fill": len(slots), "bytes_per_fill": nbytes, "fill_ms": round(fill_ms, 3),
                    "h2d_gbs": round(nbytes / (fill_ms * 1e-3) / 1e9, 2),
                    "step_us_with_concurrent_fill": round(busy_ms * 1e3, 2),
@@ -319,55 +437,18 @@ def main():
                    "fill_hidden_behind_one_step": fill_ms <= ms}
 
     # ---- per-step spread (events around every step of one more timed pass)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    for i in range(args.steps):
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    for i in range(K):
         ev[i][0].record(stream)
         step(i)
         ev[i][1].record(stream)
     torch.cuda.synchronize()
     per_step = np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
     spread = {q: round(float(np.percentile(per_step, p)), 2) for q, p in (("p10", 10), ("p50", 50), ("p90", 90))}
-
-    line = {
-        "metric": METRIC,
-        "value": round(tflops, 3),
-        "unit": "TFLOP/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": WORKLOAD_TEXT[name], "name": name, "T": T, "block_m": bm,
-                   "placement": args.placement,
-                   "gemm_form": "decode, routing in its gate/up launch" if routed_form else
-                   "decode" if decode_form else "tiles",
-                   "combine": "atomic" if args.atomic else "ordered", "layer_copies_rotated": R},
-        "hbm_gbs": round(gbs, 1),
-        "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
-        "mfma_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-        "algorithmic": {"flops": int(flops), "bytes": int(bytes_alg), "experts_touched": touched},
-        "contig_ms_per_step": round(contig_ms, 5) if contig_ms else None,
-        "overhead_vs_contiguous_pct": round((paged_alt_ms / contig_ms - 1) * 100, 3) if contig_ms else None,
-        "stages_us": {"route_align": round(route_us, 2), "gate_up": round(stage_us[0], 2),
-                      "down": round(stage_us[1], 2),
-                      # the decode form combines inside its down launch: no stage of its own
-                      "combine": None if decode_form else round(stage_us[2], 2)},
-        "step_us_spread": spread,
-        "roofline": roof,
-        "loadbuf": loadbuf,
-        "adjuster": adjuster_timing(s.E),
-    }
-
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(layer, args.cpu_seconds)
-
-    print(json.dumps(line), flush=True)
+    extra = {"step_us_spread": spread, "loadbuf": loadbuf, "adjuster": adjuster_timing(s.E)}
     for c in copies:
         c["h"].close()
+    return line, extra
 
 
 def allocator_placed(layer):
