@@ -251,6 +251,27 @@ int moe_route_forward(moe_pool *pool, const float *logits, const void *x, int64_
                       size_t ws_bytes, uint32_t flags, void *stream);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * call as moe_route_forward, same outputs bit for bit, with its workspace in a
+ * static device array of the library instead of a caller's allocation.  The
+ * array holds MOE_NOALLOC_SCRATCH_BYTES (64 MiB) on every device the library
+ * runs on, from the first call on that device until the process ends; the call
+ * allocates no device memory.  A (T, block_m, flags) whose
+ * moe_workspace_bytes exceeds it fails with MOE_ERR_WORKSPACE (256-row tiles
+ * alone need 64 MiB of partial tiles: use block_m <= 128 here).  All calls on
+ * one device share that device's array: calls that may overlap in time on one
+ * device (other streams, other threads) race and must be ordered by the
+ * caller.  Nothing in the array has to start at zero, so what an earlier call
+ * left there does not matter.  Arguments and errors otherwise as
+ * moe_route_forward.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int moe_route_forward_noalloc(moe_pool *pool, const float *logits, const void *x, int64_t T, int32_t block_m,
+                              int32_t *topk_ids, float *topk_w, int32_t *sorted_ids, int32_t *block_expert,
+                              int32_t *num_padded, int32_t active_buf, void *y, uint32_t flags, void *stream);
+
+/*
  * moe_route_forward with the weights in the two dense arrays of
  * moe_contiguous_forward (the contiguous baseline of the one-call step; same
  * kernels and launches, only the per-tile base address differs).

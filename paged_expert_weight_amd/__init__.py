@@ -33,6 +33,7 @@ MOE_LOC_POOL = 0
 MOE_LOC_LOADBUF = 1
 MOE_FLAG_ATOMIC_COMBINE = 1
 MOE_FLAG_DEFER_READ_DONE = 2
+MOE_NOALLOC_SCRATCH_BYTES = 64 << 20  # the static workspace of moe_route_forward_noalloc, per device
 MOE_FORM_TILES = 0
 MOE_FORM_DECODE = 1
 MOE_FORM_DECODE_ROUTED = 2
@@ -54,7 +55,7 @@ EXPORTS = (
     "moe_alloc_ssm_pages", "moe_free_ssm_pages", "moe_alloc_small_pages", "moe_free_small_pages",
     "moe_free_request", "moe_alloc_get_stats",
     "moe_vmm_create", "moe_vmm_destroy", "moe_vmm_views", "moe_vmm_granularity", "moe_vmm_map_experts",
-    "moe_vmm_forward",
+    "moe_vmm_forward", "moe_route_forward_noalloc",
 )
 
 
@@ -118,6 +119,7 @@ def lib():
     L.moe_paged_forward.argtypes = [P, P, i64, i32, P, P, P, P, P, i32, P, P, sz, u32, P]
     L.moe_contiguous_forward.argtypes = [P, P, P, P, i64, i32, P, P, P, P, P, P, P, sz, u32, P]
     L.moe_route_forward.argtypes = [P, P, P, i64, i32, P, P, P, P, P, i32, P, P, sz, u32, P]
+    L.moe_route_forward_noalloc.argtypes = [P, P, P, i64, i32, P, P, P, P, P, i32, P, u32, P]
     L.moe_route_contiguous_forward.argtypes = [P, P, P, P, P, i64, i32, P, P, P, P, P, P, P, sz, u32, P]
     L.moe_loadbuf_fill.argtypes = [P, i32, i32, P, P, P]
     L.moe_resolve_addrs.argtypes = [P, i32, i64, P, P, P, P, P, P, P]
@@ -294,6 +296,13 @@ def moe_route_forward(p: MoePool, logits, x, block_m: int, topk_ids, topk_w, sor
     _check(lib().moe_route_forward(p.handle, _ptr(logits), _ptr(x), x.shape[0], block_m, _ptr(topk_ids),
                                    _ptr(topk_w), _ptr(sorted_ids), _ptr(block_expert), _ptr(num_padded),
                                    active_buf, _ptr(y), _ptr(workspace), ws_bytes, flags, _stream(stream)))
+
+
+def moe_route_forward_noalloc(p: MoePool, logits, x, block_m: int, topk_ids, topk_w, sorted_ids, block_expert,
+                              num_padded, active_buf: int, y, flags: int = 0, stream=None) -> None:
+    _check(lib().moe_route_forward_noalloc(p.handle, _ptr(logits), _ptr(x), x.shape[0], block_m, _ptr(topk_ids),
+                                           _ptr(topk_w), _ptr(sorted_ids), _ptr(block_expert), _ptr(num_padded),
+                                           active_buf, _ptr(y), flags, _stream(stream)))
 
 
 def moe_route_contiguous_forward(p: MoePool, w13, w2, logits, x, block_m: int, topk_ids, topk_w, sorted_ids,

@@ -13,7 +13,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libpmoe.so")
 OBJDIR = os.path.join(HERE, "_build")
 
-SOURCES = ["route_align.hip", "moe_gemm.hip", "decode.hip", "runtime.cpp", "adjuster.cpp", "allocator.cpp", "vmm.cpp"]
+SOURCES = ["route_align.hip", "moe_gemm.hip", "decode.hip", "runtime.cpp", "adjuster.cpp", "allocator.cpp", "vmm.cpp",
+           "noalloc.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
