@@ -226,6 +226,7 @@ def bench_layer(layer, args, full):
 
     import paged_expert_weight_amd as pm
     from workloads import device as wdev
+    from workloads import synth
 
     s = layer.spec
     name, T = s.name, layer.T
@@ -236,14 +237,24 @@ def bench_layer(layer, args, full):
     R = args.rotate or max(2, min(16, math.ceil(1.0 * MALL_BYTES / max(1, ws_bytes_est)) + 1))
 
     slots = sorted(dev.host_blobs)
+    # the same layer over the twin's own bytes: w13 and w2 lie back to back in the carved
+    # allocation, so as a pool of 3(E+S) pages they hold W1_e on page 2e, W3_e on 2e+1 and W2_e on
+    # 2(E+S)+e (every expert, the load-buffer ones included).  Paged reads of this pool touch exactly
+    # the addresses the contiguous kernels read: the difference is the page lookup alone.
+    same_locs = layer.placement.locs.copy()
+    for e in range(s.E_tot):
+        same_locs[e]["kind"] = synth.LOC_POOL
+        same_locs[e]["idx"] = (2 * e, 2 * e + 1, 2 * s.E_tot + e)
     copies = []
     for r in range(R):
         big, (pool, lb0, lb1, w13, w2) = carve(dev, s, torch)
         h = pm.moe_pool_create(pool, s.pool_pages, s.d, s.f, s.E, s.k, s.S, s.loadbuf_slots, (lb0, lb1))
         pm.moe_set_expert_locs(h, layer.placement.locs)
+        h_same = pm.moe_pool_create(w13, 3 * s.E_tot, s.d, s.f, s.E, s.k, s.S, s.loadbuf_slots, (lb0, lb1))
+        pm.moe_set_expert_locs(h_same, same_locs)
         if s.loadbuf_slots:
             pm.moe_loadbuf_fill(h, 0, slots, [dev.host_blobs[k] for k in slots])
-        copies.append(dict(h=h, big=big, pool=pool, lbs=(lb0, lb1), w13=w13, w2=w2))
+        copies.append(dict(h=h, h_same=h_same, big=big, pool=pool, lbs=(lb0, lb1), w13=w13, w2=w2))
     torch.cuda.synchronize()
     dev.pool = dev.w13 = dev.w2 = None
     dev.loadbuf = None
@@ -263,42 +274,48 @@ def bench_layer(layer, args, full):
     # One step = routing + the layer, in one call (for a decode step the routing runs inside the gate/up
     # launch).  The load buffer is refilled only by the concurrent-fill measurement (buffer 1): the
     # "buffer read" mark of buffer 0 is deferred to its next fill instead of a stream marker per step.
-    def step(i, contiguous=False):
+    def step(i, mode="paged"):
         c = copies[i % R]
-        if contiguous:
+        if mode == "contiguous":
             pm.moe_route_contiguous_forward(c["h"], c["w13"], c["w2"], dev.logits, dev.x, bm, rt.topk_ids,
                                             rt.topk_w, rt.sorted_ids, rt.block_expert, rt.num_padded, y, ws, flags,
                                             stream)
         else:
-            pm.moe_route_forward(c["h"], dev.logits, dev.x, bm, rt.topk_ids, rt.topk_w, rt.sorted_ids,
-                                 rt.block_expert, rt.num_padded, 0, y, ws, flags | pm.MOE_FLAG_DEFER_READ_DONE,
-                                 stream)
+            pm.moe_route_forward(c["h_same" if mode == "paged_same" else "h"], dev.logits, dev.x, bm, rt.topk_ids,
+                                 rt.topk_w, rt.sorted_ids, rt.block_expert, rt.num_padded, 0, y, ws,
+                                 flags | pm.MOE_FLAG_DEFER_READ_DONE, stream)
 
-    def timed(K, W, contiguous=False):
+    def timed(K, W, mode="paged"):
         for i in range(W):
-            step(i, contiguous)
+            step(i, mode)
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for i in range(K):
-            step(i, contiguous)
+            step(i, mode)
         e1.record(stream)
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / K
 
-    # ---- paging overhead: the contiguous twin (same kernels, dense weight arrays carved from the same
-    # allocation as the pool, same inputs and routing) against the paged path in alternating blocks
-    # (contiguous, paged, three times each), so that both see the same clock and thermal state.  It runs
-    # before the timed region.
-    contig_ms = paged_alt_ms = None
+    # ---- paging overhead: the contiguous twin (same kernels, dense weight arrays, same inputs and
+    # routing) against the paged path over the twin's own bytes (the page lookup is the only difference)
+    # and over the layer's pool (pages in the workload's order, carved from the same allocation), in
+    # alternating blocks (three rounds of the three modes, rotated), so that all three see the same clock
+    # and thermal state.  It runs before the timed region.
+    contig_ms = same_ms = paged_alt_ms = None
     if not args.no_contig:
-        c_runs, p_runs = [], []
-        for _ in range(3):
-            c_runs.append(timed(K, W, contiguous=True))
-            p_runs.append(timed(K, W))
-        contig_ms, paged_alt_ms = sum(c_runs) / len(c_runs), sum(p_runs) / len(p_runs)
-        print(f"# {name} T={T}: contiguous {contig_ms * 1e3:.1f} us/step, paged in the same blocks "
-              f"{paged_alt_ms * 1e3:.1f}", file=sys.stderr, flush=True)
+        # blocks of about 30 ms each, and every mode in every position of the rotation once (a block that
+        # follows a host synchronisation can start at a lower clock)
+        K_cmp = min(2000, max(K, math.ceil(30.0 / max(1e-3, timed(5, W)))))
+        modes = ("contiguous", "paged_same", "paged")
+        runs = {m: [] for m in modes}
+        for rnd in range(3):
+            for i in range(3):
+                mode = modes[(rnd + i) % 3]
+                runs[mode].append(timed(K_cmp, W, mode))
+        contig_ms, same_ms, paged_alt_ms = (sum(runs[m]) / 3 for m in modes)
+        print(f"# {name} T={T}: contiguous {contig_ms * 1e3:.1f} us/step, paged over the same bytes "
+              f"{same_ms * 1e3:.1f}, paged over the pool {paged_alt_ms * 1e3:.1f}", file=sys.stderr, flush=True)
 
     # ---- the timed region (paged)
     ms = timed(K, W)
@@ -388,7 +405,11 @@ def bench_layer(layer, args, full):
         "mfma_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
         "algorithmic": {"flops": int(flops), "bytes": int(bytes_alg), "experts_touched": touched},
         "contig_ms_per_step": round(contig_ms, 5) if contig_ms else None,
-        "overhead_vs_contiguous_pct": round((paged_alt_ms / contig_ms - 1) * 100, 3) if contig_ms else None,
+        # the cost of the page lookup: paged reads of the twin's own bytes against the twin
+        "overhead_vs_contiguous_pct": round((same_ms / contig_ms - 1) * 100, 3) if contig_ms else None,
+        # the layer's pool (pages in the workload's order, load-buffer experts in the load buffer)
+        # against the twin: the lookup plus where the weights lie in memory
+        "pool_vs_contiguous_pct": round((paged_alt_ms / contig_ms - 1) * 100, 3) if contig_ms else None,
         "stages_us": {"route_align": round(route_us, 2), "gate_up": round(stage_us[0], 2),
                       "down": round(stage_us[1], 2),
                       # the decode form combines inside its down launch: no stage of its own
@@ -401,6 +422,7 @@ def bench_layer(layer, args, full):
             line.pop(k)
         for c in copies:
             c["h"].close()
+            c["h_same"].close()
         return line, extra
 
     # ---- load-buffer fill (host link) and its effect on compute
@@ -448,6 +470,7 @@ def bench_layer(layer, args, full):
     extra = {"step_us_spread": spread, "loadbuf": loadbuf, "adjuster": adjuster_timing(s.E)}
     for c in copies:
         c["h"].close()
+        c["h_same"].close()
     return line, extra
 
 
