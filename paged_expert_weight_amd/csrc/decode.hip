@@ -83,13 +83,8 @@ __device__ __forceinline__ uint4 load_stream(const uint16_t *p)
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
-__device__ __forceinline__ float wave_sum(float v)
-{
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1)
-        v += __shfl_xor(v, m, 64);
-    return v;
-}
+// lanes' partial sums added with DPP row steps and lane swaps (route_token.h)
+__device__ __forceinline__ float wave_sum(float v) { return rt::wave_sum(v, threadIdx.x & 63); }
 
 // Base of matrix m (0 W1, 1 W3, 2 W2) of expert e: a pool page, a load-buffer
 // slot (W1, W3, W2 back to back), or the contiguous arrays.
@@ -193,15 +188,16 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_dec_gate_up(const FwdArgs a)
 // code), marks the chosen experts in an LDS bitmap, and takes as its expert
 // the blockIdx.y-th chosen one in ascending id order -- the expert of aligned
 // block blockIdx.y, since with at most T <= block_m picks per expert every
-// expert fills one block.  Workgroup (0, 0) also writes the routing outputs
-// (topk ids and weights, which the down pass reads, and the aligned order, the
-// block map and num_padded, as the routing kernels would).
+// expert fills one block.  Only the ids stand before the first weight load;
+// workgroup (0, 0) computes the routing weights at its end and writes the
+// routing outputs (topk ids and weights and the aligned order, the block map
+// and num_padded, as the routing kernels would), and with them the W2 base of
+// every pick, so that the down pass starts its W2 rows after one load.
 template <bool PAGED, int NCH, int NV, int RPW>
 __global__ __launch_bounds__(64 * kDecWaves) void k_dec_route_gate_up(const FwdArgs a, const DecRouteArgs ra)
 {
     constexpr int kWords = kMaxExpertsTotal / 32;
     __shared__ int32_t s_ids[kDecMaxT * kDecMaxKeff];
-    __shared__ float s_w[kDecMaxT * kDecMaxKeff];
     __shared__ uint32_t s_bits[kWords];
     __shared__ int s_pre[kWords + 1]; // exclusive prefix popcounts of s_bits, s_pre[nwords] = experts chosen
     __shared__ int s_e;
@@ -224,11 +220,13 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_dec_route_gate_up(const FwdA
             rt::load_logits<NV>(ra.logits + (int64_t)t * ra.E, ra.E, lane, v[q]);
     }
     __syncthreads(); // the bitmap is cleared
+    float pv[TPW]; // the logit of pick `lane` of each routed token (for the weights)
 #pragma unroll
     for (int q = 0; q < TPW; q++) {
         const int t = wave + q * kDecWaves;
+        pv[q] = 0.f;
         if (t < T) {
-            rt::route_token<NV>(v[q], ra.E, ra.k, ra.S, lane, s_ids + t * keff, s_w + t * keff, nullptr);
+            pv[q] = rt::route_ids<NV>(v[q], ra.E, ra.k, ra.S, lane, s_ids + t * keff, nullptr);
             // lane j < k+S wrote pick j: mark its expert
             if (lane < keff) {
                 const int id = s_ids[t * keff + lane];
@@ -265,11 +263,19 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_dec_route_gate_up(const FwdA
         dec_gate_up_rows<PAGED, NCH, RPW>(a, e, n, [&](int i) { return s_ids[i] == e ? i : -1; });
     if (blockIdx.x != 0 || blockIdx.y != 0)
         return;
-    // the routing outputs, as the routing kernels write them
+    // the routing outputs, as the routing kernels write them, and the W2 base
+    // of every pick (the down pass reads its W2 rows from there)
     const int U = s_pre[nwords], BM = a.BM;
+#pragma unroll
+    for (int q = 0; q < TPW; q++) {
+        const int t = wave + q * kDecWaves;
+        if (t < T)
+            rt::route_weights(pv[q], ra.k, ra.S, lane, ra.topk_w + (int64_t)t * keff);
+    }
+    const uint16_t **w2b = (const uint16_t **)a.comb;
     for (int i = tid; i < n; i += NT) {
         ra.topk_ids[i] = s_ids[i];
-        ra.topk_w[i] = s_w[i];
+        w2b[i] = matrix_base<PAGED>(a, s_ids[i], 2);
     }
     for (int i = tid; i < U * BM; i += NT)
         ra.sorted_ids[i] = n;
@@ -296,10 +302,13 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_dec_route_gate_up(const FwdA
 }
 
 // grid: (d / CPG, T).  Wave w takes the token's picks w, w + 4,
-// ...: it issues the four W2 rows of its pick, reads the pick's h row (from
-// L2), and leaves w_tj * dot per column in LDS; after the one barrier the sums
-// over the picks are taken in slot order.
-template <bool PAGED, int NCH, int CPG>
+// ...: it issues the W2 rows of its pick, reads the pick's h row (from L2),
+// and leaves w_tj * dot per column in LDS; after the one barrier the sums over
+// the picks are taken in slot order.  ROUTED: the routing ran in the gate/up
+// launch, which left every pick's W2 base in the combine area of the
+// workspace (no combine buffer in this form); else the base is resolved from
+// the pick's expert id.
+template <bool PAGED, int NCH, int CPG, bool ROUTED>
 __global__ __launch_bounds__(64 * kDecWaves) void k_dec_down(const FwdArgs a)
 {
     __shared__ float res[kDecMaxKeff * CPG];
@@ -307,14 +316,20 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_dec_down(const FwdArgs a)
     const int c0 = (int)blockIdx.x * CPG;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     for (int j = wave; j < a.keff; j += kDecWaves) {
-        const int e = a.topk_ids[(int64_t)t * a.keff + j];
-        const float w = a.topk_w[(int64_t)t * a.keff + j];
+        const int64_t i = (int64_t)t * a.keff + j;
+        const uint16_t *w2;
+        if constexpr (ROUTED) {
+            w2 = ((const uint16_t *const *)a.comb)[i];
+        } else {
+            const int e = a.topk_ids[i];
+            w2 = (e >= 0 && e < a.E_tot) ? matrix_base<PAGED>(a, e, 2) : nullptr;
+        }
+        const float w = a.topk_w[i];
         float s[CPG];
 #pragma unroll
         for (int c = 0; c < CPG; c++)
             s[c] = 0.f;
-        if (e >= 0 && e < a.E_tot) {
-            const uint16_t *w2 = matrix_base<PAGED>(a, e, 2);
+        if (w2) {
             uint4 wv[CPG][NCH];
 #pragma unroll
             for (int c = 0; c < CPG; c++)
@@ -396,7 +411,10 @@ hipError_t launch_g(const FwdArgs &a, const DecRouteArgs *ra, hipStream_t s)
     launch_gate_up<PAGED, NCH_D, RPW>(a, ra, g1, s);
     mark(1);
     const dim3 g2((unsigned)(a.d / CPG), (unsigned)a.T);
-    k_dec_down<PAGED, NCH_F, CPG><<<g2, 64 * kDecWaves, 0, s>>>(a);
+    if (ra)
+        k_dec_down<PAGED, NCH_F, CPG, true><<<g2, 64 * kDecWaves, 0, s>>>(a);
+    else
+        k_dec_down<PAGED, NCH_F, CPG, false><<<g2, 64 * kDecWaves, 0, s>>>(a);
     mark(2);
     mark(3);
     return hipGetLastError();

@@ -42,6 +42,19 @@ __device__ __forceinline__ int xor32(int v, int lane)
     const auto r = __builtin_amdgcn_permlane32_swap((unsigned)v, (unsigned)v, false, false);
     return (int)(lane >= 32 ? r[0] : r[1]);
 }
+__device__ __forceinline__ float wave_sum(float x, int lane)
+{
+    const auto f = [](int v) { return __builtin_bit_cast(float, v); };
+    const auto i = [](float v) { return __builtin_bit_cast(int, v); };
+    x += f(dpp<kDppXor1>(i(x)));
+    x += f(dpp<kDppXor2>(i(x)));
+    x += f(dpp<kDppHalfMirror>(i(x)));
+    x += f(dpp<kDppMirror>(i(x)));
+    x += f(xor16(i(x), lane));
+    x += f(xor32(i(x), lane));
+    return x;
+}
+
 // Wave-wide fp64 sum, each exchange on the two 32-bit halves.
 template <int CTRL>
 __device__ __forceinline__ double dpp(double v)
@@ -159,15 +172,15 @@ __device__ __forceinline__ void sort_lane(int (&sk)[NV], int (&si)[NV])
             order_pair(sk[t], si[t], sk[t + 1], si[t + 1]);
 }
 
-// Route one token with one wave from its loaded logits.  Writes ids/w[0 .. k+S)
-// and, when lds_ids is not null, the ids into LDS as well.  Each lane sorts its
-// logits (lane, lane+64, ...) once into pick order; every pick is then the wave
-// maximum of the lanes' first entries, and among the lanes whose first entry
-// equals it the lowest expert id (the same order as comparing (logit, id)
-// pairs); the lane that holds it moves on to its next entry.
+// The k picks of one token with one wave from its loaded logits.  Writes
+// ids[0 .. k+S) (and, when lds_ids is not null, the same ids into LDS) and
+// returns, in lane j < k, the logit of pick j (for route_weights).  Each lane
+// sorts its logits (lane, lane+64, ...) once into pick order; every pick is
+// then the wave maximum of the lanes' first entries, and among the lanes whose
+// first entry equals it the lowest expert id (the same order as comparing
+// (logit, id) pairs); the lane that holds it moves on to its next entry.
 template <int NV>
-__device__ void route_token(const float (&v)[NV], int E, int k, int S, int lane, int32_t *ids, float *w,
-                            int32_t *lds_ids)
+__device__ float route_ids(const float (&v)[NV], int E, int k, int S, int lane, int32_t *ids, int32_t *lds_ids)
 {
     constexpr int kNone = 0x7fffffff, kEmpty = (int)0x80000000; // id / key of a lane's used-up entries
     int sk[NV], si[NV];
@@ -198,26 +211,42 @@ __device__ void route_token(const float (&v)[NV], int E, int k, int S, int lane,
         sk[NV - 1] ^= (sk[NV - 1] ^ kEmpty) & msk;
         si[NV - 1] ^= (si[NV - 1] ^ kNone) & msk;
     }
-    // The weights in fp64, rounded once to fp32: the difference of two fp32
-    // logits is exact in fp64, so exp of it keeps its relative accuracy at any
-    // logit gap (in fp32 the rounding of l_j - l_0 alone is |l_j - l_0| * 2^-24
-    // relative after exp, 3e-6 at a gap of 50).
-    const float my_v = key_value(my_k);
-    const float lmax = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, my_v)));
-    const double ex = lane < k ? exp((double)my_v - (double)lmax) : 0.0;
-    const double sum = wave_sum(ex, lane); // commutative pairs: every lane ends with the same sum
     if (lane < k) {
         ids[lane] = my_id;
-        w[lane] = (float)(ex / sum);
         if (lds_ids)
             lds_ids[lane] = my_id;
     }
     if (S && lane == k) {
         ids[k] = E;
-        w[k] = 1.f;
         if (lds_ids)
             lds_ids[k] = E;
     }
+    return key_value(my_k);
+}
+
+// The routing weights of one token from route_ids' per-lane pick logits:
+// w[j] = exp(l_j - l_0) / sum_i exp(l_i - l_0) over the k picks, and 1 for
+// the shared expert (pick k).  Computed in fp64, rounded once to fp32: the
+// difference of two fp32 logits is exact in fp64, so exp of it keeps its
+// relative accuracy at any logit gap (in fp32 the rounding of l_j - l_0 alone
+// is |l_j - l_0| * 2^-24 relative after exp, 3e-6 at a gap of 50).
+__device__ __forceinline__ void route_weights(float my_v, int k, int S, int lane, float *w)
+{
+    const float lmax = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, my_v)));
+    const double ex = lane < k ? exp((double)my_v - (double)lmax) : 0.0;
+    const double sum = wave_sum(ex, lane); // commutative pairs: every lane ends with the same sum
+    if (lane < k)
+        w[lane] = (float)(ex / sum);
+    if (S && lane == k)
+        w[k] = 1.f;
+}
+
+// Route one token: ids and weights.
+template <int NV>
+__device__ void route_token(const float (&v)[NV], int E, int k, int S, int lane, int32_t *ids, float *w,
+                            int32_t *lds_ids)
+{
+    route_weights(route_ids<NV>(v, E, k, S, lane, ids, lds_ids), k, S, lane, w);
 }
 
 } // namespace rt
