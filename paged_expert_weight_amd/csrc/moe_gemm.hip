@@ -913,6 +913,15 @@ using Tiles128 = Tiles<128, Gemm<128, 64, 2, 2, 1, 64, 2, true>, Gemm<128, 128, 
 using Down128w = Gemm<128, 256, 2, 4, 1, 64, 3, false>;
 using Tiles128w = Tiles<128, Gemm<128, 256, 2, 4, 1, 64, 2, true>, Down128w>;
 using Tiles128d = Tiles<128, Gemm<128, 64, 2, 2, 1, 64, 2, true>, Down128w>;
+// batches of many 128-row blocks with d a multiple of 512: 512-column down
+// tiles (8 waves of 64x128, two stages fill the 160 KB of LDS), so a block's h
+// rows are re-read by half as many column tiles (Qwen3-Next-shaped down GEMM
+// 400 -> 376 us); with few blocks the halved tile count leaves CUs idle (a
+// 1024-token Qwen1.5-shaped layer: 69 -> 70 us), hence kWideDownTiles
+using Down128x = Gemm<128, 512, 2, 4, 1, 64, 2, false>;
+using Tiles128wx = Tiles<128, Gemm<128, 256, 2, 4, 1, 64, 2, true>, Down128x>;
+using Tiles128dx = Tiles<128, Gemm<128, 64, 2, 2, 1, 64, 2, true>, Down128x>;
+constexpr int64_t kWideDownTiles = 1024; // 512-column down tiles from this many on (at most blocks x d / 512)
 // when d is not a multiple of 128 (d and f are multiples of 64)
 using Tiles128n = Tiles<128, Gemm<128, 64, 2, 2, 1, 64, 2, true>, Gemm<128, 64, 2, 2, 1, 64, 2, false>>;
 // large blocks (MFMA-bound shapes): 8 waves, two per SIMD, each with a 64x128
@@ -1037,6 +1046,14 @@ hipError_t launch_paged(const FwdArgs &a, hipStream_t s)
     case 32: return launch_tiles<Tiles32, PAGED>(a, s);
     case 64: return a.d % 256 == 0 ? launch_tiles<Tiles64w, PAGED>(a, s) : launch_tiles<Tiles64, PAGED>(a, s);
     case 128:
+        if (a.d % 512 == 0) {
+            // the most blocks the batch can produce (as the launch grid counts them)
+            const int64_t n = a.T * a.keff;
+            int64_t blocks = n / 128 + (n < a.E_tot ? n : a.E_tot);
+            blocks = blocks < a.blocks_cap ? blocks : a.blocks_cap;
+            if (blocks * (a.d / 512) >= kWideDownTiles)
+                return a.f % 256 == 0 ? launch_tiles<Tiles128wx, PAGED>(a, s) : launch_tiles<Tiles128dx, PAGED>(a, s);
+        }
         if (a.d % 256 == 0)
             return a.f % 256 == 0 ? launch_tiles<Tiles128w, PAGED>(a, s) : launch_tiles<Tiles128d, PAGED>(a, s);
         return a.d % 128 == 0 ? launch_tiles<Tiles128, PAGED>(a, s) : launch_tiles<Tiles128n, PAGED>(a, s);

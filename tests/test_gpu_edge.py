@@ -2,7 +2,8 @@
 oracle: one expert with k = 1, k = E, every token on one expert (one expert
 owning many blocks at every tile height), the smallest shapes (d = f = 64, and
 d not a multiple of 128), a ragged token count, a shared expert beside two
-routed ones, and the largest expert count (E + S = 1024).  Routing ids,
+routed ones, the largest expert count (E + S = 1024), and a batch with enough
+128-row blocks for the 512-column down tiles.  Routing ids,
 aligned order and block map are compared bit for bit, y within the bar, and
 paged against contiguous weights bit for bit."""
 import dataclasses
@@ -39,6 +40,10 @@ EDGE = {
                          loadbuf_experts=(13, 14, 15), loadbuf_slots=4, seed=4005),
     "max_experts": _spec("max_experts", T=40, d=64, f=64, E=1023, k=8, S=1, pool_pages=3 * 1024 + 8,
                          loadbuf_experts=tuple(range(1000, 1023)), loadbuf_slots=24, seed=4006),
+    # enough 128-row blocks (1800 picks over 1024 experts: up to 1038 blocks) for the 512-column down
+    # tiles, with f not a multiple of 256 (64-column gate/up tiles beside them)
+    "wide_down": _spec("wide_down", T=600, d=512, f=192, E=1023, k=2, S=1, pool_pages=3 * 1024 + 5,
+                       loadbuf_experts=tuple(range(1010, 1023)), loadbuf_slots=16, seed=4009),
 }
 
 
