@@ -38,10 +38,12 @@ HBM_PEAK_GBS = 8000.0
 # 1 GiB copy reads back, plus WRITE_SIZE), keyed by workload, T, block_m, atomic combine and a
 # hash of the GEMM sources the counters were taken on.  Reported only while that hash matches.
 MEASURED_TRAFFIC = {
-    ("qwen15", 1024, 128, False, "1c636e3b22c34cd4"): 718566434,
-    ("qwen3n", 8192, 128, False, "1c636e3b22c34cd4"): 2788758883,
-    ("decode", 1, 16, False, "1c636e3b22c34cd4"): 46282238,
-    ("mixtral", 4096, 256, False, "1c636e3b22c34cd4"): 4069161737,
+    ("mixtral", 4096, 256, False, "ece14ea5c65134b8"): 4270166254,
+    ("qwen15", 1024, 128, False, "ece14ea5c65134b8"): 718582685,
+    ("qwen3n", 8192, 128, False, "ece14ea5c65134b8"): 2791154133,
+    ("decode", 1, 16, False, "ece14ea5c65134b8"): 46328330,
+    ("decode", 8, 16, False, "ece14ea5c65134b8"): 300421914,
+    ("decode", 32, 16, False, "ece14ea5c65134b8"): 577650526,
 }
 GEMM_SOURCES = ("paged_expert_weight_amd/csrc/moe_gemm.hip", "paged_expert_weight_amd/csrc/decode.hip",
                 "paged_expert_weight_amd/csrc/internal.h")
@@ -468,6 +470,8 @@ def bench_layer(layer, args, full):
     per_step = np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
     spread = {q: round(float(np.percentile(per_step, p)), 2) for q, p in (("p10", 10), ("p50", 50), ("p90", 90))}
     extra = {"step_us_spread": spread, "loadbuf": loadbuf, "adjuster": adjuster_timing(s.E)}
+    if roof["bound"] == "mfma":
+        extra["dense_library_gemm"] = dense_library_gemm(int(rt.num_padded.item()), s.d, s.f)
     for c in copies:
         c["h"].close()
         c["h_same"].close()
@@ -927,6 +931,36 @@ def pipeline_bench(args):
     pipe.close()
     for h in hs:
         h.close()
+
+
+def dense_library_gemm(rows: int, d: int, f: int, reps: int = 10):
+    """Context for the MFMA fraction of the grouped GEMMs: the vendor library's dense bf16 GEMM
+    (torch.matmul, hipBLASLt on ROCm) on the same executed shapes, all padded rows of the aligned
+    order as one dense matrix: gate/up [rows, d] x [d, 2f], down [rows, f] x [f, d]."""
+    import torch
+    g = torch.Generator(device="cuda").manual_seed(0)
+    out = {"rows": rows}
+    for name, (m, k, n) in (("gate_up", (rows, d, 2 * f)), ("down", (rows, f, d))):
+        a = torch.randn(m, k, device="cuda", dtype=torch.bfloat16, generator=g)
+        b = torch.randn(k, n, device="cuda", dtype=torch.bfloat16, generator=g).contiguous()
+        c = torch.empty(m, n, device="cuda", dtype=torch.bfloat16)
+        for _ in range(3):
+            torch.matmul(a, b, out=c)
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            torch.matmul(a, b, out=c)
+            e1.record()
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        ms = sorted(ts)[len(ts) // 2]
+        out[f"{name}_us"] = round(ms * 1e3, 1)
+        out[f"{name}_mfma_frac"] = round(2.0 * m * k * n / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)
+        del a, b, c
+    torch.cuda.empty_cache()
+    return out
 
 
 def adjuster_timing(E: int, layers: int = 48, rounds: int = 2000):
