@@ -21,11 +21,13 @@
 //   combine:  y[t] = bf16( sum_j comb[t*(k+S)+j] ), j ascending.
 //
 // Operands are K-contiguous on both sides (x rows and weight rows run along d;
-// h rows and W2 rows run along f).  Each K-step of 32 moves 64-byte row
-// segments from HBM straight into LDS (buffer_load_dwordx4 ... lds, no VGPR
-// round trip), into one of S LDS stages, so S-1 K-steps are in flight while one
-// is multiplied; v_mfma_f32_16x16x32_bf16 reads its operands from LDS with one
-// 16-byte read per lane, XOR-swizzled so 8 rows never share a bank group.
+// h rows and W2 rows run along f).  Each K-step (64 elements for most tiles)
+// moves 128-byte row segments from HBM straight into LDS
+// (buffer_load_dwordx4 ... lds, no VGPR round trip): the A rows into one of S
+// stages of their ring and the B rows into one of SB >= S stages of theirs, so
+// S-1 (SB-1) K-steps of A (B) rows are in flight while one is multiplied;
+// v_mfma_f32_16x16x32_bf16 reads its operands from LDS with one 16-byte read
+// per lane, XOR-swizzled so 8 rows never share a bank group.
 #include "internal.h"
 
 #include <mutex>
@@ -311,7 +313,13 @@ __device__ __forceinline__ void wait_vm_lgkm0(Int<N>)
 // The K order of the accumulation (32-wide MFMA steps, lane group g holding k
 // 8g..8g+7 of each step) is the same for every tile shape, so the result of an
 // output element does not depend on BM, BN or the weight layout.
-template <int BM, int BN, int WAVES_M, int WAVES_N, int WK, int BK, int S, bool G1>
+constexpr int gcd_(int a, int b) { return b ? gcd_(b, a % b) : a; }
+
+// S stages of A rows and SB >= S stages of B rows: each operand has its own
+// ring of LDS buffers, and the B rows (the weights, whose misses go to HBM)
+// may be loaded further ahead than the A rows (x or h rows, mostly L2 or MALL
+// hits) when the LDS holds more B stages than A stages.
+template <int BM, int BN, int WAVES_M, int WAVES_N, int WK, int BK, int S, bool G1, int SB = S>
 struct Gemm {
     using Geo = StageGeom<BK>;
     // WAVES_M x WAVES_N waves share one tile; with WK > 1 (one wave per tile)
@@ -326,53 +334,81 @@ struct Gemm {
     static constexpr int B_ROWS = G1 ? 2 * BN : BN;
     static constexpr int ROWS = BM + B_ROWS;
     static_assert(ROWS % (Geo::ROWS_PER_LD * NT) == 0, "DMA instructions must split evenly over the waves");
-    static constexpr int IPW = ROWS / Geo::ROWS_PER_LD / NT; // DMA instructions per wave per stage
+    static constexpr int IPW = ROWS / Geo::ROWS_PER_LD / NT; // DMA instructions per wave per K-step
+    static constexpr int IA = BM / Geo::ROWS_PER_LD / NT;    // of which A rows (the first IA)
+    static constexpr int IB = IPW - IA;
+    static_assert(IA * Geo::ROWS_PER_LD * NT == BM, "A rows split evenly over the waves");
     static_assert(BM % Geo::ROWS_PER_LD == 0 && BN % Geo::ROWS_PER_LD == 0, "sections");
-    static constexpr int STAGE_BYTES = ROWS * Geo::ROWB;
-    static constexpr int LDS_BYTES = WK * S * STAGE_BYTES;
-    static_assert(S >= 2 && S <= 8 && (S - 2) * IPW < 64, "stages");
+    // K-steps of lookahead of the two rings, and the loop period (both ring
+    // positions are compile-time constants inside one period)
+    static constexpr int LA = S - 1, LB = SB - 1, P = S * SB / gcd_(S, SB);
+    static constexpr int A_BYTES = BM * Geo::ROWB, B_BYTES = B_ROWS * Geo::ROWB;
+    static constexpr int RING_BYTES = S * A_BYTES + SB * B_BYTES; // per K range
+    static constexpr int LDS_BYTES = WK * RING_BYTES;
+    // this wave's DMA instructions issued after the A rows of the K-step awaited at
+    // a step's top (everything later in the stream may stay in flight): the B rows of
+    // the step that issued it, when B runs further ahead, and LA - 1 whole steps
+    static constexpr int N_AFTER = (LB > LA ? IB : 0) + (LA - 1) * IPW;
+    static_assert(S >= 2 && SB >= S && SB <= 8 && N_AFTER < 64, "stages");
     static constexpr int BM_ = BM, BN_ = BN, WK_ = WK, WAVES_N_ = WAVES_N;
 
     __amdgpu_buffer_rsrc_t ra, rb0, rb1;
     uint32_t voff[IPW];
     int wave, wt, kg, wm, wn, l16, lg;
-    uint8_t *lds; // WK x S stages of STAGE_BYTES, one workgroup-scope array
+    uint8_t *lds; // WK rings (S A stages, then SB B stages), one workgroup-scope array
     f32x4 acc0[FM][FN], acc1[FM][FN];
 
-    // Stage J at a constant offset: the waits on the DMA into one stage then
+    // Stages at constant offsets: the waits on the DMA into one stage then
     // never cover the LDS reads of another.
     template <int J>
-    __device__ __forceinline__ uint8_t *stage() const
+    __device__ __forceinline__ uint8_t *a_stage() const
     {
         static_assert(J < S, "stage");
-        return lds + (kg * S + J) * STAGE_BYTES;
+        return lds + kg * RING_BYTES + J * A_BYTES;
+    }
+    template <int J>
+    __device__ __forceinline__ uint8_t *b_stage() const
+    {
+        static_assert(J < SB, "stage");
+        return lds + kg * RING_BYTES + S * A_BYTES + J * B_BYTES;
     }
 
-    // DMA of K-step kt into stage J: instruction i of this wave reads section
-    // 0 (A), 1 (B gate / W2) or 2 (B up); STREAM: the B rows non-temporally.
-    template <int J, bool STREAM>
-    __device__ __forceinline__ void issue(int kt)
+    // DMA of the A rows of K-step kt into A stage J (this wave's instructions i < IA)
+    template <int J>
+    __device__ __forceinline__ void issue_a(int kt)
     {
-        uint8_t *slot = stage<J>();
+        uint8_t *slot = a_stage<J>();
         const int soff = kt * BK * 2;
 #pragma unroll
-        for (int i = 0; i < IPW; i++) {
+        for (int i = 0; i < IA; i++) {
             const int q = wt + NT * i;
-            const int row0 = q * Geo::ROWS_PER_LD;
             auto *dst = (__attribute__((address_space(3))) void *)(slot + q * 1024);
-            if (row0 < BM)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, dst, 16, voff[i], soff, 0, kDmaPlain);
-            else if (!G1 || row0 - BM < BN)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, dst, 16, voff[i], soff, 0, kDmaPlain);
+        }
+    }
+
+    // DMA of the B rows of K-step kt into B stage J (instructions i >= IA): the
+    // W1 / W2 rows, then the W3 rows; STREAM: non-temporally.
+    template <int J, bool STREAM>
+    __device__ __forceinline__ void issue_b(int kt)
+    {
+        uint8_t *slot = b_stage<J>();
+        const int soff = kt * BK * 2;
+#pragma unroll
+        for (int i = IA; i < IPW; i++) {
+            const int q = wt + NT * i - BM / Geo::ROWS_PER_LD; // instruction within the B rows
+            auto *dst = (__attribute__((address_space(3))) void *)(slot + q * 1024);
+            if (!G1 || q * Geo::ROWS_PER_LD < BN)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rb0, dst, 16, voff[i], soff, 0, STREAM ? kDmaStream : kDmaPlain);
             else
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rb1, dst, 16, voff[i], soff, 0, STREAM ? kDmaStream : kDmaPlain);
         }
     }
 
-    template <int J>
+    template <int JA, int JB>
     __device__ __forceinline__ void compute()
     {
-        const uint8_t *sp = stage<J>();
+        const uint8_t *sa = a_stage<JA>(), *sb = b_stage<JB>();
 #pragma unroll
         for (int sub = 0; sub < BK / 32; sub++) {
             const int chunk = 4 * sub + lg;
@@ -380,15 +416,16 @@ struct Gemm {
 #pragma unroll
             for (int i = 0; i < FM; i++) {
                 const int row = wm * WM + 16 * i + l16;
-                af[i] = *(const bf16x8 *)(sp + row * Geo::ROWB + ((chunk ^ Geo::swz(row)) * 16));
+                af[i] = *(const bf16x8 *)(sa + row * Geo::ROWB + ((chunk ^ Geo::swz(row)) * 16));
             }
 #pragma unroll
             for (int j = 0; j < FN; j++) {
-                const int row = BM + wn * WN + 16 * j + l16;
-                b0[j] = *(const bf16x8 *)(sp + row * Geo::ROWB + ((chunk ^ Geo::swz(row)) * 16));
+                // B row r of the stage (row BM + r of the rows the swizzle counts)
+                const int r = wn * WN + 16 * j + l16;
+                b0[j] = *(const bf16x8 *)(sb + r * Geo::ROWB + ((chunk ^ Geo::swz(BM + r)) * 16));
                 if constexpr (G1) {
-                    const int row1 = row + BN;
-                    b1[j] = *(const bf16x8 *)(sp + row1 * Geo::ROWB + ((chunk ^ Geo::swz(row1)) * 16));
+                    const int r1 = r + BN;
+                    b1[j] = *(const bf16x8 *)(sb + r1 * Geo::ROWB + ((chunk ^ Geo::swz(BM + r1)) * 16));
                 }
             }
 #pragma unroll
@@ -402,44 +439,52 @@ struct Gemm {
         }
     }
 
-    template <int J, bool STREAM>
+    // The loads before the first K-step, in the order the steady state issues
+    // them (step s issues A(s + LA), then B(s + LB)), for virtual steps
+    // s = kb - LB .. kb - 1: the waits count on that order.
+    template <int V, bool STREAM>
     __device__ __forceinline__ void prologue(int kb, int ke)
     {
-        if constexpr (J < S - 1) {
-            if (kb + J < ke)
-                this->template issue<J, STREAM>(kb + J);
-            this->template prologue<J + 1, STREAM>(kb, ke);
+        if constexpr (V < LB) {
+            constexpr int a = V - LB + LA; // A(kb + a), at A position a
+            if constexpr (a >= 0)
+                if (kb + a < ke)
+                    this->template issue_a<a % S>(kb + a);
+            if (kb + V < ke)
+                this->template issue_b<V % SB, STREAM>(kb + V);
+            this->template prologue<V + 1, STREAM>(kb, ke);
         }
     }
 
-    // one pass over the S stages: K-steps kt0 .. kt0+S-1 (of the range ending at ke)
+    // one loop period: K-steps kt0 .. kt0+P-1 (of the range ending at ke)
     template <int J, bool STREAM>
     __device__ __forceinline__ void steps(int kt0, int ke)
     {
-        if constexpr (J < S) {
+        if constexpr (J < P) {
             const int kt = kt0 + J;
-            // stage kt has landed for this wave and this wave's reads of the
-            // stage about to be refilled are done; then the same for every
+            // K-step kt has landed for this wave and this wave's reads of the
+            // stages about to be refilled are done; then the same for every
             // wave that shares the stages.  Only steps inside [kb, ke) are
-            // loaded, so near the end fewer later stages are in flight and
-            // the wait drains them all.
-            if (kt + S - 2 < ke)
-                wait_vm_lgkm0(Int<(S - 2) * IPW>{});
+            // loaded, so near the end fewer later loads are in flight and the
+            // wait drains them all.
+            if (kt + LB - 1 < ke)
+                wait_vm_lgkm0(Int<N_AFTER>{});
             else
                 wait_vm_lgkm0(Int<0>{});
             if constexpr (NT > 1)
                 __builtin_amdgcn_s_barrier();
-            constexpr int NEXT = (J + S - 1) % S;
-            if (kt + S - 1 < ke)
-                this->template issue<NEXT, STREAM>(kt + S - 1);
+            if (kt + LA < ke)
+                this->template issue_a<(J + LA) % S>(kt + LA);
+            if (kt + LB < ke)
+                this->template issue_b<(J + LB) % SB, STREAM>(kt + LB);
             if (kt < ke)
-                this->template compute<J>();
+                this->template compute<J % S, J % SB>();
             this->template steps<J + 1, STREAM>(kt0, ke);
         }
     }
 
-    // K-steps [kb, ke): begin() issues the first S-1 stages, then the caller
-    // may issue loads of its own, then run() does the rest.
+    // K-steps [kb, ke): begin() issues the loads ahead of the first step, then
+    // the caller may issue loads of its own, then run() does the rest.
     template <bool STREAM>
     __device__ __forceinline__ void begin(int kb, int ke)
     {
@@ -456,7 +501,7 @@ struct Gemm {
                 acc0[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
                 acc1[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
             }
-        for (int kt0 = kb; kt0 < ke; kt0 += S)
+        for (int kt0 = kb; kt0 < ke; kt0 += P)
             this->template steps<0, STREAM>(kt0, ke);
         wait_vm_lgkm0(Int<0>{}); // no DMA may still be writing this workgroup's LDS when it exits
     }
@@ -513,8 +558,7 @@ __device__ __forceinline__ void gemm_tile(const FwdArgs &a, G &g, int b, int nt,
     constexpr int BK = G::Geo::ROWB / 2;
     using Geo = typename G::Geo;
     // DMA instructions i < IA of a wave stage A rows, the others B rows
-    constexpr int IA = BM / Geo::ROWS_PER_LD / G::NT;
-    static_assert(IA * Geo::ROWS_PER_LD * G::NT == BM, "A rows split evenly over the waves");
+    constexpr int IA = G::IA;
     const int lane = threadIdx.x & 63;
     const int lrow = lane / Geo::CH, lpos = lane % Geo::CH;
     // The tile's first loads are issued together so that their latencies
@@ -905,14 +949,18 @@ using Tiles64 = Tiles<64, Gemm<64, 64, 2, 2, 1, 64, 2, true>, Gemm<64, 64, 2, 2,
 // block's h rows are re-read by 4x fewer column tiles; 63 against 77 us for the
 // down GEMM of a 512-token Qwen1.5-shaped layer)
 using Tiles64w = Tiles<64, Gemm<64, 64, 2, 2, 1, 64, 2, true>, Gemm<64, 256, 2, 4, 1, 64, 2, false>>;
-using Tiles128 = Tiles<128, Gemm<128, 64, 2, 2, 1, 64, 2, true>, Gemm<128, 128, 2, 2, 1, 64, 2, false>>;
+// 128 x 64 gate/up tiles hold three stages of weight rows beside two of x rows
+// (80 KB of LDS, two workgroups per CU): the weight rows are loaded two K-steps
+// ahead (a 1024-token Qwen1.5-shaped gate/up GEMM 153 -> 149 us)
+using Gate128 = Gemm<128, 64, 2, 2, 1, 64, 2, true, 3>;
+using Tiles128 = Tiles<128, Gate128, Gemm<128, 128, 2, 2, 1, 64, 2, false>>;
 // 128-row blocks of layers with many small experts (a block's x or h rows are
 // re-read once per column tile): 256-column tiles, 8 waves of 64x64
 // accumulators (gate/up: 64 x (64 gate + 64 up)); the gate/up stages fill all
 // 160 KB of LDS, the down GEMM's short K loop (K = f) keeps three stages.
 using Down128w = Gemm<128, 256, 2, 4, 1, 64, 3, false>;
 using Tiles128w = Tiles<128, Gemm<128, 256, 2, 4, 1, 64, 2, true>, Down128w>;
-using Tiles128d = Tiles<128, Gemm<128, 64, 2, 2, 1, 64, 2, true>, Down128w>;
+using Tiles128d = Tiles<128, Gate128, Down128w>;
 // batches of many 128-row blocks with d a multiple of 512: 512-column down
 // tiles (8 waves of 64x128, two stages fill the 160 KB of LDS), so a block's h
 // rows are re-read by half as many column tiles (Qwen3-Next-shaped down GEMM
@@ -920,10 +968,10 @@ using Tiles128d = Tiles<128, Gemm<128, 64, 2, 2, 1, 64, 2, true>, Down128w>;
 // 1024-token Qwen1.5-shaped layer: 69 -> 70 us), hence kWideDownTiles
 using Down128x = Gemm<128, 512, 2, 4, 1, 64, 2, false>;
 using Tiles128wx = Tiles<128, Gemm<128, 256, 2, 4, 1, 64, 2, true>, Down128x>;
-using Tiles128dx = Tiles<128, Gemm<128, 64, 2, 2, 1, 64, 2, true>, Down128x>;
+using Tiles128dx = Tiles<128, Gate128, Down128x>;
 constexpr int64_t kWideDownTiles = 1024; // 512-column down tiles from this many on (at most blocks x d / 512)
 // when d is not a multiple of 128 (d and f are multiples of 64)
-using Tiles128n = Tiles<128, Gemm<128, 64, 2, 2, 1, 64, 2, true>, Gemm<128, 64, 2, 2, 1, 64, 2, false>>;
+using Tiles128n = Tiles<128, Gate128, Gemm<128, 64, 2, 2, 1, 64, 2, false>>;
 // large blocks (MFMA-bound shapes): 8 waves, two per SIMD, each with a 64x128
 // accumulator tile (gate/up: 64 x (64 gate + 64 up)); 256x256 down tiles.  K
 // steps of 64: every staged row is a 128-byte segment, which L2 feeds into LDS
