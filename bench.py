@@ -177,9 +177,9 @@ def main():
 
 
 # The configurations every default run times besides the headline one (the decode sweep
-# as one entry per batch size).
-ALL_CONFIGS = (("tiny", 16), ("qwen15", 1024), ("decode", 1), ("decode", 8), ("decode", 32), ("decode", 128),
-               ("decode", 512), ("mixtral", 4096), ("qwen3n", 8192))
+# as one entry per batch size, with 2 and 4 tokens beside the sweep's 1, 8, 32, 128, 512).
+ALL_CONFIGS = (("tiny", 16), ("qwen15", 1024), ("decode", 1), ("decode", 2), ("decode", 4), ("decode", 8),
+               ("decode", 32), ("decode", 128), ("decode", 512), ("mixtral", 4096), ("qwen3n", 8192))
 _HOST_LAYERS = {}
 
 
