@@ -90,6 +90,7 @@ def parse():
     ap.add_argument("--rotate", type=int, default=0, help="layer copies to rotate over (default: automatic)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-contig", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="skip the graph-replayed steps of the small batches")
     ap.add_argument("--no-fill", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target seconds of oracle work")
     ap.add_argument("--pipeline", action="store_true",
@@ -276,16 +277,17 @@ def bench_layer(layer, args, full):
     # One step = routing + the layer, in one call (for a decode step the routing runs inside the gate/up
     # launch).  The load buffer is refilled only by the concurrent-fill measurement (buffer 1): the
     # "buffer read" mark of buffer 0 is deferred to its next fill instead of a stream marker per step.
-    def step(i, mode="paged"):
+    def step(i, mode="paged", st=None):
         c = copies[i % R]
+        st = stream if st is None else st
         if mode == "contiguous":
             pm.moe_route_contiguous_forward(c["h"], c["w13"], c["w2"], dev.logits, dev.x, bm, rt.topk_ids,
                                             rt.topk_w, rt.sorted_ids, rt.block_expert, rt.num_padded, y, ws, flags,
-                                            stream)
+                                            st)
         else:
             pm.moe_route_forward(c["h_same" if mode == "paged_same" else "h"], dev.logits, dev.x, bm, rt.topk_ids,
                                  rt.topk_w, rt.sorted_ids, rt.block_expert, rt.num_padded, 0, y, ws,
-                                 flags | pm.MOE_FLAG_DEFER_READ_DONE, stream)
+                                 flags | pm.MOE_FLAG_DEFER_READ_DONE, st)
 
     def timed(K, W, mode="paged"):
         for i in range(W):
@@ -322,6 +324,16 @@ def bench_layer(layer, args, full):
     # ---- the timed region (paged)
     ms = timed(K, W)
     print(f"# {name} T={T}: paged {ms * 1e3:.1f} us/step", file=sys.stderr, flush=True)
+
+    # ---- the same steps captured in a HIP graph and replayed (what a serving loop that captures its
+    # layers sees): the stream-launched figure above includes the host launch path and the gaps between
+    # launches, the replayed one the kernels and the command processor's dispatch only.  The step
+    # launches kernels only (the load buffer's fill is complete, its read mark deferred).
+    graph = None
+    if T <= GRAPH_MAX_T and not args.no_graph:
+        graph = graph_timed(step, R, K, W, stream)
+        print(f"# {name} T={T}: paged, graph replay {graph['paged'] * 1e3:.1f} us/step, contiguous "
+              f"{graph['contiguous'] * 1e3:.1f}", file=sys.stderr, flush=True)
 
     ids = rt.topk_ids.cpu().numpy()
     n = T * s.k_eff
@@ -412,6 +424,14 @@ def bench_layer(layer, args, full):
         # the layer's pool (pages in the workload's order, load-buffer experts in the load buffer)
         # against the twin: the lookup plus where the weights lie in memory
         "pool_vs_contiguous_pct": round((paged_alt_ms / contig_ms - 1) * 100, 3) if contig_ms else None,
+        "graph_replay": None if graph is None else {
+            "us_per_step": round(graph["paged"] * 1e3, 2),
+            "tflops": round(flops / (graph["paged"] * 1e-3) / 1e12, 3),
+            "hbm_gbs": round(bytes_alg / (graph["paged"] * 1e-3) / 1e9, 1),
+            "hbm_frac": round(bytes_alg / (graph["paged"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "contig_us_per_step": round(graph["contiguous"] * 1e3, 2),
+            "pool_vs_contiguous_pct": round((graph["paged"] / graph["contiguous"] - 1) * 100, 3),
+            "steps_per_graph": graph["steps_per_graph"]},
         "stages_us": {"route_align": round(route_us, 2), "gate_up": round(stage_us[0], 2),
                       "down": round(stage_us[1], 2),
                       # the decode form combines inside its down launch: no stage of its own
@@ -931,6 +951,45 @@ def pipeline_bench(args):
     pipe.close()
     for h in hs:
         h.close()
+
+
+GRAPH_MAX_T = 512  # batches whose graph-replayed step is reported
+
+
+def graph_timed(step, R, K, W, stream):
+    """Per-step time of `step` captured in one HIP graph (a whole number of rotations of the layer
+    copies, about 20 steps) and replayed, for the paged path over the layer's pool and for the
+    contiguous twin, in alternating blocks of replays."""
+    import torch
+    G = R * max(1, math.ceil(20 / R))
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    graphs = {}
+    for mode in ("paged", "contiguous"):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side, capture_error_mode="relaxed"):
+            for i in range(G):
+                step(i, mode, side)
+        graphs[mode] = g
+    torch.cuda.synchronize()
+    reps = max(1, math.ceil(K / G))
+    out = {"paged": 0.0, "contiguous": 0.0, "steps_per_graph": G}
+    for rnd in range(3):
+        for mode in (("paged", "contiguous") if rnd % 2 == 0 else ("contiguous", "paged")):
+            g = graphs[mode]
+            for _ in range(max(1, math.ceil(W / G))):
+                g.replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            out[mode] += e0.elapsed_time(e1) / (reps * G) / 3
+    del graphs
+    torch.cuda.synchronize()
+    return out
 
 
 def dense_library_gemm(rows: int, d: int, f: int, reps: int = 10):

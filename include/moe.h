@@ -244,6 +244,15 @@ int moe_paged_forward(moe_pool *pool, const void *x, int64_t T, int32_t block_m,
  *   logits       device fp32 [T][E] router logits (finite values).
  *   topk_ids ... num_padded: out, as moe_route writes them.
  *   x, active_buf, y, workspace, flags: as moe_paged_forward.
+ * HIP graph capture: the call enqueues kernel launches only (no memset, no
+ * allocation, no copy) when stage timing is off, the table reads no load
+ * buffer or the active buffer's last fill has completed before the call, and
+ * MOE_FLAG_DEFER_READ_DONE is set; so enqueued on a capturing stream, it
+ * records the step, and replays of the graph recompute every output from the
+ * inputs at the same addresses (a fill-completion check is made at capture:
+ * capture in relaxed or thread-local mode).  A replay is outside the load
+ * buffer's fill / read events: the caller orders fills of the active buffer
+ * against replays.
  */
 int moe_route_forward(moe_pool *pool, const float *logits, const void *x, int64_t T, int32_t block_m,
                       int32_t *topk_ids, float *topk_w, int32_t *sorted_ids, int32_t *block_expert,
