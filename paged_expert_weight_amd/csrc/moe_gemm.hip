@@ -109,13 +109,31 @@ __device__ __forceinline__ const uint16_t *down_base(const FwdArgs &a, int e)
 
 // ---------------------------------------------------------------------------- tile order
 // Workgroups are dispatched round-robin over the 8 XCDs (workgroup i runs on
-// XCD i mod 8, each XCD with its own L2).  The grid is sized for the most
-// blocks the routing can produce, but only num_padded / BM blocks exist, so
-// the logical tiles u of the existing blocks are dealt out first: XCD x walks
-// the contiguous range u in [x*per_xcd, (x+1)*per_xcd) and surplus workgroups
-// exit.  Tiles are grouped GM blocks at a time, column-tile major inside a
-// group: the GM blocks of a group reuse each weight tile from L2, and each
-// block's activation rows are reused across the group's column tiles.
+// XCD i mod 8, each XCD with its own L2), and inside an XCD to whichever CU
+// frees first.  The grid is sized for the most blocks the routing can produce,
+// but only num_padded / BM blocks exist, so the logical tiles u of the
+// existing blocks are dealt out first and surplus workgroups exit.  Up to
+// 128-row tiles, XCD x walks the contiguous range u in [x*per_xcd,
+// (x+1)*per_xcd).  The long 256-row tiles go to the XCDs in chunks of
+// kXcdChunk consecutive tiles, in turn: the k-th workgroup of XCD x takes tile
+// u = ((k / kXcdChunk) * 8 + x) * kXcdChunk + k mod kXcdChunk (their grid is
+// whole rounds of chunks), so the tiles an XCD runs at one time are still
+// neighbours in u, while every XCD works through the whole order; with
+// contiguous eighths the XCD whose tiles ran slowest was left alone at the
+// end (Mixtral-shaped step 2642 -> 2598 us; the shorter tiles of the other
+// shapes ran 1-8 % slower this way).  Tiles are grouped GM blocks at a time,
+// column-tile major inside a group: the GM blocks of a group reuse each weight
+// tile from L2, and each block's activation rows are reused across the
+// group's column tiles.
+constexpr int kXcdChunk = 32;
+constexpr int kXcdRound = 8 * kXcdChunk; // the grid of chunk-dealt tiles is a multiple of this
+
+__device__ __forceinline__ int chunk_tile(int i)
+{
+    const int x = i & 7, k = i >> 3;
+    return ((k / kXcdChunk) * 8 + x) * kXcdChunk + k % kXcdChunk;
+}
+
 struct TileSpace {
     int blocks, total, per_xcd; // blocks of BM rows, (block, column tile) pairs, pairs per XCD range
 };
@@ -220,15 +238,23 @@ __device__ __forceinline__ BlockInfo tile_pick(const FwdArgs &a, const TileSpace
     }
 }
 
-// One tile per workgroup: workgroup i takes tile (i mod 8) * per_xcd + i / 8.
-template <int GM, bool ALIGNED>
+// One tile per workgroup: workgroup i takes tile (i mod 8) * per_xcd + i / 8,
+// or chunk_tile(i) (CHUNKED: the 256-row tiles).
+template <int GM, bool ALIGNED, bool CHUNKED>
 __device__ __forceinline__ bool tile_of(const FwdArgs &a, int BM, int ntiles, int &b, int &nt, BlockInfo &bi,
                                         int &nblocks)
 {
     const TileSpace t = tile_space(a, BM, ntiles);
     nblocks = t.blocks;
-    const int u = (int)(blockIdx.x % 8) * t.per_xcd + (int)(blockIdx.x / 8);
-    if ((int)(blockIdx.x / 8) >= t.per_xcd || u >= t.total)
+    int u;
+    if constexpr (CHUNKED) {
+        u = chunk_tile((int)blockIdx.x);
+    } else {
+        u = (int)(blockIdx.x % 8) * t.per_xcd + (int)(blockIdx.x / 8);
+        if ((int)(blockIdx.x / 8) >= t.per_xcd)
+            return false;
+    }
+    if (u >= t.total)
         return false;
     bi = tile_pick<GM, ALIGNED>(a, t, ntiles, u, b, nt);
     return true;
@@ -753,8 +779,10 @@ __global__ __launch_bounds__(64 * G::NW) void k_gemm(const FwdArgs a)
         const TailPlan tp = tail_plan(ts, a.slots[G1 ? 0 : 1]);
         if (tp.tail > 0) {
             const int i = (int)blockIdx.x;
-            if (i < tp.full) { // whole tiles, dealt to the XCDs as in tile_of (full is a multiple of 8)
-                const BlockInfo bi = tile_pick<GM, TAIL>(a, ts, ntiles, (i & 7) * (tp.full >> 3) + (i >> 3), b, nt);
+            if (i < tp.full) { // whole tiles, dealt to the XCDs as in tile_of when full is whole rounds of
+                               // chunks, else in contiguous eighths (full is a multiple of 8)
+                const int u = tp.full % kXcdRound == 0 ? chunk_tile(i) : (i & 7) * (tp.full >> 3) + (i >> 3);
+                const BlockInfo bi = tile_pick<GM, TAIL>(a, ts, ntiles, u, b, nt);
                 gemm_tile<G, G1, PAGED, ATOMIC, TAIL>(a, g, b, nt, bi, ts.blocks);
             } else if (i - tp.full < tp.tail * tp.ks) {
                 const int v = i - tp.full;
@@ -768,7 +796,7 @@ __global__ __launch_bounds__(64 * G::NW) void k_gemm(const FwdArgs a)
     }
     BlockInfo bi;
     int nblocks;
-    if (!tile_of<GM, TAIL>(a, BM, ntiles, b, nt, bi, nblocks))
+    if (!tile_of<GM, TAIL, TAIL>(a, BM, ntiles, b, nt, bi, nblocks))
         return;
     gemm_tile<G, G1, PAGED, ATOMIC, TAIL>(a, g, b, nt, bi, nblocks);
 #endif
@@ -1052,7 +1080,11 @@ hipError_t launch_tiles_t(const FwdArgs &a_in, hipStream_t s)
         if (a.ev[i])
             (void)hipEventRecord(a.ev[i], s);
     };
-    auto grid = [&](int ntiles, int slots) { return (unsigned)((grid_m * ntiles + 7) / 8 * 8 + slots); };
+    // whole rounds of chunks for the chunk-dealt (TAIL) tiles, whole rounds of XCDs otherwise
+    constexpr int64_t kRound = TAIL ? kXcdRound : 8;
+    auto grid = [&](int ntiles, int slots) {
+        return (unsigned)((grid_m * ntiles + kRound - 1) / kRound * kRound + slots);
+    };
     if (ATOMIC) {
         const int64_t n4 = a.T * a.d / 4;
         k_zero<<<(unsigned)((n4 + 255) / 256), 256, 0, s>>>((float4 *)a.comb, n4);
