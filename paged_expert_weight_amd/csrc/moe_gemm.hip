@@ -112,26 +112,30 @@ __device__ __forceinline__ const uint16_t *down_base(const FwdArgs &a, int e)
 // XCD i mod 8, each XCD with its own L2), and inside an XCD to whichever CU
 // frees first.  The grid is sized for the most blocks the routing can produce,
 // but only num_padded / BM blocks exist, so the logical tiles u of the
-// existing blocks are dealt out first and surplus workgroups exit.  Up to
-// 128-row tiles, XCD x walks the contiguous range u in [x*per_xcd,
-// (x+1)*per_xcd).  The long 256-row tiles go to the XCDs in chunks of
-// kXcdChunk consecutive tiles, in turn: the k-th workgroup of XCD x takes tile
-// u = ((k / kXcdChunk) * 8 + x) * kXcdChunk + k mod kXcdChunk (their grid is
-// whole rounds of chunks), so the tiles an XCD runs at one time are still
-// neighbours in u, while every XCD works through the whole order; with
-// contiguous eighths the XCD whose tiles ran slowest was left alone at the
-// end (Mixtral-shaped step 2642 -> 2598 us; the shorter tiles of the other
-// shapes ran 1-8 % slower this way).  Tiles are grouped GM blocks at a time,
-// column-tile major inside a group: the GM blocks of a group reuse each weight
-// tile from L2, and each block's activation rows are reused across the
-// group's column tiles.
-constexpr int kXcdChunk = 32;
-constexpr int kXcdRound = 8 * kXcdChunk; // the grid of chunk-dealt tiles is a multiple of this
+// existing blocks are dealt out first and surplus workgroups exit.  Two ways
+// of dealing them, chosen per launch:
+// - contiguous eighths: XCD x walks the range u in [x*per_xcd, (x+1)*per_xcd);
+// - chunks of C consecutive tiles to the XCDs in turn: the k-th workgroup of
+//   XCD x takes tile u = ((k / C) * 8 + x) * C + k mod C (the grid is whole
+//   rounds of 8C), so the tiles an XCD runs at one time are still neighbours
+//   in u while every XCD works through the whole order.  With contiguous
+//   eighths the XCD whose tiles ran slowest was left alone at the end of a
+//   Mixtral-shaped launch (256-row tiles, chunks of 32: step 2642 -> 2598 us)
+//   and of the gate/up launch of layers with many 128-row blocks (chunks of
+//   64: Qwen3-Next-shaped gate/up 605 -> 578 us).  The other launches keep the
+//   eighths: chunked, they ran 1-8 % slower (Qwen3-Next-shaped down, 128- and
+//   64-row tiles of 1024- and 512-token layers).
+// Tiles are grouped GM blocks at a time, column-tile major inside a group: the
+// GM blocks of a group reuse each weight tile from L2, and each block's
+// activation rows are reused across the group's column tiles.
+constexpr int kXcdChunk = 32;     // 256-row tiles
+constexpr int kXcdChunkWide = 64; // 128 x 256 gate/up tiles of layers with many blocks
 
+template <int C>
 __device__ __forceinline__ int chunk_tile(int i)
 {
     const int x = i & 7, k = i >> 3;
-    return ((k / kXcdChunk) * 8 + x) * kXcdChunk + k % kXcdChunk;
+    return ((k / C) * 8 + x) * C + k % C;
 }
 
 struct TileSpace {
@@ -238,17 +242,17 @@ __device__ __forceinline__ BlockInfo tile_pick(const FwdArgs &a, const TileSpace
     }
 }
 
-// One tile per workgroup: workgroup i takes tile (i mod 8) * per_xcd + i / 8,
-// or chunk_tile(i) (CHUNKED: the 256-row tiles).
-template <int GM, bool ALIGNED, bool CHUNKED>
+// One tile per workgroup: workgroup i takes tile (i mod 8) * per_xcd + i / 8
+// (CHUNK = 0), or chunk_tile<CHUNK>(i).
+template <int GM, bool ALIGNED, int CHUNK>
 __device__ __forceinline__ bool tile_of(const FwdArgs &a, int BM, int ntiles, int &b, int &nt, BlockInfo &bi,
                                         int &nblocks)
 {
     const TileSpace t = tile_space(a, BM, ntiles);
     nblocks = t.blocks;
     int u;
-    if constexpr (CHUNKED) {
-        u = chunk_tile((int)blockIdx.x);
+    if constexpr (CHUNK > 0) {
+        u = chunk_tile<CHUNK>((int)blockIdx.x);
     } else {
         u = (int)(blockIdx.x % 8) * t.per_xcd + (int)(blockIdx.x / 8);
         if ((int)(blockIdx.x / 8) >= t.per_xcd)
@@ -754,7 +758,7 @@ __device__ __forceinline__ void gemm_tile(const FwdArgs &a, G &g, int b, int nt,
     }
 }
 
-template <class G, int GM, bool G1, bool PAGED, bool ATOMIC, bool TAIL>
+template <class G, int GM, bool G1, bool PAGED, bool ATOMIC, bool TAIL, int CHUNK>
 __global__ __launch_bounds__(64 * G::NW) void k_gemm(const FwdArgs a)
 {
     // The host pass only needs this kernel's signature (for its launch stub);
@@ -781,7 +785,8 @@ __global__ __launch_bounds__(64 * G::NW) void k_gemm(const FwdArgs a)
             const int i = (int)blockIdx.x;
             if (i < tp.full) { // whole tiles, dealt to the XCDs as in tile_of when full is whole rounds of
                                // chunks, else in contiguous eighths (full is a multiple of 8)
-                const int u = tp.full % kXcdRound == 0 ? chunk_tile(i) : (i & 7) * (tp.full >> 3) + (i >> 3);
+                static_assert(CHUNK > 0, "the split-tail launches deal their tiles in chunks");
+                const int u = tp.full % (8 * CHUNK) == 0 ? chunk_tile<CHUNK>(i) : (i & 7) * (tp.full >> 3) + (i >> 3);
                 const BlockInfo bi = tile_pick<GM, TAIL>(a, ts, ntiles, u, b, nt);
                 gemm_tile<G, G1, PAGED, ATOMIC, TAIL>(a, g, b, nt, bi, ts.blocks);
             } else if (i - tp.full < tp.tail * tp.ks) {
@@ -796,7 +801,7 @@ __global__ __launch_bounds__(64 * G::NW) void k_gemm(const FwdArgs a)
     }
     BlockInfo bi;
     int nblocks;
-    if (!tile_of<GM, TAIL, TAIL>(a, BM, ntiles, b, nt, bi, nblocks))
+    if (!tile_of<GM, TAIL, CHUNK>(a, BM, ntiles, b, nt, bi, nblocks))
         return;
     gemm_tile<G, G1, PAGED, ATOMIC, TAIL>(a, g, b, nt, bi, nblocks);
 #endif
@@ -962,11 +967,13 @@ __global__ __launch_bounds__(256) void k_resolve(const ResolveArgs r, const FwdA
 
 // Tile shapes per block height: the gate/up and down GEMMs,
 // Gemm<BM, BN, waves M, waves N, split-K waves, BK, stages, gate/up>.
-template <int BM_, class G1T, class G2T>
+template <int BM_, class G1T, class G2T, int CHUNK1_ = 0, int CHUNK2_ = 0>
 struct Tiles {
     static constexpr int BM = BM_;
     using K1 = G1T;
     using K2 = G2T;
+    // tiles dealt to the XCDs in chunks of this many (0: contiguous eighths), per launch
+    static constexpr int CHUNK1 = CHUNK1_, CHUNK2 = CHUNK2_;
     static_assert(G1T::BM_ == BM_ && G2T::BM_ == BM_, "block height");
 };
 // decode-sized blocks: one wave per 16-row tile, waves splitting K (many bytes in flight)
@@ -995,7 +1002,7 @@ using Tiles128d = Tiles<128, Gate128, Down128w>;
 // 400 -> 376 us); with few blocks the halved tile count leaves CUs idle (a
 // 1024-token Qwen1.5-shaped layer: 69 -> 70 us), hence kWideDownTiles
 using Down128x = Gemm<128, 512, 2, 4, 1, 64, 2, false>;
-using Tiles128wx = Tiles<128, Gemm<128, 256, 2, 4, 1, 64, 2, true>, Down128x>;
+using Tiles128wx = Tiles<128, Gemm<128, 256, 2, 4, 1, 64, 2, true>, Down128x, kXcdChunkWide>;
 using Tiles128dx = Tiles<128, Gate128, Down128x>;
 constexpr int64_t kWideDownTiles = 1024; // 512-column down tiles from this many on (at most blocks x d / 512)
 // when d is not a multiple of 128 (d and f are multiples of 64)
@@ -1004,7 +1011,8 @@ using Tiles128n = Tiles<128, Gate128, Gemm<128, 64, 2, 2, 1, 64, 2, false>>;
 // accumulator tile (gate/up: 64 x (64 gate + 64 up)); 256x256 down tiles.  K
 // steps of 64: every staged row is a 128-byte segment, which L2 feeds into LDS
 // markedly faster than 64-byte ones; two stages fill 128 KB of LDS.
-using Tiles256 = Tiles<256, Gemm<256, 128, 4, 2, 1, 64, 2, true>, Gemm<256, 256, 4, 2, 1, 64, 2, false>>;
+using Tiles256 = Tiles<256, Gemm<256, 128, 4, 2, 1, 64, 2, true>, Gemm<256, 256, 4, 2, 1, 64, 2, false>, kXcdChunk,
+                       kXcdChunk>;
 // when f or d is not a multiple of 128 / 256
 using Tiles256n = Tiles<256, Gemm<256, 64, 4, 2, 1, 32, 4, true>, Gemm<256, 64, 4, 1, 1, 32, 4, false>>;
 
@@ -1066,8 +1074,11 @@ hipError_t launch_tiles_t(const FwdArgs &a_in, hipStream_t s)
         return hipErrorInvalidValue;
     constexpr int T1 = 64 * G1T::NW, T2 = 64 * G2T::NW;
     constexpr int GM = TAIL ? kGroupMLong : kGroupM;
-    auto k1 = k_gemm<G1T, GM, true, PAGED, false, TAIL>;
-    auto k2 = k_gemm<G2T, GM, false, PAGED, ATOMIC, TAIL>;
+    // the split-tail launches deal their tiles in chunks (kXcdChunk unless the table says otherwise)
+    constexpr int C1 = C::CHUNK1 ? C::CHUNK1 : (TAIL ? kXcdChunk : 0);
+    constexpr int C2 = C::CHUNK2 ? C::CHUNK2 : (TAIL ? kXcdChunk : 0);
+    auto k1 = k_gemm<G1T, GM, true, PAGED, false, TAIL, C1>;
+    auto k2 = k_gemm<G2T, GM, false, PAGED, ATOMIC, TAIL, C2>;
     a.slots[0] = a.slots[1] = 0;
     if constexpr (TAIL) {
         const int p1 = resident_slots((const void *)k1, T1), p2 = resident_slots((const void *)k2, T2);
@@ -1080,23 +1091,23 @@ hipError_t launch_tiles_t(const FwdArgs &a_in, hipStream_t s)
         if (a.ev[i])
             (void)hipEventRecord(a.ev[i], s);
     };
-    // whole rounds of chunks for the chunk-dealt (TAIL) tiles, whole rounds of XCDs otherwise
-    constexpr int64_t kRound = TAIL ? kXcdRound : 8;
-    auto grid = [&](int ntiles, int slots) {
-        return (unsigned)((grid_m * ntiles + kRound - 1) / kRound * kRound + slots);
+    // whole rounds of chunks for chunk-dealt tiles, whole rounds of XCDs otherwise
+    auto grid = [&](int ntiles, int slots, int chunk) {
+        const int64_t round = 8 * (chunk > 0 ? chunk : 1);
+        return (unsigned)((grid_m * ntiles + round - 1) / round * round + slots);
     };
     if (ATOMIC) {
         const int64_t n4 = a.T * a.d / 4;
         k_zero<<<(unsigned)((n4 + 255) / 256), 256, 0, s>>>((float4 *)a.comb, n4);
     }
     mark(0);
-    k1<<<grid(a.f / BN1, a.slots[0]), T1, 0, s>>>(a);
+    k1<<<grid(a.f / BN1, a.slots[0], C1), T1, 0, s>>>(a);
     if constexpr (TAIL)
         if (a.slots[0])
             k_tail_fixup<BM, BN1, GM, true, false>
                 <<<(unsigned)(a.slots[0] / 2 * fixup_chunks(BM, BN1)), 256, 0, s>>>(a);
     mark(1);
-    k2<<<grid(a.d / BN2, a.slots[1]), T2, 0, s>>>(a);
+    k2<<<grid(a.d / BN2, a.slots[1], C2), T2, 0, s>>>(a);
     if constexpr (TAIL)
         if (a.slots[1])
             k_tail_fixup<BM, BN2, GM, false, ATOMIC>
