@@ -47,11 +47,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint3
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, 0x00020000);
 }
 
-__device__ __forceinline__ i32x4 bload(__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff)
-{
-    return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
-}
-
 __device__ __forceinline__ uint16_t f32_to_bf16(float v)
 {
     uint32_t u = __float_as_uint(v);

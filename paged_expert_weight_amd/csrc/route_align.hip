@@ -458,7 +458,6 @@ __global__ __launch_bounds__(kAlignThreads) void k_align_scan(const RouteArgs a,
     __shared__ int seg[kMaxExpertsTotal];
     __shared__ int segc[kMaxExpertsTotal];
     __shared__ int tmp[kAlignWaves];
-    const int n = (int)(a.T * a.keff);
     const int nchp = count_stride(a.T * a.keff);
     const int e = threadIdx.x; // E_tot <= kAlignThreads
     const bool mine = e < a.E_tot;
