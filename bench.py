@@ -16,9 +16,10 @@ Prints ONE JSON line.  Default workload: the Mixtral-8x7B-shaped layer (T=4096,
 d=4096, f=14336, E=8, top-2, Zipf(1.2) routing; all experts paged in a
 fragmented pool), the largest configuration; every other configuration (the
 tiny, Qwen1.5-MoE-shaped and Qwen3-Next-shaped layers and the decode sweep
-T = 1, 8, 32, 128, 512) is timed in the same run and reported under "configs"
-(step time, fractions of the rooflines, paged vs contiguous, the dominant
-kernel's roofline).
+T = 1, 2, 4, 8, 32, 128, 512) is timed in the same run and reported under
+"configs" (step time, fractions of the rooflines, paged vs contiguous, the
+dominant kernel's roofline; for batches of up to 512 tokens also the step
+replayed from a HIP graph).
 """
 from __future__ import annotations
 
