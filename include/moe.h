@@ -38,6 +38,13 @@
  *     earlier launch surfaces as MOE_ERR_HIP on a later call.  No exception
  *     crosses this boundary.
  *   - T = 0 tokens is a valid no-op.
+ *   - Concurrency: the host state of one pool, pipeline or allocator handle is
+ *     not guarded, so calls on one handle must not run at the same time from
+ *     several host threads; calls on different handles may.  On the device,
+ *     forwards over one pool enqueued on different streams may overlap (they
+ *     only read the pool, the load buffers and the page table) when each has
+ *     its own workspace and outputs; page-table uploads and load-buffer fills
+ *     are ordered against them as stated at those calls.
  */
 #ifndef PMOE_MOE_H
 #define PMOE_MOE_H
@@ -210,9 +217,11 @@ int moe_route(moe_pool *pool, const float *logits, int64_t T, int32_t block_m,
  *                last moe_loadbuf_fill of that buffer, and marks the buffer
  *                consumed when its last read is done (with
  *                MOE_FLAG_DEFER_READ_DONE: when the next fill of the buffer is
- *                enqueued, by an event on `stream` then); it fails with
- *                MOE_ERR_STATE if the table names load-buffer experts and that
- *                buffer was never filled.
+ *                enqueued, by an event on `stream` then); a fill waits for
+ *                every forward that read the buffer before it was enqueued,
+ *                on any number of streams.  It fails with MOE_ERR_STATE if the
+ *                table names load-buffer experts and that buffer was never
+ *                filled.
  *   y            device bf16 [T][d] out.
  *   workspace    device, >= moe_workspace_bytes(pool, T, block_m, flags) bytes;
  *                holds the SiLU-gated activations [sorted_cap][f] (bf16) and the

@@ -28,8 +28,11 @@ struct moe_pool {
     hipEvent_t consumed[2] = {nullptr, nullptr}; // last forward reading buffer b done (write-after-read)
     bool ever_filled[2] = {false, false};
     bool consumed_rec[2] = {false, false};
-    // streams of forwards that read buffer b with MOE_FLAG_DEFER_READ_DONE and
-    // have not been marked yet (by the next fill of b or by destroy)
+    hipStream_t consumed_stream[2] = {nullptr, nullptr}; // stream of the last record of consumed[b]
+    // streams of forwards that read buffer b and have not been marked yet (by
+    // the next fill of b or by destroy): forwards with MOE_FLAG_DEFER_READ_DONE,
+    // and forwards whose consumed[b] record a later forward on another stream
+    // replaced while it was still pending
     std::vector<hipStream_t> deferred_readers[2];
     // stage timing (measurement only): one set of 4 events per recorded forward
     bool timing = false;
@@ -339,15 +342,33 @@ int loadbuf_read_begin(moe_pool *p, int32_t buf, hipStream_t s)
 
 // After a forward that read load buffer buf on stream s: mark the buffer read
 // (write after read), now or (MOE_FLAG_DEFER_READ_DONE) at its next fill.
+// consumed[buf] is one event: recording it on s replaces the record of an
+// earlier forward, so when that record was made on another stream and has not
+// fired yet, that stream goes to the buffer's unmarked readers and the next
+// fill marks it again; a fill thus waits for every forward that read the
+// buffer before it, on whichever streams.
 int loadbuf_read_end(moe_pool *p, int32_t buf, uint32_t flags, hipStream_t s)
 {
+    auto &rd = p->deferred_readers[buf];
+    auto add_reader = [&](hipStream_t r) {
+        if (std::find(rd.begin(), rd.end(), r) == rd.end())
+            rd.push_back(r);
+    };
     if (flags & MOE_FLAG_DEFER_READ_DONE) {
-        auto &rd = p->deferred_readers[buf];
-        if (std::find(rd.begin(), rd.end(), s) == rd.end())
-            rd.push_back(s);
+        add_reader(s);
     } else {
+        if (p->consumed_rec[buf] && p->consumed_stream[buf] != s) {
+            const hipError_t q = hipEventQuery(p->consumed[buf]);
+            if (q == hipErrorNotReady) {
+                (void)hipGetLastError();
+                add_reader(p->consumed_stream[buf]);
+            } else if (q != hipSuccess) {
+                return hip_fail(q, "hipEventQuery");
+            }
+        }
         HIP_TRY(hipEventRecord(p->consumed[buf], s));
         p->consumed_rec[buf] = true;
+        p->consumed_stream[buf] = s;
     }
     return MOE_OK;
 }
@@ -666,6 +687,7 @@ int moe_loadbuf_fill(moe_pool *p, int32_t buf, int32_t n, const int32_t *slots, 
             continue; // same stream: already ordered
         HIP_TRY(hipEventRecord(p->consumed[buf], r));
         p->consumed_rec[buf] = true;
+        p->consumed_stream[buf] = r;
         HIP_TRY(hipStreamWaitEvent(s, p->consumed[buf], 0));
     }
     p->deferred_readers[buf].clear();

@@ -455,6 +455,44 @@ def test_fill_waits_for_a_queued_forward_of_its_buffer(flags):
     assert picks_loadbuf and np.isnan(y_f64(y2)).any()
 
 
+@pytest.mark.parametrize("flags", [0, pm.MOE_FLAG_DEFER_READ_DONE])
+def test_fill_waits_for_forwards_on_two_streams(flags):
+    """Two forwards read load buffer 0 on two streams: the first is held back
+    behind a sleep kernel, the second runs at once (and, without the deferred
+    flag, re-records the buffer's "read" event on its own stream after the
+    first one's).  A fill of buffer 0 with NaN pages enqueued after both must
+    wait for both, so both outputs match the oracle."""
+    c = Case(host_layer("tiny"))
+    s = c.s
+    held, free, copy = torch.cuda.Stream(), torch.cuda.Stream(), torch.cuda.Stream()
+    ys = []
+    torch.cuda.synchronize()
+    for st, sleep in ((held, True), (free, False)):
+        ws = pm.workspace(c.pool, s.T, 16)
+        with torch.cuda.stream(st):
+            if sleep:
+                torch.cuda._sleep(50_000_000)
+            r = pm.route(c.pool, c.dev.logits, 16, ws, stream=st)
+            y = torch.empty_like(c.dev.x)
+            pm.moe_paged_forward(c.pool, c.dev.x, 16, r.topk_ids, r.topk_w, r.sorted_ids, r.block_expert,
+                                 r.num_padded, 0, y, ws, flags, st)
+        ys.append((y, ws, r))
+    free.synchronize()
+    still_held = not held.query()
+    slots = sorted(c.dev.host_blobs)
+    nan = torch.full((3 * s.f * s.d,), float("nan"), dtype=torch.bfloat16).pin_memory()
+    pm.moe_loadbuf_fill(c.pool, 0, slots, [nan] * len(slots), copy)
+    torch.cuda.synchronize()
+    assert still_held, "the held forward had finished before the fill was enqueued; the test shows nothing"
+    ids, w = _oracle_routing(c)
+    assert np.isin(ids, synth.loadbuf_experts(s)).any(), "no token reads the load buffer"
+    ref = oracle.moe(c.layer.x, c.layer.w13, c.layer.w2, ids, w)
+    for y, _, _ in ys:
+        got = y_f64(y)
+        assert np.all(np.isfinite(got)) and max_rel_err(got, ref) <= TOL
+    c.pool.close()
+
+
 def test_state_errors():
     c = case("tiny")
     s = c.s
