@@ -131,8 +131,9 @@ typedef struct {
  * loading buffers when it was just copied in).  Validates desc (MOE_ERR_INVALID_ARG /
  * MOE_ERR_UNSUPPORTED / MOE_ERR_ALIGN), then allocates the handle's own small
  * state on the current device: the device copy of the location table
- * (E + S entries), a pinned staging copy, and four hipEvents (filled and
- * consumed, per load buffer).  The table starts with every expert unset; a
+ * (E + S entries), a pinned staging copy, a "filled" hipEvent per load
+ * buffer, and, as streams run forwards that read a load buffer, one "read"
+ * hipEvent per such stream (reused from fill to fill).  The table starts with every expert unset; a
  * forward before moe_set_expert_locs fails with MOE_ERR_STATE.
  * *out receives the handle; destroy it with moe_pool_destroy.
  */

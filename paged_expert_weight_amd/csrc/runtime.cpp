@@ -25,14 +25,19 @@ struct moe_pool {
     bool locs_set = false;
     bool uses_loadbuf = false;          // the table names at least one load-buffer expert
     hipEvent_t filled[2] = {nullptr, nullptr};   // last fill of buffer b done (read-after-write)
-    hipEvent_t consumed[2] = {nullptr, nullptr}; // last forward reading buffer b done (write-after-read)
     bool ever_filled[2] = {false, false};
-    bool consumed_rec[2] = {false, false};
-    hipStream_t consumed_stream[2] = {nullptr, nullptr}; // stream of the last record of consumed[b]
-    // streams of forwards that read buffer b and have not been marked yet (by
-    // the next fill of b or by destroy): forwards with MOE_FLAG_DEFER_READ_DONE,
-    // and forwards whose consumed[b] record a later forward on another stream
-    // replaced while it was still pending
+    // write-after-read marks of buffer b since its last fill: per stream that
+    // ran a forward reading it, an event recorded after that stream's last
+    // such forward (one event per stream, so forwards on several streams are
+    // all waited for by the next fill); events return to spare_events then
+    struct ReadMark {
+        hipStream_t stream;
+        hipEvent_t done;
+    };
+    std::vector<ReadMark> read_marks[2];
+    std::vector<hipEvent_t> spare_events;
+    // streams of forwards that read buffer b with MOE_FLAG_DEFER_READ_DONE and
+    // have not been marked yet (by the next fill of b or by destroy)
     std::vector<hipStream_t> deferred_readers[2];
     // stage timing (measurement only): one set of 4 events per recorded forward
     bool timing = false;
@@ -340,36 +345,42 @@ int loadbuf_read_begin(moe_pool *p, int32_t buf, hipStream_t s)
     return MOE_OK;
 }
 
+// A spare write-after-read event of the pool, or a new one.
+int take_read_event(moe_pool *p, hipEvent_t *ev)
+{
+    if (!p->spare_events.empty()) {
+        *ev = p->spare_events.back();
+        p->spare_events.pop_back();
+        return MOE_OK;
+    }
+    // marks the end of reads only: no cache writeback is needed before a later overwrite
+    const hipError_t e = hipEventCreateWithFlags(ev, kReadDoneEvent);
+    if (e != hipSuccess)
+        return hip_fail(e, "hipEventCreate");
+    return MOE_OK;
+}
+
 // After a forward that read load buffer buf on stream s: mark the buffer read
-// (write after read), now or (MOE_FLAG_DEFER_READ_DONE) at its next fill.
-// consumed[buf] is one event: recording it on s replaces the record of an
-// earlier forward, so when that record was made on another stream and has not
-// fired yet, that stream goes to the buffer's unmarked readers and the next
-// fill marks it again; a fill thus waits for every forward that read the
-// buffer before it, on whichever streams.
+// (write after read), now (the event of stream s, recorded again) or
+// (MOE_FLAG_DEFER_READ_DONE) at its next fill.
 int loadbuf_read_end(moe_pool *p, int32_t buf, uint32_t flags, hipStream_t s)
 {
-    auto &rd = p->deferred_readers[buf];
-    auto add_reader = [&](hipStream_t r) {
-        if (std::find(rd.begin(), rd.end(), r) == rd.end())
-            rd.push_back(r);
-    };
     if (flags & MOE_FLAG_DEFER_READ_DONE) {
-        add_reader(s);
-    } else {
-        if (p->consumed_rec[buf] && p->consumed_stream[buf] != s) {
-            const hipError_t q = hipEventQuery(p->consumed[buf]);
-            if (q == hipErrorNotReady) {
-                (void)hipGetLastError();
-                add_reader(p->consumed_stream[buf]);
-            } else if (q != hipSuccess) {
-                return hip_fail(q, "hipEventQuery");
-            }
-        }
-        HIP_TRY(hipEventRecord(p->consumed[buf], s));
-        p->consumed_rec[buf] = true;
-        p->consumed_stream[buf] = s;
+        auto &rd = p->deferred_readers[buf];
+        if (std::find(rd.begin(), rd.end(), s) == rd.end())
+            rd.push_back(s);
+        return MOE_OK;
     }
+    auto &marks = p->read_marks[buf];
+    hipEvent_t ev = nullptr;
+    for (const auto &m : marks)
+        if (m.stream == s)
+            ev = m.done;
+    if (!ev) {
+        CHECK(take_read_event(p, &ev));
+        marks.push_back({s, ev});
+    }
+    HIP_TRY(hipEventRecord(ev, s));
     return MOE_OK;
 }
 
@@ -444,13 +455,9 @@ int moe_pool_create(const moe_pool_desc *desc, moe_pool **out)
         return cleanup(hip_fail(e, "hipHostMalloc(staging)"));
     if ((e = hipEventCreateWithFlags(&p->upload_done, hipEventDisableTiming)) != hipSuccess)
         return cleanup(hip_fail(e, "hipEventCreate"));
-    for (int b = 0; b < 2; b++) {
+    for (int b = 0; b < 2; b++)
         if ((e = hipEventCreateWithFlags(&p->filled[b], hipEventDisableTiming)) != hipSuccess)
             return cleanup(hip_fail(e, "hipEventCreate"));
-        // marks the end of reads only: no cache writeback is needed before a later overwrite
-        if ((e = hipEventCreateWithFlags(&p->consumed[b], kReadDoneEvent)) != hipSuccess)
-            return cleanup(hip_fail(e, "hipEventCreate"));
-    }
     *out = p;
     return MOE_OK;
 }
@@ -467,15 +474,22 @@ int moe_pool_destroy(moe_pool *p)
                 (void)hipEventSynchronize(p->filled[b]);
             (void)hipEventDestroy(p->filled[b]);
         }
-        if (p->consumed[b]) {
-            if (p->consumed_rec[b])
-                (void)hipEventSynchronize(p->consumed[b]);
-            for (hipStream_t r : p->deferred_readers[b]) // forwards whose reads were not marked yet
-                if (hipEventRecord(p->consumed[b], r) == hipSuccess)
-                    (void)hipEventSynchronize(p->consumed[b]);
-            (void)hipEventDestroy(p->consumed[b]);
+        for (const auto &m : p->read_marks[b]) {
+            (void)hipEventSynchronize(m.done);
+            p->spare_events.push_back(m.done);
+        }
+        p->read_marks[b].clear();
+        for (hipStream_t r : p->deferred_readers[b]) { // forwards whose reads were not marked yet
+            hipEvent_t ev = nullptr;
+            if (pmoe::take_read_event(p, &ev) == MOE_OK) {
+                if (hipEventRecord(ev, r) == hipSuccess)
+                    (void)hipEventSynchronize(ev);
+                p->spare_events.push_back(ev);
+            }
         }
     }
+    for (hipEvent_t ev : p->spare_events)
+        (void)hipEventDestroy(ev);
     if (p->upload_done)
         (void)hipEventDestroy(p->upload_done);
     for (auto &ev : p->tev)
@@ -678,17 +692,25 @@ int moe_loadbuf_fill(moe_pool *p, int32_t buf, int32_t n, const int32_t *slots, 
         }
     }
     hipStream_t s = (hipStream_t)copy_stream;
-    if (p->consumed_rec[buf])
-        HIP_TRY(hipStreamWaitEvent(s, p->consumed[buf], 0));
-    // deferred readers: mark each stream now (the wait takes the event as
-    // recorded at the time of the call, so one event serves them in turn)
+    // write after read: every stream's last forward that read this buffer
+    // (a forward on the copy stream itself is ordered already).  A wait takes
+    // an event as recorded at the time of the call, so the events can be
+    // reused at once.
+    for (const auto &m : p->read_marks[buf]) {
+        if (m.stream != s)
+            HIP_TRY(hipStreamWaitEvent(s, m.done, 0));
+        p->spare_events.push_back(m.done);
+    }
+    p->read_marks[buf].clear();
+    // deferred readers: mark each stream now
     for (hipStream_t r : p->deferred_readers[buf]) {
         if (r == s)
             continue; // same stream: already ordered
-        HIP_TRY(hipEventRecord(p->consumed[buf], r));
-        p->consumed_rec[buf] = true;
-        p->consumed_stream[buf] = r;
-        HIP_TRY(hipStreamWaitEvent(s, p->consumed[buf], 0));
+        hipEvent_t ev = nullptr;
+        CHECK(pmoe::take_read_event(p, &ev));
+        p->spare_events.push_back(ev);
+        HIP_TRY(hipEventRecord(ev, r));
+        HIP_TRY(hipStreamWaitEvent(s, ev, 0));
     }
     p->deferred_readers[buf].clear();
     if (p->ever_filled[buf])
