@@ -153,3 +153,56 @@ def test_library_has_no_oracle_dependency():
     subprocess.run([sys.executable, "-c", code], check=True, cwd=ROOT)
     out = subprocess.run(["nm", "-D", pm.LIB_PATH], capture_output=True, text=True).stdout
     assert "oracle_" not in out
+
+
+def _prototypes():
+    """name -> (return kind, [parameter kinds]) of every prototype in include/."""
+    out = {}
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if not fn.endswith(".h"):
+            continue
+        text = open(os.path.join(ROOT, "include", fn)).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        for ret, name, params in re.findall(r"^(int32_t|int|const char \*|void)\s*\b(moe_[a-z_0-9]+)\s*\(([^)]*)\)\s*;",
+                                            text, flags=re.M):
+            kinds = []
+            for p in params.split(","):
+                p = " ".join(p.split())
+                if p in ("", "void"):
+                    continue
+                kinds.append(_kind(p.rsplit(" ", 1)[0] if "*" not in p else "*"))
+            out[name] = (_kind(ret.strip()), kinds)
+    return out
+
+
+def _kind(t: str) -> str:
+    if "*" in t:
+        return "ptr"
+    return {"int": "i32", "int32_t": "i32", "int64_t": "i64", "size_t": "sz", "uint32_t": "u32"}[t]
+
+
+def _ctype_kind(c) -> str:
+    if c in (ctypes.c_void_p, ctypes.c_char_p) or issubclass(c, ctypes._Pointer):
+        return "ptr"
+    for k, ct in (("i32", ctypes.c_int32), ("i64", ctypes.c_int64), ("sz", ctypes.c_size_t),
+                  ("u32", ctypes.c_uint32)):
+        if c is ct:
+            return k
+    raise AssertionError(f"unexpected ctypes type {c}")
+
+
+def test_binding_signatures_match_the_header(lib):
+    """Every binding's ctypes argument and result types against its prototype
+    in include/: the same count, and pointer / int32 / int64 / size_t /
+    uint32 in each position (a wrong width would truncate a size or a
+    pointer without an error)."""
+    protos = _prototypes()
+    assert set(protos) == set(pm.EXPORTS)
+    for name, (ret, kinds) in sorted(protos.items()):
+        f = getattr(lib, name)
+        got = [_ctype_kind(a) for a in (f.argtypes or [])]
+        assert got == kinds, f"{name}: binding {got}, header {kinds}"
+        r = f.restype
+        assert (r is ctypes.c_char_p and ret == "ptr") or (r in (ctypes.c_int, ctypes.c_int32) and ret == "i32"), \
+            f"{name}: result {r}, header {ret}"
