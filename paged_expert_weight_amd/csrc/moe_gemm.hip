@@ -56,6 +56,43 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float v)
     return (uint16_t)(u >> 16);
 }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+
+// Two fp32 values rounded to the nearest bf16 (ties to even) by the hardware
+// conversion v_cvt_pk_bf16_f32, packed with lo in bits 0-15: for every value
+// that is not a NaN the same bits as f32_to_bf16.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
+{
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
+}
+
+// N adjacent values rounded to bf16 and stored with one instruction (N = 1, 2,
+// 4 or 8; p aligned to 2N bytes); NT: non-temporally.
+template <int N, bool NT>
+__device__ __forceinline__ void store_bf16(uint16_t *p, const float (&v)[N])
+{
+    static_assert(N == 1 || N == 2 || N == 4 || N == 8, "store width");
+    auto put = [p](auto o) {
+        using V = decltype(o);
+        if constexpr (NT)
+            __builtin_nontemporal_store(o, (V *)p);
+        else
+            *(V *)p = o;
+    };
+    if constexpr (N == 1)
+        put((uint16_t)pack_bf16x2(v[0], 0.f));
+    else if constexpr (N == 2)
+        put(pack_bf16x2(v[0], v[1]));
+    else if constexpr (N == 4)
+        put((u32x2){pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])});
+    else
+        put((u32x4v){pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                     pack_bf16x2(v[6], v[7])});
+}
+
 // Page bases of expert e: the per-tile resolver shared by the GEMMs and moe_resolve_addrs.
 // The whole 16-byte entry in one load (the table is 16-byte aligned), so that
 // the page bases follow one memory round trip after the expert is known.
@@ -574,6 +611,19 @@ struct Gemm {
     }
 };
 
+// The output column (within the tile) whose weight row B stage row r holds.
+// compute() gives wave (wm, wn) the stage rows wn*WN + 16*j + l16 as fragment j
+// of lane l16; they hold columns wn*WN + FN*l16 + j, so a lane's FN
+// accumulators of one output row are FN adjacent columns and the epilogue
+// stores them with one 2*FN-byte store (the K order of every output is
+// unchanged: only which weight row a stage row is loaded from).
+template <class G>
+__device__ __forceinline__ int stage_col(int r)
+{
+    const int w = r / G::WN, q = r % G::WN;
+    return w * G::WN + (q % 16) * G::FN + q / 16;
+}
+
 // One output tile (block b, column tile nt) of a grouped GEMM.
 template <class G, bool G1, bool PAGED, bool ATOMIC, bool E_KNOWN>
 __device__ __forceinline__ void gemm_tile(const FwdArgs &a, G &g, int b, int nt, BlockInfo bi, int nblocks,
@@ -637,8 +687,8 @@ __device__ __forceinline__ void gemm_tile(const FwdArgs &a, G &g, int b, int nt,
             else // the block's h row
                 off = pick ? (uint32_t)(b * BM + row) * (uint32_t)f * 2u : kOOB;
         } else {
-            const int br = (row - BM) % BN;
-            off = (uint32_t)(n0 + br) * (uint32_t)K * 2u;
+            const int br = (row - BM) % BN; // B stage row (W1 / W2 rows, then W3 rows)
+            off = (uint32_t)(n0 + stage_col<G>(br)) * (uint32_t)K * 2u;
         }
         g.voff[i] = off + chunk * 16u;
     }
@@ -693,6 +743,7 @@ __device__ __forceinline__ void gemm_tile(const FwdArgs &a, G &g, int b, int nt,
     if (!g.reduce_k())
         return;
     const int lg = g.lg, l16 = g.l16;
+    const int col0 = g.wn * G::WN + G::FN * l16; // this lane's FN adjacent columns (stage_col)
     if (part) {
         // partial tile [BM][BNE] fp32 (gate/up: gate columns, then up columns)
         constexpr int BNE = G1 ? 2 * BN : BN;
@@ -703,7 +754,7 @@ __device__ __forceinline__ void gemm_tile(const FwdArgs &a, G &g, int b, int nt,
 #pragma unroll
                 for (int r = 0; r < 4; r++) {
                     const int row = g.wm * G::WM + i * 16 + 4 * lg + r;
-                    const int col = g.wn * G::WN + j * 16 + l16;
+                    const int col = col0 + j;
                     part[row * BNE + col] = g.acc0[i][j][r];
                     if constexpr (G1)
                         part[row * BNE + BN + col] = g.acc1[i][j][r];
@@ -724,12 +775,13 @@ __device__ __forceinline__ void gemm_tile(const FwdArgs &a, G &g, int b, int nt,
                 if (eflat[i][r] < 0)
                     continue;
                 const int row = g.wm * G::WM + i * 16 + 4 * lg + r;
+                float hv[G::FN];
 #pragma unroll
                 for (int j = 0; j < G::FN; j++) {
-                    const int col = g.wn * G::WN + j * 16 + l16;
                     const float gt = g.acc0[i][j][r], up = g.acc1[i][j][r];
-                    hb[(int64_t)row * f + col] = f32_to_bf16(gt / (1.f + __expf(-gt)) * up);
+                    hv[j] = gt / (1.f + __expf(-gt)) * up;
                 }
+                store_bf16<G::FN, false>(hb + (int64_t)row * f + col0, hv);
             }
     } else {
 #pragma unroll
@@ -739,15 +791,17 @@ __device__ __forceinline__ void gemm_tile(const FwdArgs &a, G &g, int b, int nt,
                 const int flat = eflat[i][r];
                 if (flat < 0)
                     continue;
+                if constexpr (ATOMIC) {
 #pragma unroll
-                for (int j = 0; j < G::FN; j++) {
-                    const int col = n0 + g.wn * G::WN + j * 16 + l16;
-                    if constexpr (ATOMIC)
-                        unsafeAtomicAdd(&((float *)a.comb)[(int64_t)(flat / a.keff) * d + col],
+                    for (int j = 0; j < G::FN; j++)
+                        unsafeAtomicAdd(&((float *)a.comb)[(int64_t)(flat / a.keff) * d + n0 + col0 + j],
                                         g.acc0[i][j][r] * ewt[i][r]);
-                    else // written once, read once by the combine: non-temporal
-                        __builtin_nontemporal_store(f32_to_bf16(g.acc0[i][j][r]),
-                                                    &((uint16_t *)a.comb)[(int64_t)flat * d + col]);
+                } else { // written once, read once by the combine: non-temporal
+                    float ov[G::FN];
+#pragma unroll
+                    for (int j = 0; j < G::FN; j++)
+                        ov[j] = g.acc0[i][j][r];
+                    store_bf16<G::FN, true>((uint16_t *)a.comb + (int64_t)flat * d + n0 + col0, ov);
                 }
             }
     }
