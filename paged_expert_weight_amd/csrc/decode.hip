@@ -157,7 +157,7 @@ __device__ __forceinline__ void dec_gate_up_rows(const FwdArgs &a, int e, int nc
             for (int r = 0; r < RPW; r++) {
                 const float gs = wave_sum(sg[r]), us = wave_sum(su[r]);
                 if (lane == r)
-                    a.h[(int64_t)flat * a.f + r0 + r] = f32_to_bf16_rne(gs / (1.f + __expf(-gs)) * us);
+                    a.h[(int64_t)flat * a.f + r0 + r] = f32_to_bf16_rne(silu_mul(gs, us));
             }
         }
     }

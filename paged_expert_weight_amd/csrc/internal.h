@@ -12,6 +12,15 @@ struct DevLoc {
     int32_t idx[3]; // pool: W1, W3, W2 page; load buffer: slot in idx[0]
 };
 
+// The SwiGLU gate of one h element as every forward kernel computes it:
+// silu(g) * u = g * (1 / (1 + e^-g)) * u in fp32, with the hardware's
+// exponential (v_exp_f32) and reciprocal (v_rcp_f32, 1 ulp) instead of an
+// IEEE division (about ten instructions); h is rounded to bf16 right after.
+__device__ __forceinline__ float silu_mul(float g, float u)
+{
+    return g * __builtin_amdgcn_rcpf(1.f + __expf(-g)) * u;
+}
+
 constexpr int kMaxExpertsTotal = 1024; // E + S
 constexpr int kMaxTopK = 32;
 

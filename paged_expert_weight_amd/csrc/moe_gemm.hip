@@ -778,8 +778,7 @@ __device__ __forceinline__ void gemm_tile(const FwdArgs &a, G &g, int b, int nt,
                 float hv[G::FN];
 #pragma unroll
                 for (int j = 0; j < G::FN; j++) {
-                    const float gt = g.acc0[i][j][r], up = g.acc1[i][j][r];
-                    hv[j] = gt / (1.f + __expf(-gt)) * up;
+                    hv[j] = silu_mul(g.acc0[i][j][r], g.acc1[i][j][r]);
                 }
                 store_bf16<G::FN, false>(hb + (int64_t)row * f + col0, hv);
             }
@@ -892,7 +891,7 @@ __global__ __launch_bounds__(256) void k_tail_fixup(const FwdArgs a)
     const int n0 = nt * BN;
     uint2 o;
     if constexpr (G1) {
-        auto hv = [](float g, float u) { return (uint32_t)f32_to_bf16(g / (1.f + __expf(-g)) * u); };
+        auto hv = [](float g, float u) { return (uint32_t)f32_to_bf16(silu_mul(g, u)); };
         o.x = hv(s0.x, s1.x) | (hv(s0.y, s1.y) << 16);
         o.y = hv(s0.z, s1.z) | (hv(s0.w, s1.w) << 16);
         *(uint2 *)&a.h[((int64_t)b * BM + row) * a.f + n0 + col] = o;
