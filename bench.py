@@ -39,12 +39,12 @@ HBM_PEAK_GBS = 8000.0
 # 1 GiB copy reads back, plus WRITE_SIZE), keyed by workload, T, block_m, atomic combine and a
 # hash of the GEMM sources the counters were taken on.  Reported only while that hash matches.
 MEASURED_TRAFFIC = {
-    ("mixtral", 4096, 256, False, "4d95f5a1b2589922"): 3801238873,
-    ("qwen15", 1024, 128, False, "4d95f5a1b2589922"): 718627311,
-    ("qwen3n", 8192, 128, False, "4d95f5a1b2589922"): 2762364366,
-    ("decode", 1, 16, False, "4d95f5a1b2589922"): 46326348,
-    ("decode", 8, 16, False, "4d95f5a1b2589922"): 300416140,
-    ("decode", 32, 16, False, "4d95f5a1b2589922"): 577648379,
+    ("mixtral", 4096, 256, False, "dcff8896ee5b326d"): 3803704174,
+    ("qwen15", 1024, 128, False, "dcff8896ee5b326d"): 718556427,
+    ("qwen3n", 8192, 128, False, "dcff8896ee5b326d"): 2774106874,
+    ("decode", 1, 16, False, "dcff8896ee5b326d"): 46326334,
+    ("decode", 8, 16, False, "dcff8896ee5b326d"): 300422472,
+    ("decode", 32, 16, False, "dcff8896ee5b326d"): 577641500,
 }
 GEMM_SOURCES = ("paged_expert_weight_amd/csrc/moe_gemm.hip", "paged_expert_weight_amd/csrc/decode.hip",
                 "paged_expert_weight_amd/csrc/internal.h")

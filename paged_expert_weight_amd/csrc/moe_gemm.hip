@@ -47,23 +47,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint3
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, 0x00020000);
 }
 
-__device__ __forceinline__ uint16_t f32_to_bf16(float v)
-{
-    uint32_t u = __float_as_uint(v);
-    if ((u & 0x7fffffffu) > 0x7f800000u)
-        return 0x7fc0;
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
-}
-
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
 
-// Two fp32 values rounded to the nearest bf16 (ties to even) by the hardware
-// conversion v_cvt_pk_bf16_f32, packed with lo in bits 0-15: for every value
-// that is not a NaN the same bits as f32_to_bf16.
+// Two fp32 values rounded to the nearest bf16 (ties to even; a NaN stays a
+// NaN) by the hardware conversion v_cvt_pk_bf16_f32, packed with lo in bits
+// 0-15.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
 {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
@@ -891,9 +882,8 @@ __global__ __launch_bounds__(256) void k_tail_fixup(const FwdArgs a)
     const int n0 = nt * BN;
     uint2 o;
     if constexpr (G1) {
-        auto hv = [](float g, float u) { return (uint32_t)f32_to_bf16(silu_mul(g, u)); };
-        o.x = hv(s0.x, s1.x) | (hv(s0.y, s1.y) << 16);
-        o.y = hv(s0.z, s1.z) | (hv(s0.w, s1.w) << 16);
+        o.x = pack_bf16x2(silu_mul(s0.x, s1.x), silu_mul(s0.y, s1.y));
+        o.y = pack_bf16x2(silu_mul(s0.z, s1.z), silu_mul(s0.w, s1.w));
         *(uint2 *)&a.h[((int64_t)b * BM + row) * a.f + n0 + col] = o;
     } else {
         const int flat = a.sorted_ids[b * BM + row];
@@ -907,8 +897,8 @@ __global__ __launch_bounds__(256) void k_tail_fixup(const FwdArgs a)
             unsafeAtomicAdd(y32 + 2, s0.z * w);
             unsafeAtomicAdd(y32 + 3, s0.w * w);
         } else {
-            o.x = (uint32_t)f32_to_bf16(s0.x) | ((uint32_t)f32_to_bf16(s0.y) << 16);
-            o.y = (uint32_t)f32_to_bf16(s0.z) | ((uint32_t)f32_to_bf16(s0.w) << 16);
+            o.x = pack_bf16x2(s0.x, s0.y);
+            o.y = pack_bf16x2(s0.z, s0.w);
             *(uint2 *)&((uint16_t *)a.comb)[(int64_t)flat * a.d + n0 + col] = o;
         }
     }
@@ -955,10 +945,10 @@ __global__ __launch_bounds__(256) void k_combine(const uint16_t *part, const flo
             }
     }
     uint4 o;
-    o.x = (uint32_t)f32_to_bf16(acc[0]) | ((uint32_t)f32_to_bf16(acc[1]) << 16);
-    o.y = (uint32_t)f32_to_bf16(acc[2]) | ((uint32_t)f32_to_bf16(acc[3]) << 16);
-    o.z = (uint32_t)f32_to_bf16(acc[4]) | ((uint32_t)f32_to_bf16(acc[5]) << 16);
-    o.w = (uint32_t)f32_to_bf16(acc[6]) | ((uint32_t)f32_to_bf16(acc[7]) << 16);
+    o.x = pack_bf16x2(acc[0], acc[1]);
+    o.y = pack_bf16x2(acc[2], acc[3]);
+    o.z = pack_bf16x2(acc[4], acc[5]);
+    o.w = pack_bf16x2(acc[6], acc[7]);
     *(uint4 *)&y[t * d + c] = o;
 }
 
@@ -970,8 +960,8 @@ __global__ __launch_bounds__(256) void k_convert(const float *y32, int64_t T, in
         return;
     const float4 v = *(const float4 *)&y32[idx * 4];
     uint2 o;
-    o.x = (uint32_t)f32_to_bf16(v.x) | ((uint32_t)f32_to_bf16(v.y) << 16);
-    o.y = (uint32_t)f32_to_bf16(v.z) | ((uint32_t)f32_to_bf16(v.w) << 16);
+    o.x = pack_bf16x2(v.x, v.y);
+    o.y = pack_bf16x2(v.z, v.w);
     *(uint2 *)&y[idx * 4] = o;
 }
 
