@@ -404,11 +404,19 @@ struct Gemm {
     static constexpr int N_AFTER = (LB > LA ? IB : 0) + (LA - 1) * IPW;
     static_assert(S >= 2 && SB >= S && SB <= 8 && N_AFTER < 64, "stages");
     static constexpr int BM_ = BM, BN_ = BN, WK_ = WK, WAVES_N_ = WAVES_N;
+    // Waves whose rows are all padding skip their MFMAs in 128-row tiles, the height
+    // of layers with many small experts, whose blocks are mostly padding (414 of the
+    // 513 experts of a Qwen3-Next-shaped layer have one block of ~60 picks): a
+    // 8192-token step 1008 -> 984 us.  Elsewhere it measured no gain (256-row
+    // tiles: their weight rows stream at the same rate whatever the MFMA load;
+    // 64-row tiles: +1 us at 512 tokens), and those kernels compile without it.
+    static constexpr bool kSkipPaddingWaves = BM == 128;
 
     __amdgpu_buffer_rsrc_t ra, rb0, rb1;
     uint32_t voff[IPW];
     int wave, wt, kg, wm, wn, l16, lg;
     uint8_t *lds; // WK rings (S A stages, then SB B stages), one workgroup-scope array
+    bool live;    // false: every output row of this wave is padding, so it multiplies nothing
     f32x4 acc0[FM][FN], acc1[FM][FN];
 
     // Stages at constant offsets: the waits on the DMA into one stage then
@@ -461,6 +469,9 @@ struct Gemm {
     template <int JA, int JB>
     __device__ __forceinline__ void compute()
     {
+        if constexpr (kSkipPaddingWaves)
+            if (!live) // its accumulators stay zero, as they would over the zero rows staged for padding
+                return;
         const uint8_t *sa = a_stage<JA>(), *sb = b_stage<JB>();
 #pragma unroll
         for (int sub = 0; sub < BK / 32; sub++) {
@@ -712,8 +723,20 @@ __device__ __forceinline__ void gemm_tile(const FwdArgs &a, G &g, int b, int nt,
     // the picks are read before the first stages are issued (nothing waits
     // for them until the epilogue); the ordered combine applies the routing
     // weights itself, the atomic one reads them after the K loop
+    g.live = true;
     if constexpr (kPrefetchRows)
         epilogue_picks();
+    if constexpr (kPrefetchRows && G::kSkipPaddingWaves) {
+        // a wave whose rows (all WM of them, over its lanes) are padding skips its
+        // MFMAs and operand reads; it still issues its share of the stage DMA
+        bool any = false;
+#pragma unroll
+        for (int i = 0; i < G::FM; i++)
+#pragma unroll
+            for (int r = 0; r < 4; r++)
+                any |= eflat[i][r] >= 0;
+        g.live = __ballot(any) != 0;
+    }
 
     // K-steps [kb, ke): range ks of nks (the whole contraction unless the tile
     // is split), divided again over the WK waves of a split-K tile
