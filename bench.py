@@ -39,12 +39,12 @@ HBM_PEAK_GBS = 8000.0
 # 1 GiB copy reads back, plus WRITE_SIZE), keyed by workload, T, block_m, atomic combine and a
 # hash of the GEMM sources the counters were taken on.  Reported only while that hash matches.
 MEASURED_TRAFFIC = {
-    ("mixtral", 4096, 256, False, "dcff8896ee5b326d"): 3803704174,
-    ("qwen15", 1024, 128, False, "dcff8896ee5b326d"): 718556427,
-    ("qwen3n", 8192, 128, False, "dcff8896ee5b326d"): 2774106874,
-    ("decode", 1, 16, False, "dcff8896ee5b326d"): 46326334,
-    ("decode", 8, 16, False, "dcff8896ee5b326d"): 300422472,
-    ("decode", 32, 16, False, "dcff8896ee5b326d"): 577641500,
+    ("mixtral", 4096, 256, False, "09cbd99b79f1d43e"): 3821861346,
+    ("qwen15", 1024, 128, False, "09cbd99b79f1d43e"): 718599675,
+    ("qwen3n", 8192, 128, False, "09cbd99b79f1d43e"): 2754058075,
+    ("decode", 1, 16, False, "09cbd99b79f1d43e"): 46326297,
+    ("decode", 8, 16, False, "09cbd99b79f1d43e"): 300422173,
+    ("decode", 32, 16, False, "09cbd99b79f1d43e"): 577640983,
 }
 GEMM_SOURCES = ("paged_expert_weight_amd/csrc/moe_gemm.hip", "paged_expert_weight_amd/csrc/decode.hip",
                 "paged_expert_weight_amd/csrc/internal.h")
