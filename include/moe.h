@@ -231,7 +231,8 @@ int moe_route(moe_pool *pool, const float *logits, int64_t T, int32_t block_m,
  *                between calls.
  *   flags        0, MOE_FLAG_ATOMIC_COMBINE, MOE_FLAG_DEFER_READ_DONE, or both.
  * Gate/up GEMM: each output tile resolves its W1 and W3 page bases once and
- * fuses silu(gate) * up into its epilogue; down GEMM: each tile resolves its
+ * fuses silu(gate) * up into its epilogue (fp32, g * rcp(1 + exp(-g)) * u with
+ * the hardware exponential and reciprocal, then rounded to bf16 h); down GEMM: each tile resolves its
  * W2 page once; each expert output row is rounded to bf16, and the k+S rows of
  * a token are scaled by their routing weights and added in fp32 in slot order
  * (bit-reproducible) before the sum is rounded to bf16.  With
