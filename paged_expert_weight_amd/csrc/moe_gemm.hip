@@ -15,10 +15,15 @@
 //             the same columns j0..j0+BN of both halves, so gate and up of one
 //             output land in the same lane and the SiLU*mul epilogue runs in
 //             registers.
-//   down:     o[i][r] = sum_c h[i][c] W2_e[r][c], W2 page [d][f]; scaled by the
-//             routing weight of flat pick i and written to the combine buffer
-//             row i (fixed order) or added into y32[token] (fp32 atomics).
-//   combine:  y[t] = bf16( sum_j comb[t*(k+S)+j] ), j ascending.
+//   down:     o[i][r] = sum_c h[i][c] W2_e[r][c], W2 page [d][f]; row i is
+//             rounded to bf16 into the combine buffer at its flat pick (ordered
+//             mode), or scaled by the pick's routing weight and added into
+//             y32[token] (fp32 atomics).
+//   combine:  y[t] = bf16( sum_j w[t][j] * comb[t*(k+S)+j] ), in fp32, j ascending.
+//
+// Epilogues store each lane's adjacent output columns of a row with one 8- or
+// 16-byte store (stage_col); in 128-row tiles a wave whose rows are all
+// padding skips its MFMAs (kSkipPaddingWaves).
 //
 // Operands are K-contiguous on both sides (x rows and weight rows run along d;
 // h rows and W2 rows run along f).  Each K-step (64 elements for most tiles)
