@@ -384,6 +384,20 @@ int loadbuf_read_end(moe_pool *p, int32_t buf, uint32_t flags, hipStream_t s)
     return MOE_OK;
 }
 
+// The end of a forward whose launches may read load buffer buf, rc being the
+// forward's result: the read mark is recorded even when the forward failed (a
+// launch that failed may follow launches already enqueued that read the
+// buffer), and the forward's own error, if any, is the one reported.
+int loadbuf_read_end_after(moe_pool *p, int32_t buf, uint32_t flags, hipStream_t s, int rc)
+{
+    if (rc == MOE_OK)
+        return loadbuf_read_end(p, buf, flags, s);
+    const std::string first = g_err;
+    (void)loadbuf_read_end(p, buf, flags, s);
+    g_err = first;
+    return rc;
+}
+
 } // namespace pmoe
 
 extern "C" {
@@ -595,13 +609,14 @@ int paged_begin(moe_pool *p, int64_t T, int32_t active_buf, uint32_t flags, hipS
     return MOE_OK;
 }
 
-// After a paged forward: mark its load buffer read (write after read), now
-// or (MOE_FLAG_DEFER_READ_DONE) at the buffer's next fill.
-int paged_end(moe_pool *p, int64_t T, int32_t active_buf, uint32_t flags, hipStream_t s)
+// After a paged forward whose result is rc: mark its load buffer read (write
+// after read), now or (MOE_FLAG_DEFER_READ_DONE) at the buffer's next fill,
+// also when the forward failed part-way.
+int paged_end(moe_pool *p, int64_t T, int32_t active_buf, uint32_t flags, hipStream_t s, int rc)
 {
     if (T > 0 && p->uses_loadbuf)
-        return pmoe::loadbuf_read_end(p, active_buf, flags, s);
-    return MOE_OK;
+        return pmoe::loadbuf_read_end_after(p, active_buf, flags, s, rc);
+    return rc;
 }
 
 } // namespace
@@ -613,10 +628,10 @@ int moe_paged_forward(moe_pool *p, const void *x, int64_t T, int32_t block_m, co
 {
     hipStream_t s = (hipStream_t)stream;
     CHECK(paged_begin(p, T, active_buf, flags, s));
-    CHECK(forward_common(p, nullptr, nullptr, true, x, T, block_m, topk_ids, topk_w, sorted_ids, block_expert,
-                         num_padded, active_buf, y, ws, ws_bytes, flags & MOE_FLAG_ATOMIC_COMBINE, s,
-                         T > 0 ? next_timing_events(p) : nullptr));
-    return paged_end(p, T, active_buf, flags, s);
+    const int rc = forward_common(p, nullptr, nullptr, true, x, T, block_m, topk_ids, topk_w, sorted_ids,
+                                  block_expert, num_padded, active_buf, y, ws, ws_bytes,
+                                  flags & MOE_FLAG_ATOMIC_COMBINE, s, T > 0 ? next_timing_events(p) : nullptr);
+    return paged_end(p, T, active_buf, flags, s, rc);
 }
 
 int moe_route_forward(moe_pool *p, const float *logits, const void *x, int64_t T, int32_t block_m,
@@ -628,10 +643,11 @@ int moe_route_forward(moe_pool *p, const float *logits, const void *x, int64_t T
     CHECK(paged_begin(p, T, active_buf, flags, s));
     if (T > 0 && !logits)
         return fail(MOE_ERR_INVALID_ARG, "logits is null");
-    CHECK(forward_common(p, nullptr, nullptr, true, x, T, block_m, topk_ids, topk_w, sorted_ids, block_expert,
-                         num_padded, active_buf, y, ws, ws_bytes, flags & MOE_FLAG_ATOMIC_COMBINE, s,
-                         T > 0 ? next_timing_events(p) : nullptr, logits));
-    return paged_end(p, T, active_buf, flags, s);
+    const int rc = forward_common(p, nullptr, nullptr, true, x, T, block_m, topk_ids, topk_w, sorted_ids,
+                                  block_expert, num_padded, active_buf, y, ws, ws_bytes,
+                                  flags & MOE_FLAG_ATOMIC_COMBINE, s, T > 0 ? next_timing_events(p) : nullptr,
+                                  logits);
+    return paged_end(p, T, active_buf, flags, s, rc);
 }
 
 int moe_route_contiguous_forward(const moe_pool *p, const void *w13, const void *w2, const float *logits,
@@ -1202,12 +1218,21 @@ int moe_pipeline_forward(moe_pipeline *p, int32_t layer, const void *x, int64_t 
             return hip_fail(q, "hipEventQuery");
         }
     }
-    CHECK(forward_common(h, nullptr, nullptr, true, x, T, block_m, topk_ids, topk_w, sorted_ids, block_expert,
-                         num_padded, b, y, ws, ws_bytes, flags, s, nullptr));
+    const int rc = forward_common(h, nullptr, nullptr, true, x, T, block_m, topk_ids, topk_w, sorted_ids,
+                                  block_expert, num_padded, b, y, ws, ws_bytes, flags, s, nullptr);
     if (T > 0 && uses_lb) {
-        HIP_TRY(hipEventRecord(p->consumed[b], s));
-        p->consumed_rec[b] = true;
+        // recorded also when the forward failed part-way: launches enqueued
+        // before a failing one still read the buffer
+        const hipError_t e = hipEventRecord(p->consumed[b], s);
+        if (e == hipSuccess)
+            p->consumed_rec[b] = true;
+        else if (rc == MOE_OK)
+            return hip_fail(e, "hipEventRecord");
+        else
+            (void)hipGetLastError();
     }
+    if (rc != MOE_OK)
+        return rc;
     if (p->filled_for[b] == layer)
         p->unread[b] = false;
     return MOE_OK;

@@ -27,6 +27,8 @@ bool pool_shape(const moe_pool *p, int32_t *E_tot, int64_t *page_bytes);
 // the layer handle's load-buffer events around a forward that reads buffer buf
 int loadbuf_read_begin(moe_pool *p, int32_t buf, hipStream_t s);
 int loadbuf_read_end(moe_pool *p, int32_t buf, uint32_t flags, hipStream_t s);
+// the same after a forward whose result is rc, also when it failed part-way
+int loadbuf_read_end_after(moe_pool *p, int32_t buf, uint32_t flags, hipStream_t s, int rc);
 // the layer handle's load-buffer base addresses
 void pool_loadbufs(const moe_pool *p, void *bases[2]);
 } // namespace pmoe
@@ -327,9 +329,9 @@ int moe_vmm_forward(const moe_vmm *v, moe_pool *pool, const void *x, int64_t T, 
     const int rc = moe_contiguous_forward(pool, v->w13_va, v->w2_va, x, T, block_m, topk_ids, topk_w, sorted_ids,
                                           block_expert, num_padded, y, ws, ws_bytes,
                                           flags & MOE_FLAG_ATOMIC_COMBINE, stream);
-    if (rc != MOE_OK || !lb)
+    if (!lb)
         return rc;
-    return pmoe::loadbuf_read_end(pool, v->active_buf, flags, s);
+    return pmoe::loadbuf_read_end_after(pool, v->active_buf, flags, s, rc);
 }
 
 } // extern "C"

@@ -508,10 +508,20 @@ def test_state_errors():
     with pytest.raises(pm.MoeError) as ei:
         pm.paged_forward(p2, c.dev.x, r, 1, ws)
     assert ei.value.code == pm.MOE_ERR_STATE
-    # workspace too small
-    with pytest.raises(pm.MoeError) as ei:
-        pm.paged_forward(c.pool, c.dev.x, r, 0, ws[:256])
-    assert ei.value.code == pm.MOE_ERR_WORKSPACE
+    # workspace too small: the forward's own error is reported (the load buffer's
+    # read mark, recorded after a failed forward too, does not replace it), and
+    # the buffer can be filled and read again afterwards
+    for flags in (0, pm.MOE_FLAG_DEFER_READ_DONE):
+        with pytest.raises(pm.MoeError) as ei:
+            pm.paged_forward(c.pool, c.dev.x, r, 0, ws[:256], flags)
+        assert ei.value.code == pm.MOE_ERR_WORKSPACE
+        assert "workspace" in str(ei.value)
+    slots = sorted(c.dev.host_blobs)
+    pm.moe_loadbuf_fill(c.pool, 0, slots, [c.dev.host_blobs[k] for k in slots])
+    y, _ = c.forward(16)
+    torch.cuda.synchronize()
+    ids, w = oracle.route(c.layer.logits, s.k, s.S)
+    assert max_rel_err(y_f64(y), oracle.moe(c.layer.x, c.layer.w13, c.layer.w2, ids, w)) <= TOL
     # pageable host memory is refused for a fill
     pageable = torch.empty(3 * s.f * s.d, dtype=torch.bfloat16)
     with pytest.raises(pm.MoeError) as ei:
