@@ -410,7 +410,7 @@ int moe_stage_times(moe_pool *pool, float *ms, int32_t *count);
  */
 
 /*
- * How many experts to evict or add this round.  short_pages: expert pages the
+ * How many experts to evict or add in this scheduling round.  short_pages: expert pages the
  * scheduler is short of (R_b); free_pages: free expert pages (F_b).  An expert
  * holds 3 expert pages.  R_b > 0: *n_evict = ceil((R_b + 1) / 3).  Else
  * F_b < 2: *n_evict = 1.  Else F_b > 9: *n_add = min(5, floor((F_b - 9) / 3)).
