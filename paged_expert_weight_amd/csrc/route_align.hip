@@ -23,7 +23,8 @@
 //      are placed at once, in flat order.
 // Small batches run routing and alignment in one workgroup (one launch; the
 // smallest with a leaner eight-wave form); larger ones route with one wave per token and align in one workgroup up to
-// kChunkElems entries, or with histogram / scan / scatter kernels over chunks.
+// kChunkElems entries, or over chunks with two launches: the per-chunk histograms,
+// then one workgroup per chunk that scans the counts and scatters its chunk.
 #include "internal.h"
 #include "route_token.h"
 
@@ -444,88 +445,67 @@ __global__ __launch_bounds__(kAlignThreads) void k_align_hist(const RouteArgs a)
         a.counts[(int64_t)e * nchp + blockIdx.x] = hist[e];
 }
 
-// One workgroup: segment starts (left after the counts, as (start, count)
-// pairs per expert, for the scatter workgroups), num_padded; then counts[e][ch]
-// is replaced in place by the start of chunk ch's run of expert e.  Thread e
-// holds its expert's column in registers, kScanRegs chunks at a time (16-byte
-// loads, all issued before the first is used); up to kScanRegs chunks
-// (kScanRegs * kMultiChunk flat entries) the column is read once and serves
-// both the total and the cursors.
+// One workgroup per chunk of flat entries.  Every workgroup reads the whole
+// count table (E_tot columns of nch chunks: 90 KB for 90112 picks over 513
+// experts) for each expert's total and its count in the chunks before its own,
+// scans the padded totals into segment starts (the same scan in every
+// workgroup; workgroup 0 stores num_padded), then ranks and scatters its chunk
+// and writes the padding and block map of its share of the experts.  Thread e
+// holds expert e's column in registers, kScanRegs chunks at a time (16-byte
+// loads, all issued before the first is used).  Doing the scan here instead of
+// in a one-workgroup launch of its own takes a launch and its memory round
+// trips off the step.
 constexpr int kScanRegs = 48;
 
-__global__ __launch_bounds__(kAlignThreads) void k_align_scan(const RouteArgs a, int nch)
-{
-    __shared__ int seg[kMaxExpertsTotal];
-    __shared__ int segc[kMaxExpertsTotal];
-    __shared__ int tmp[kAlignWaves];
-    const int nchp = count_stride(a.T * a.keff);
-    const int e = threadIdx.x; // E_tot <= kAlignThreads
-    const bool mine = e < a.E_tot;
-    int32_t *col = a.counts + (int64_t)(mine ? e : 0) * nchp;
-    int4 v[kScanRegs / 4];
-    auto load = [&](int ch0) { // chunks ch0 .. ch0 + kScanRegs (ch0 and nchp are multiples of 4)
-#pragma unroll
-        for (int r = 0; r < kScanRegs / 4; r++)
-            v[r] = (mine && ch0 + 4 * r < nchp) ? *(const int4 *)(col + ch0 + 4 * r) : make_int4(0, 0, 0, 0);
-    };
-    // entries past nch (row padding) are never written: count only ch < nch
-    auto at = [&](int ch0, int i) {
-        const int4 q = v[i / 4];
-        const int x = (i & 3) == 0 ? q.x : (i & 3) == 1 ? q.y : (i & 3) == 2 ? q.z : q.w;
-        return ch0 + i < nch ? x : 0;
-    };
-    int c = 0;
-    for (int ch0 = 0; ch0 < nch; ch0 += kScanRegs) {
-        load(ch0);
-#pragma unroll
-        for (int i = 0; i < kScanRegs; i++)
-            c += at(ch0, i);
-    }
-    scan_segments([&](int) { return c; }, a.E_tot, a.BM, seg, segc, tmp, a);
-    if (!mine)
-        return;
-    // the segments, for the scatter workgroups that write the padding and block map
-    int32_t *segs = a.counts + (int64_t)a.E_tot * nchp;
-    segs[2 * e] = seg[e];
-    segs[2 * e + 1] = segc[e];
-    int run = seg[e]; // written by this thread in scan_segments
-    for (int ch0 = 0; ch0 < nch; ch0 += kScanRegs) {
-        if (nch > kScanRegs) // v holds the last batch: read this one again
-            load(ch0);
-        int out[kScanRegs];
-#pragma unroll
-        for (int i = 0; i < kScanRegs; i++) {
-            out[i] = run;
-            run += at(ch0, i);
-        }
-#pragma unroll
-        for (int r = 0; r < kScanRegs / 4; r++)
-            if (ch0 + 4 * r < nch)
-                *(int4 *)(col + ch0 + 4 * r) = make_int4(out[4 * r], out[4 * r + 1], out[4 * r + 2], out[4 * r + 3]);
-    }
-}
-
-__global__ __launch_bounds__(kAlignThreads) void k_align_scatter(const RouteArgs a)
+__global__ __launch_bounds__(kAlignThreads) void k_align_scatter(const RouteArgs a, int nch)
 {
     __shared__ AlignSmem sm;
     const int64_t n = a.T * a.keff;
-    const int64_t lo = (int64_t)blockIdx.x * kMultiChunk;
+    const int ch = (int)blockIdx.x;
+    const int64_t lo = (int64_t)ch * kMultiChunk;
     const int cn = (int)min((int64_t)kMultiChunk, n - lo);
-    zero_counts(sm, a.E_tot);
-    stage_ids(sm.ids, a.topk_ids + lo, cn);
-    lds_sync();
+    const int nchp = count_stride(n);
+    const int e = threadIdx.x; // E_tot <= kAlignThreads
+    const bool mine = e < a.E_tot;
+    const int32_t *col = a.counts + (int64_t)(mine ? e : 0) * nchp;
+    int tot = 0, before = 0;
+    for (int ch0 = 0; ch0 < nch; ch0 += kScanRegs) {
+        int4 v[kScanRegs / 4];
+#pragma unroll
+        for (int r = 0; r < kScanRegs / 4; r++)
+            v[r] = (mine && ch0 + 4 * r < nchp) ? *(const int4 *)(col + ch0 + 4 * r) : make_int4(0, 0, 0, 0);
+        if (ch0 == 0) { // this chunk's ids are staged while the first columns load
+            zero_counts(sm, a.E_tot);
+            stage_ids(sm.ids, a.topk_ids + lo, cn);
+        }
+        // entries past nch (row padding) are never written: count only chunks < nch
+#pragma unroll
+        for (int i = 0; i < kScanRegs; i++) {
+            const int4 q = v[i / 4];
+            const int x = (i & 3) == 0 ? q.x : (i & 3) == 1 ? q.y : (i & 3) == 2 ? q.z : q.w;
+            const int c = ch0 + i;
+            tot += c < nch ? x : 0;
+            before += c < ch ? x : 0;
+        }
+    }
+    int total;
+    const int seg = wg_exclusive_scan(mine ? (tot + a.BM - 1) / a.BM * a.BM : 0, sm.tmp, &total);
+    if (mine) {
+        sm.seg[e] = seg;
+        sm.segc[e] = tot;
+    }
+    if (ch == 0 && threadIdx.x == 0)
+        *a.num_padded = total;
     chunk_hist(sm.ids, cn, a.E_tot, sm.cnt);
     lds_sync();
-    const int nchp = count_stride(n);
-    wave_cursors([&](int e) { return a.counts[(int64_t)e * nchp + blockIdx.x]; }, a.E_tot, sm.cnt);
+    wave_cursors([&](int) { return seg + before; }, a.E_tot, sm.cnt);
     lds_sync();
     chunk_scatter(sm.ids, cn, (int)lo, a.E_tot, sm.cnt, a.sorted_ids);
     // this workgroup's share of the experts: their padding and block map (one
     // workgroup would issue all of these stores alone, at one CU's store rate)
-    const int32_t *segs = a.counts + (int64_t)a.E_tot * nchp;
     const int e0 = (int)((int64_t)blockIdx.x * a.E_tot / gridDim.x);
     const int e1 = (int)((int64_t)(blockIdx.x + 1) * a.E_tot / gridDim.x);
-    pad_segments([&](int x, int &ox, int &cx) { ox = segs[2 * x]; cx = segs[2 * x + 1]; }, e0, e1, a.BM, (int)n, a);
+    pad_segments([&](int x, int &ox, int &cx) { ox = sm.seg[x]; cx = sm.segc[x]; }, e0, e1, a.BM, (int)n, a);
 }
 
 template <int NV>
@@ -546,8 +526,7 @@ hipError_t launch_nv(const RouteArgs &a, hipStream_t s)
     } else {
         const int nch = (int)((n + kMultiChunk - 1) / kMultiChunk);
         k_align_hist<<<nch, kAlignThreads, 0, s>>>(a);
-        k_align_scan<<<1, kAlignThreads, 0, s>>>(a, nch);
-        k_align_scatter<<<nch, kAlignThreads, 0, s>>>(a);
+        k_align_scatter<<<nch, kAlignThreads, 0, s>>>(a, nch);
     }
     return hipGetLastError();
 }
@@ -559,8 +538,8 @@ int64_t route_workspace_bytes(int64_t T, int keff, int E_tot)
     const int64_t n = T * keff;
     if (n <= kChunkElems)
         return 0;
-    // counts [E_tot][stride], then (segment start, count) per expert
-    return ((int64_t)count_stride(n) + 2) * E_tot * (int64_t)sizeof(int32_t);
+    // counts [E_tot][stride]
+    return (int64_t)count_stride(n) * E_tot * (int64_t)sizeof(int32_t);
 }
 
 hipError_t launch_route_align(const RouteArgs &a, hipStream_t s)
