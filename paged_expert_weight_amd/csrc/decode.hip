@@ -88,17 +88,22 @@ __device__ __forceinline__ float wave_sum(float v) { return rt::wave_sum(v, thre
 
 // Base of matrix m (0 W1, 1 W3, 2 W2) of expert e: a pool page, a load-buffer
 // slot (W1, W3, W2 back to back), or the contiguous arrays.
+// Base of matrix m of the expert whose table entry is L (kind, idx[0..2]).
+__device__ __forceinline__ const uint16_t *matrix_base_of(const FwdArgs &a, int4 L, int m)
+{
+    const int64_t fd = (int64_t)a.f * a.d;
+    const bool in_pool = L.x == 0; // selects: no field is loaded late
+    const int64_t o = in_pool ? (int64_t)(m == 0 ? L.y : m == 1 ? L.z : L.w) * fd : ((int64_t)L.y * 3 + m) * fd;
+    return (in_pool ? a.pool : a.loadbuf) + o;
+}
+
 template <bool PAGED>
 __device__ __forceinline__ const uint16_t *matrix_base(const FwdArgs &a, int e, int m)
 {
     const int64_t fd = (int64_t)a.f * a.d;
     if constexpr (PAGED) {
         // the whole 16-byte entry in one load (the table is 16-byte aligned)
-        const int4 L = *(const int4 *)(a.locs + e); // kind, idx[0..2]
-        const bool in_pool = L.x == 0;               // selects: no field is loaded late
-        const int64_t o = in_pool ? (int64_t)(m == 0 ? L.y : m == 1 ? L.z : L.w) * fd
-                                  : ((int64_t)L.y * 3 + m) * fd;
-        return (in_pool ? a.pool : a.loadbuf) + o;
+        return matrix_base_of(a, *(const int4 *)(a.locs + e), m);
     } else {
         if (m < 2)
             return a.w13 + (int64_t)e * 2 * fd + m * fd;
@@ -111,12 +116,12 @@ __device__ __forceinline__ const uint16_t *matrix_base(const FwdArgs &a, int e, 
 // weight rows first, finds the valid picks with a ballot while those loads are
 // in flight, then reads each pick's x row (shared by all waves, so mostly from
 // L2) and writes that pick's h values.
-template <bool PAGED, int NCH, int RPW, class PickFn>
-__device__ __forceinline__ void dec_gate_up_rows(const FwdArgs &a, int e, int ncand, PickFn pick)
+template <int NCH, int RPW, class PickFn>
+__device__ __forceinline__ void dec_gate_up_rows(const FwdArgs &a, const uint16_t *w1, const uint16_t *w3, int ncand,
+                                                 PickFn pick)
 {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r0 = ((int)blockIdx.x * kDecWaves + wave) * RPW;
-    const uint16_t *w1 = matrix_base<PAGED>(a, e, 0), *w3 = matrix_base<PAGED>(a, e, 1);
     uint4 g[RPW][NCH], u[RPW][NCH];
 #pragma unroll
     for (int r = 0; r < RPW; r++)
@@ -177,7 +182,7 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_dec_gate_up(const FwdArgs a)
         return;
     const int64_t nflat = a.T * a.keff;
     const int32_t *sid = a.sorted_ids + (int64_t)b * a.BM;
-    dec_gate_up_rows<PAGED, NCH, RPW>(a, e, a.BM, [&](int i) {
+    dec_gate_up_rows<NCH, RPW>(a, matrix_base<PAGED>(a, e, 0), matrix_base<PAGED>(a, e, 1), a.BM, [&](int i) {
         const int flat = sid[i];
         return (flat >= 0 && flat < nflat) ? flat : -1;
     });
@@ -193,7 +198,10 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_dec_gate_up(const FwdArgs a)
 // routing outputs (topk ids and weights and the aligned order, the block map
 // and num_padded, as the routing kernels would), and with them the W2 base of
 // every pick, so that the down pass starts its W2 rows after one load.
-template <bool PAGED, int NCH, int NV, int RPW>
+// NL > 0: the expert table (E + S <= 64 NL entries, one per lane) is loaded
+// beside the logits, so the chosen expert's page bases follow the routing
+// without a table read in between.
+template <bool PAGED, int NCH, int NV, int RPW, int NL>
 __global__ __launch_bounds__(64 * kDecWaves) void k_dec_route_gate_up(const FwdArgs a, const DecRouteArgs ra)
 {
     constexpr int kWords = kMaxExpertsTotal / 32;
@@ -209,6 +217,14 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_dec_route_gate_up(const FwdA
         s_bits[i] = 0;
     if (tid == 0)
         s_e = -1;
+    int4 tl[NL > 0 ? NL : 1];
+    if constexpr (PAGED && NL > 0) {
+#pragma unroll
+        for (int q = 0; q < NL; q++) {
+            const int i = lane + 64 * q;
+            tl[q] = i < a.E_tot ? *(const int4 *)(a.locs + i) : make_int4(0, 0, 0, 0);
+        }
+    }
     // wave w routes tokens w and w + kDecWaves (T <= 2 * kDecWaves): both
     // tokens' logits are loaded before either is routed
     constexpr int TPW = kDecMaxT / kDecWaves;
@@ -259,8 +275,25 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_dec_route_gate_up(const FwdA
     }
     __syncthreads();
     const int e = __builtin_amdgcn_readfirstlane(s_e); // uniform: the table entry and bases load as scalars
-    if (e >= 0)
-        dec_gate_up_rows<PAGED, NCH, RPW>(a, e, n, [&](int i) { return s_ids[i] == e ? i : -1; });
+    if (e >= 0) {
+        const uint16_t *w1, *w3;
+        if constexpr (PAGED && NL > 0) {
+            const int q = e >> 6, l = e & 63;
+            int4 L = tl[0];
+#pragma unroll
+            for (int j = 1; j < NL; j++)
+                if (q == j)
+                    L = tl[j];
+            L = make_int4(__builtin_amdgcn_readlane(L.x, l), __builtin_amdgcn_readlane(L.y, l),
+                          __builtin_amdgcn_readlane(L.z, l), __builtin_amdgcn_readlane(L.w, l));
+            w1 = matrix_base_of(a, L, 0);
+            w3 = matrix_base_of(a, L, 1);
+        } else {
+            w1 = matrix_base<PAGED>(a, e, 0);
+            w3 = matrix_base<PAGED>(a, e, 1);
+        }
+        dec_gate_up_rows<NCH, RPW>(a, w1, w3, n, [&](int i) { return s_ids[i] == e ? i : -1; });
+    }
     if (blockIdx.x != 0 || blockIdx.y != 0)
         return;
     // the routing outputs, as the routing kernels write them, and the W2 base
@@ -369,7 +402,14 @@ struct RoutedGateUp {
     template <bool PAGED, int NV>
     static void go(const FwdArgs &a, const DecRouteArgs &r, dim3 g, hipStream_t s)
     {
-        k_dec_route_gate_up<PAGED, NCH_D, NV, RPW><<<g, 64 * kDecWaves, 0, s>>>(a, r);
+        // the table beside the logits pays at one token only (T=1 17.4 -> 17.2 us;
+        // T=2 and 4 measured 0.1-0.4 us slower)
+        if (PAGED && a.T == 1 && a.E_tot <= 64)
+            k_dec_route_gate_up<PAGED, NCH_D, NV, RPW, 1><<<g, 64 * kDecWaves, 0, s>>>(a, r);
+        else if (PAGED && a.T == 1 && a.E_tot <= 128)
+            k_dec_route_gate_up<PAGED, NCH_D, NV, RPW, 2><<<g, 64 * kDecWaves, 0, s>>>(a, r);
+        else
+            k_dec_route_gate_up<PAGED, NCH_D, NV, RPW, 0><<<g, 64 * kDecWaves, 0, s>>>(a, r);
     }
 };
 
