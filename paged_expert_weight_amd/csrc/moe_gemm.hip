@@ -373,10 +373,10 @@ __device__ __forceinline__ void wait_vm_lgkm0(Int<N>)
 // output element does not depend on BM, BN or the weight layout.
 constexpr int gcd_(int a, int b) { return b ? gcd_(b, a % b) : a; }
 
-// S stages of A rows and SB >= S stages of B rows: each operand has its own
-// ring of LDS buffers, and the B rows (the weights, whose misses go to HBM)
-// may be loaded further ahead than the A rows (x or h rows, mostly L2 or MALL
-// hits) when the LDS holds more B stages than A stages.
+// S stages of A rows and SB stages of B rows: each operand has its own ring of
+// LDS buffers, so one operand may be loaded further ahead than the other (the
+// B rows, weights whose misses go to HBM, or the A rows, x rows gathered by
+// token).
 template <int BM, int BN, int WAVES_M, int WAVES_N, int WK, int BK, int S, bool G1, int SB = S>
 struct Gemm {
     using Geo = StageGeom<BK>;
@@ -397,17 +397,22 @@ struct Gemm {
     static constexpr int IB = IPW - IA;
     static_assert(IA * Geo::ROWS_PER_LD * NT == BM, "A rows split evenly over the waves");
     static_assert(BM % Geo::ROWS_PER_LD == 0 && BN % Geo::ROWS_PER_LD == 0, "sections");
-    // K-steps of lookahead of the two rings, and the loop period (both ring
-    // positions are compile-time constants inside one period)
-    static constexpr int LA = S - 1, LB = SB - 1, P = S * SB / gcd_(S, SB);
+    // K-steps of lookahead of the two rings, the longer one, and the loop period
+    // (both ring positions are compile-time constants inside one period)
+    static constexpr int LA = S - 1, LB = SB - 1, LM = LA > LB ? LA : LB, P = S * SB / gcd_(S, SB);
     static constexpr int A_BYTES = BM * Geo::ROWB, B_BYTES = B_ROWS * Geo::ROWB;
     static constexpr int RING_BYTES = S * A_BYTES + SB * B_BYTES; // per K range
     static constexpr int LDS_BYTES = WK * RING_BYTES;
-    // this wave's DMA instructions issued after the A rows of the K-step awaited at
-    // a step's top (everything later in the stream may stay in flight): the B rows of
-    // the step that issued it, when B runs further ahead, and LA - 1 whole steps
-    static constexpr int N_AFTER = (LB > LA ? IB : 0) + (LA - 1) * IPW;
-    static_assert(S >= 2 && SB >= S && SB <= 8 && N_AFTER < 64, "stages");
+    // Each step issues the nearer operand's rows first, then the farther one's
+    // (A first when the lookaheads are equal).  At a step's top the rows of the
+    // step awaited last in the stream are the nearer operand's, issued Ln steps
+    // before; after them come the farther operand's rows of that step and Ln - 1
+    // whole steps, which may stay in flight.
+    static constexpr bool B_FIRST = LA > LB;
+    static constexpr int N_AFTER = LA == LB ? (LA - 1) * IPW
+                                   : B_FIRST ? IA + (LB - 1) * IPW
+                                             : IB + (LA - 1) * IPW;
+    static_assert(S >= 2 && SB >= 2 && S <= 8 && SB <= 8 && N_AFTER < 64, "stages");
     static constexpr int BM_ = BM, BN_ = BN, WK_ = WK, WAVES_N_ = WAVES_N;
     // Waves whose rows are all padding skip their MFMAs in 128-row tiles, the height
     // of layers with many small experts, whose blocks are mostly padding (414 of the
@@ -509,18 +514,30 @@ struct Gemm {
     }
 
     // The loads before the first K-step, in the order the steady state issues
-    // them (step s issues A(s + LA), then B(s + LB)), for virtual steps
-    // s = kb - LB .. kb - 1: the waits count on that order.
+    // them (step s issues A(s + LA) and B(s + LB), the nearer one first), for
+    // virtual steps s = kb - LM .. kb - 1: the waits count on that order.
     template <int V, bool STREAM>
     __device__ __forceinline__ void prologue(int kb, int ke)
     {
-        if constexpr (V < LB) {
-            constexpr int a = V - LB + LA; // A(kb + a), at A position a
-            if constexpr (a >= 0)
-                if (kb + a < ke)
-                    this->template issue_a<a % S>(kb + a);
-            if (kb + V < ke)
-                this->template issue_b<V % SB, STREAM>(kb + V);
+        if constexpr (V < LM) {
+            constexpr int a = V - LM + LA, bq = V - LM + LB; // A(kb + a), B(kb + bq)
+            auto pa = [&]() {
+                if constexpr (a >= 0)
+                    if (kb + a < ke)
+                        this->template issue_a<a % S>(kb + a);
+            };
+            auto pb = [&]() {
+                if constexpr (bq >= 0)
+                    if (kb + bq < ke)
+                        this->template issue_b<bq % SB, STREAM>(kb + bq);
+            };
+            if constexpr (B_FIRST) {
+                pb();
+                pa();
+            } else {
+                pa();
+                pb();
+            }
             this->template prologue<V + 1, STREAM>(kb, ke);
         }
     }
@@ -536,16 +553,20 @@ struct Gemm {
             // wave that shares the stages.  Only steps inside [kb, ke) are
             // loaded, so near the end fewer later loads are in flight and the
             // wait drains them all.
-            if (kt + LB - 1 < ke)
+            if (kt + LM - 1 < ke)
                 wait_vm_lgkm0(Int<N_AFTER>{});
             else
                 wait_vm_lgkm0(Int<0>{});
             if constexpr (NT > 1)
                 __builtin_amdgcn_s_barrier();
+            if constexpr (B_FIRST)
+                if (kt + LB < ke)
+                    this->template issue_b<(J + LB) % SB, STREAM>(kt + LB);
             if (kt + LA < ke)
                 this->template issue_a<(J + LA) % S>(kt + LA);
-            if (kt + LB < ke)
-                this->template issue_b<(J + LB) % SB, STREAM>(kt + LB);
+            if constexpr (!B_FIRST)
+                if (kt + LB < ke)
+                    this->template issue_b<(J + LB) % SB, STREAM>(kt + LB);
             if (kt < ke)
                 this->template compute<J % S, J % SB>();
             this->template steps<J + 1, STREAM>(kt0, ke);
