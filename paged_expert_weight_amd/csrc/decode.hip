@@ -402,14 +402,23 @@ struct RoutedGateUp {
     template <bool PAGED, int NV>
     static void go(const FwdArgs &a, const DecRouteArgs &r, dim3 g, hipStream_t s)
     {
-        // the table beside the logits pays at one token only (T=1 17.4 -> 17.2 us;
-        // T=2 and 4 measured 0.1-0.4 us slower)
-        if (PAGED && a.T == 1 && a.E_tot <= 64)
-            k_dec_route_gate_up<PAGED, NCH_D, NV, RPW, 1><<<g, 64 * kDecWaves, 0, s>>>(a, r);
-        else if (PAGED && a.T == 1 && a.E_tot <= 128)
-            k_dec_route_gate_up<PAGED, NCH_D, NV, RPW, 2><<<g, 64 * kDecWaves, 0, s>>>(a, r);
-        else
-            k_dec_route_gate_up<PAGED, NCH_D, NV, RPW, 0><<<g, 64 * kDecWaves, 0, s>>>(a, r);
+        // the table beside the logits pays at one token only (the launches with
+        // RPW = kDecRowsPerWave1; T=1 17.4 -> 17.2 us, 2 and 4 tokens measured
+        // 0.1-0.4 us slower), with E + S <= 64 (NV = 1) or <= 128 (NV <= 2)
+        constexpr bool kTable = PAGED && RPW == kDecRowsPerWave1 && NV <= 2;
+        if constexpr (kTable && NV == 1) {
+            if (a.E_tot <= 64) {
+                k_dec_route_gate_up<PAGED, NCH_D, NV, RPW, 1><<<g, 64 * kDecWaves, 0, s>>>(a, r);
+                return;
+            }
+        }
+        if constexpr (kTable) {
+            if (a.E_tot <= 128) {
+                k_dec_route_gate_up<PAGED, NCH_D, NV, RPW, 2><<<g, 64 * kDecWaves, 0, s>>>(a, r);
+                return;
+            }
+        }
+        k_dec_route_gate_up<PAGED, NCH_D, NV, RPW, 0><<<g, 64 * kDecWaves, 0, s>>>(a, r);
     }
 };
 
