@@ -39,12 +39,12 @@ HBM_PEAK_GBS = 8000.0
 # 1 GiB copy reads back, plus WRITE_SIZE), keyed by workload, T, block_m, atomic combine and a
 # hash of the GEMM sources the counters were taken on.  Reported only while that hash matches.
 MEASURED_TRAFFIC = {
-    ("mixtral", 4096, 256, False, "ec3eaf9a8e4e550f"): 3821861346,
-    ("qwen15", 1024, 128, False, "ec3eaf9a8e4e550f"): 718599675,
-    ("qwen3n", 8192, 128, False, "ec3eaf9a8e4e550f"): 2754058075,
-    ("decode", 1, 16, False, "ec3eaf9a8e4e550f"): 46326297,
-    ("decode", 8, 16, False, "ec3eaf9a8e4e550f"): 300422173,
-    ("decode", 32, 16, False, "ec3eaf9a8e4e550f"): 577640983,
+    ("mixtral", 4096, 256, False, "5f15fe591c9d3dea"): 3815101055,
+    ("qwen15", 1024, 128, False, "5f15fe591c9d3dea"): 718603284,
+    ("qwen3n", 8192, 128, False, "5f15fe591c9d3dea"): 2753745525,
+    ("decode", 1, 16, False, "5f15fe591c9d3dea"): 46328000,
+    ("decode", 8, 16, False, "5f15fe591c9d3dea"): 300422574,
+    ("decode", 32, 16, False, "5f15fe591c9d3dea"): 577644221,
 }
 GEMM_SOURCES = ("paged_expert_weight_amd/csrc/moe_gemm.hip", "paged_expert_weight_amd/csrc/decode.hip",
                 "paged_expert_weight_amd/csrc/internal.h")
