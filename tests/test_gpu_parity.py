@@ -84,6 +84,19 @@ def test_route_align_bitexact_large(name, block_m):
     _check_routing(c, r, block_m)
 
 
+# Batches past 48 alignment chunks of 2048 picks (120000 and 132000 picks): the
+# scatter workgroups read the per-chunk count table in two batches of columns.
+@pytest.mark.parametrize("S", (0, 1))
+@pytest.mark.parametrize("block_m", (16, 128))
+def test_route_align_bitexact_many_chunks(S, block_m):
+    s = synth.spec("tiny", T=12000, E=64, k=10, S=S, pool_pages=3 * (64 + S), loadbuf_experts=(), loadbuf_slots=0,
+                   seed=3200 + S)
+    c = Case(synth.make_layer(s))
+    r, _ = c.route(block_m)
+    torch.cuda.synchronize()
+    _check_routing(c, r, block_m)
+
+
 # The one-workgroup routing forms at their limits: many experts with a shared
 # one (lanes hold 8 logits each), the largest expert count (E+S = 1024) with
 # k = 32 and the most picks the smallest form takes (T*(k+S) = 495), and the
