@@ -78,6 +78,38 @@ def test_decode_step_equals_two_calls(T, bm):
     c.pool.close()
 
 
+# One-token steps across the expert counts that pick how the launch reads the
+# chosen expert's table entry: one entry per lane loaded beside the logits
+# (E + S <= 64, or <= 128 in two registers), else a table read after the
+# routing; load-buffer experts among them (the slot form of the entry).
+@pytest.mark.parametrize("E,S", [(8, 0), (63, 1), (64, 1), (100, 0), (127, 1), (128, 1), (200, 0)])
+def test_one_token_step_across_expert_counts(E, S):
+    s = synth.spec("tiny", T=1, E=E, k=4, S=S, pool_pages=3 * (E + S), loadbuf_experts=(0, 1, E // 2, E - 1),
+                   loadbuf_slots=4, seed=3300 + E)
+    L = synth.make_layer(s)
+    # the load-buffer experts are among the picks of the token
+    L.logits[0, [0, E // 2, E - 1]] += 6.0
+    c = Case(L)
+    assert pm.moe_route_forward_form(c.pool, 1) == pm.MOE_FORM_DECODE_ROUTED
+    y2, r2 = _two_calls(c, 16)
+    y1, r1 = _one_call(c, 16)
+    ws = torch.zeros(pm.moe_workspace_bytes(c.pool, 1, 16, 0), dtype=torch.uint8, device="cuda")
+    r3 = pm.RouteOut(c.pool, 1, 16)
+    y3 = torch.full_like(c.dev.x, float("nan"))
+    pm.moe_route_contiguous_forward(c.pool, c.dev.w13, c.dev.w2, c.dev.logits, c.dev.x, 16, r3.topk_ids, r3.topk_w,
+                                    r3.sorted_ids, r3.block_expert, r3.num_padded, y3, ws)
+    torch.cuda.synchronize()
+    _same_routing(r1, r2, 16)
+    _same_routing(r1, r3, 16)
+    assert torch.equal(y1, y2) and torch.equal(y1, y3)
+    ids, w = oracle.route(c.layer.logits, c.s.k, c.s.S)
+    assert np.array_equal(r1.topk_ids.cpu().numpy(), ids)
+    assert {0, E // 2, E - 1} <= set(ids[0].tolist())
+    ref = oracle.moe(c.layer.x, c.layer.w13, c.layer.w2, ids, w)
+    assert max_rel_err(y_f64(y1), ref) <= TOL
+    c.pool.close()
+
+
 @pytest.mark.parametrize("T", [1, 3, 4, 8])
 def test_decode_step_512_experts_and_shared(T):
     """E = 512 (eight logits per lane), k = 10 and the shared expert, Zipf routing."""
