@@ -34,11 +34,11 @@ struct RouteArgs {
     int32_t *block_expert;
     int32_t *num_padded;
     int64_t sorted_cap, blocks_cap;
-    int32_t *counts; // workspace: [nchunks][E_tot] (large path only)
+    int32_t *counts; // workspace: per-chunk counts [E_tot][chunks rounded up to 4] (large path only)
 };
 
 // Route + align.  Picks the fused one-workgroup path for small T, otherwise
-// route / histogram / scan / scatter.
+// route, then per-chunk histograms and a scan + scatter per chunk.
 hipError_t launch_route_align(const RouteArgs &a, hipStream_t s);
 int64_t route_workspace_bytes(int64_t T, int keff, int E_tot);
 
