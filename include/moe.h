@@ -171,7 +171,10 @@ int moe_set_expert_locs(moe_pool *pool, const moe_expert_loc *locs, int32_t n, v
 int moe_route_capacity(const moe_pool *pool, int64_t T, int32_t block_m,
                        int64_t *sorted_cap, int64_t *blocks_cap);
 
-/* Bytes of device workspace moe_route and the forwards need for (T, block_m, flags). */
+/* Bytes of device workspace moe_route and the forwards need for (T, block_m, flags).
+ * A workspace may hold anything when a call starts: every call writes each
+ * workspace byte before it reads it, and leaves nothing a later call depends
+ * on.  Calls that may overlap on the device need separate workspaces. */
 int moe_workspace_bytes(const moe_pool *pool, int64_t T, int32_t block_m, uint32_t flags,
                         size_t *bytes);
 
