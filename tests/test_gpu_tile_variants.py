@@ -39,13 +39,17 @@ CASES = [
     ("128 x 64 gate/up, 64-column down (d % 128 != 0)", 128, 192, 128, 300, 8, 2, 1),
     ("256-row tiles (f % 128 == 0, d % 256 == 0)", 256, 256, 128, 700, 4, 2, 1),
     ("256-row tiles, 64 columns (f % 128 != 0)", 256, 256, 192, 700, 4, 2, 0),
+    # experts whose last 256-row block holds 129 rows (one past the second
+    # pair of waves) and exactly 128 (the last two waves padding only)
+    ("256-row tiles, a last block of 129 rows", 256, 512, 256, 1500, 8, 2, 1, 7111),
+    ("256-row tiles, a last block of 128 rows", 256, 512, 256, 1500, 8, 2, 1, 7113),
 ]
 
 
-def _layer(i, bm, d, f, T, E, k, S):
+def _layer(i, bm, d, f, T, E, k, S, seed=None):
     spec = dataclasses.replace(synth.SPECS["tiny"], name=f"tiles{i}", T=T, d=d, f=f, E=E, k=k, S=S,
                                pool_pages=3 * (E + S) + 5, loadbuf_experts=(E - 1,), loadbuf_slots=1,
-                               zipf_s=1.2, kv_pages_per_hole=0, seed=7100 + i)
+                               zipf_s=1.2, kv_pages_per_hole=0, seed=7100 + i if seed is None else seed)
     return synth.make_layer(spec)
 
 
@@ -58,8 +62,8 @@ def _need_gpu():
 
 @pytest.mark.parametrize("i", range(len(CASES)), ids=[c[0] for c in CASES])
 def test_tile_configuration_matches_oracle(i):
-    label, bm, d, f, T, E, k, S = CASES[i]
-    layer = _layer(i, bm, d, f, T, E, k, S)
+    label, bm, d, f, T, E, k, S = CASES[i][:8]
+    layer = _layer(i, *CASES[i][1:])
     c = Case(layer)
     assert pm.moe_forward_form(c.pool, T) == pm.MOE_FORM_TILES, label
     ids, w = oracle.route(layer.logits, k, S)
@@ -68,6 +72,8 @@ def test_tile_configuration_matches_oracle(i):
     last = counts[counts > 0] % bm
     if bm == 128:  # some expert's last block has a wave of padding rows only
         assert np.any((last > 0) & (last <= 64)), label
+    if "a last block of" in label:
+        assert np.any(last == int(label.split()[-2])), label
     y, r = c.forward(bm)
     yc, _ = c.contiguous(bm)
     torch.cuda.synchronize()
