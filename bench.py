@@ -35,19 +35,21 @@ sys.path.insert(0, ROOT)
 
 METRIC = "paged fused-MoE TFLOP/s & HBM GB/s (%roofline) + overhead vs contiguous"
 HBM_PEAK_GBS = 8000.0
-# HBM bytes per k_gemm1 launch measured with rocprofv3 (FETCH_SIZE scaled by 2.0, the factor a
-# 1 GiB copy reads back, plus WRITE_SIZE), keyed by workload, T, block_m, atomic combine and a
-# hash of the GEMM sources the counters were taken on.  Reported only while that hash matches.
+# HBM bytes per launch of the roofline kernel (k_gemm1, or the decode form's gate/up launch)
+# measured with rocprofv3 (FETCH_SIZE scaled by 2.0, the factor a 1 GiB copy reads back, plus
+# WRITE_SIZE), keyed by workload, T, block_m, atomic combine and a hash of that kernel's
+# sources as the counters were taken on them.  Reported only while that hash matches.
 MEASURED_TRAFFIC = {
-    ("mixtral", 4096, 256, False, "5f15fe591c9d3dea"): 3815101055,
-    ("qwen15", 1024, 128, False, "5f15fe591c9d3dea"): 718603284,
-    ("qwen3n", 8192, 128, False, "5f15fe591c9d3dea"): 2753745525,
-    ("decode", 1, 16, False, "5f15fe591c9d3dea"): 46328000,
-    ("decode", 8, 16, False, "5f15fe591c9d3dea"): 300422574,
-    ("decode", 32, 16, False, "5f15fe591c9d3dea"): 577644221,
+    ("mixtral", 4096, 256, False, "4aa6c51d8c2dd39b"): 3815101055,
+    ("qwen15", 1024, 128, False, "4aa6c51d8c2dd39b"): 718603284,
+    ("qwen3n", 8192, 128, False, "4aa6c51d8c2dd39b"): 2753745525,
+    ("decode", 1, 16, False, "6eafe738c137ba5d"): 46328000,
+    ("decode", 8, 16, False, "6eafe738c137ba5d"): 300422574,
+    ("decode", 32, 16, False, "4aa6c51d8c2dd39b"): 577644221,
 }
-GEMM_SOURCES = ("paged_expert_weight_amd/csrc/moe_gemm.hip", "paged_expert_weight_amd/csrc/decode.hip",
-                "paged_expert_weight_amd/csrc/internal.h")
+GEMM_SOURCES = ("paged_expert_weight_amd/csrc/moe_gemm.hip", "paged_expert_weight_amd/csrc/internal.h")
+DECODE_SOURCES = ("paged_expert_weight_amd/csrc/decode.hip", "paged_expert_weight_amd/csrc/route_token.h",
+                  "paged_expert_weight_amd/csrc/internal.h")
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 MALL_BYTES = 256 << 20
 
@@ -63,16 +65,16 @@ WORKLOAD_TEXT = {
 }
 
 
-def gemm_source_hash() -> str:
-    """Hash of the kernel sources' code: comments, trailing blanks and empty lines
-    removed, so that the measured traffic stays keyed to the code it was taken on
-    and only a change of code (not of a comment) drops it.  The sources hold no
-    string literal with a comment marker."""
+def source_hash(paths=GEMM_SOURCES) -> str:
+    """Hash of kernel sources' code (the grouped GEMMs', by default): comments,
+    trailing blanks and empty lines removed, so that the measured traffic stays
+    keyed to the code it was taken on and only a change of code (not of a
+    comment) drops it.  The sources hold no string literal with a comment marker."""
     import hashlib
     import re
     h = hashlib.sha256()
     root = os.path.dirname(os.path.abspath(__file__))
-    for p in GEMM_SOURCES:
+    for p in paths:
         with open(os.path.join(root, p), encoding="utf-8") as fh:
             code = re.sub(r"//[^\n]*|/\*.*?\*/", "", fh.read(), flags=re.S)
         lines = [ln.rstrip() for ln in code.splitlines()]
@@ -80,8 +82,17 @@ def gemm_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(name, T, bm, atomic):
-    return MEASURED_TRAFFIC.get((name, T, bm, bool(atomic), gemm_source_hash()))
+def gemm_source_hash() -> str:
+    return source_hash(GEMM_SOURCES)
+
+
+def decode_source_hash() -> str:
+    return source_hash(DECODE_SOURCES)
+
+
+def measured_traffic(name, T, bm, atomic, decode_form):
+    h = decode_source_hash() if decode_form else gemm_source_hash()
+    return MEASURED_TRAFFIC.get((name, T, bm, bool(atomic), h))
 
 
 def parse():
@@ -395,7 +406,7 @@ def bench_layer(layer, args, full):
         roof = {"bound": "mfma", "achieved": round(g1_flops / g1_s / 1e12, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = measured_traffic(name, T, bm, args.atomic)
+    roof["traffic"] = measured_traffic(name, T, bm, args.atomic, routed_form or decode_form)
     roof["kernel"] = ("k_dec_route_gate_up (routing + paged gate/up, decode form: weight rows dotted with the "
                       "picks' x rows + SiLU*mul)" if routed_form else
                       "k_dec_gate_up (paged gate/up, decode form: weight rows dotted with the picks' x rows + SiLU*mul)"

@@ -234,20 +234,34 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_dec_route_gate_up(const FwdA
         const int t = wave + q * kDecWaves;
         if (t < T)
             rt::load_logits<NV>(ra.logits + (int64_t)t * ra.E, ra.E, lane, v[q]);
+        else
+#pragma unroll
+            for (int i = 0; i < NV; i++)
+                v[q][i] = 0.f;
     }
     __syncthreads(); // the bitmap is cleared
     float pv[TPW]; // the logit of pick `lane` of each routed token (for the weights)
+    bool live[TPW];
+#pragma unroll
+    for (int q = 0; q < TPW; q++)
+        live[q] = wave + q * kDecWaves < T;
+    // all of the wave's tokens at once when all are live (their cross-lane
+    // steps overlap), else the live ones one after the other
+    if (live[TPW - 1]) {
+        rt::route_ids_n<NV, TPW>(v, live, ra.E, ra.k, ra.S, lane, s_ids + wave * keff, kDecWaves * keff, nullptr, pv);
+    } else {
+#pragma unroll
+        for (int q = 0; q < TPW - 1; q++)
+            if (live[q])
+                pv[q] = rt::route_ids<NV>(v[q], ra.E, ra.k, ra.S, lane, s_ids + (wave + q * kDecWaves) * keff, nullptr);
+    }
 #pragma unroll
     for (int q = 0; q < TPW; q++) {
         const int t = wave + q * kDecWaves;
-        pv[q] = 0.f;
-        if (t < T) {
-            pv[q] = rt::route_ids<NV>(v[q], ra.E, ra.k, ra.S, lane, s_ids + t * keff, nullptr);
-            // lane j < k+S wrote pick j: mark its expert
-            if (lane < keff) {
-                const int id = s_ids[t * keff + lane];
-                atomicOr(&s_bits[id >> 5], 1u << (id & 31));
-            }
+        // lane j < k+S wrote pick j: mark its expert
+        if (t < T && lane < keff) {
+            const int id = s_ids[t * keff + lane];
+            atomicOr(&s_bits[id >> 5], 1u << (id & 31));
         }
     }
     __syncthreads();
@@ -299,11 +313,13 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_dec_route_gate_up(const FwdA
     // the routing outputs, as the routing kernels write them, and the W2 base
     // of every pick (the down pass reads its W2 rows from there)
     const int U = s_pre[nwords], BM = a.BM;
+    if (live[TPW - 1]) {
+        rt::route_weights_n<TPW>(pv, live, ra.k, ra.S, lane, ra.topk_w + (int64_t)wave * keff, kDecWaves * keff);
+    } else {
 #pragma unroll
-    for (int q = 0; q < TPW; q++) {
-        const int t = wave + q * kDecWaves;
-        if (t < T)
-            rt::route_weights(pv[q], ra.k, ra.S, lane, ra.topk_w + (int64_t)t * keff);
+        for (int q = 0; q < TPW - 1; q++)
+            if (live[q])
+                rt::route_weights(pv[q], ra.k, ra.S, lane, ra.topk_w + (int64_t)(wave + q * kDecWaves) * keff);
     }
     const uint16_t **w2b = (const uint16_t **)a.comb;
     for (int i = tid; i < n; i += NT) {

@@ -62,6 +62,25 @@ __global__ __launch_bounds__(256) void k_route(const RouteArgs a)
     route_token<NV>(v, a.E, a.k, a.S, lane, a.topk_ids + t * a.keff, a.topk_w + t * a.keff, nullptr);
 }
 
+// Route a wave's tokens (token r's outputs at flat offset off + r * step, its
+// ids also at lds_ids + r * step): all R at once when all are live, so that
+// their cross-lane steps overlap, else the live ones one after the other (an
+// interleaved round of dead tokens costs issue slots and gains nothing).
+template <int NV, int R>
+__device__ __forceinline__ void route_wave_tokens(const float (&v)[R][NV], const bool (&live)[R], const RouteArgs &a,
+                                                  int lane, int64_t off, int step, int32_t *lds_ids)
+{
+    if (live[R - 1]) {
+        route_token_n<NV, R>(v, live, a.E, a.k, a.S, lane, a.topk_ids + off, a.topk_w + off, step, lds_ids);
+        return;
+    }
+#pragma unroll
+    for (int r = 0; r < R - 1; r++)
+        if (live[r])
+            route_token<NV>(v[r], a.E, a.k, a.S, lane, a.topk_ids + off + r * step, a.topk_w + off + r * step,
+                            lds_ids + r * step);
+}
+
 // dst[i] = src[i] for i < n (n <= kChunkElems): all loads of a thread are
 // issued before any of them is waited for.
 __device__ __forceinline__ void stage_ids(int32_t *dst, const int32_t *src, int n)
@@ -282,19 +301,19 @@ __global__ __launch_bounds__(kAlignThreads) void k_route_align_small(const Route
     // all their logits first, then route them
     constexpr int TPW = kSmallTokens / kAlignWaves;
     float v[TPW][NV];
+    bool live[TPW];
 #pragma unroll
     for (int r = 0; r < TPW; r++) {
         const int t = w + r * kAlignWaves;
-        if (t < (int)a.T)
+        live[r] = t < (int)a.T;
+        if (live[r])
             load_logits<NV>(a.logits + (int64_t)t * a.E, a.E, lane, v[r]);
-    }
+        else
 #pragma unroll
-    for (int r = 0; r < TPW; r++) {
-        const int t = w + r * kAlignWaves;
-        if (t < (int)a.T)
-            route_token<NV>(v[r], a.E, a.k, a.S, lane, a.topk_ids + (int64_t)t * a.keff,
-                            a.topk_w + (int64_t)t * a.keff, sm.ids + t * a.keff);
+            for (int i = 0; i < NV; i++)
+                v[r][i] = 0.f;
     }
+    route_wave_tokens<NV, TPW>(v, live, a, lane, (int64_t)w * a.keff, kAlignWaves * a.keff, sm.ids + w * a.keff);
     lds_sync();
     align_in_one_wg(sm, (int)a.T * a.keff, a);
 }
@@ -322,19 +341,19 @@ __global__ __launch_bounds__(kTinyThreads) void k_route_align_tiny(const RouteAr
         s_cnt[i] = 0;
     constexpr int TPW = kTinyTokens / kTinyWaves;
     float v[TPW][NV];
+    bool live[TPW];
 #pragma unroll
     for (int r = 0; r < TPW; r++) {
         const int t = w + r * kTinyWaves;
-        if (t < (int)a.T)
+        live[r] = t < (int)a.T;
+        if (live[r])
             load_logits<NV>(a.logits + (int64_t)t * a.E, a.E, lane, v[r]);
-    }
+        else
 #pragma unroll
-    for (int r = 0; r < TPW; r++) {
-        const int t = w + r * kTinyWaves;
-        if (t < (int)a.T)
-            route_token<NV>(v[r], a.E, a.k, a.S, lane, a.topk_ids + (int64_t)t * a.keff,
-                            a.topk_w + (int64_t)t * a.keff, s_ids + t * a.keff);
+            for (int i = 0; i < NV; i++)
+                v[r][i] = 0.f;
     }
+    route_wave_tokens<NV, TPW>(v, live, a, lane, (int64_t)w * a.keff, kTinyWaves * a.keff, s_ids + w * a.keff);
     lds_sync();
 
     // per-wave counts and each pick's rank within its wave

@@ -3,8 +3,9 @@
 //
 // Lane L holds logits L, L+64, ..., sorted once into pick order (larger logit
 // first, equal logits by lower id); each of the k rounds takes a butterfly max
-// of the lanes' first entries and a butterfly min of the ids of the lanes whose
-// first entry equals it (DPP and lane-swap steps, no LDS), so all lanes agree
+// of the lanes' first entries (DPP and lane-swap steps, no LDS), then the id of
+// the lowest lane holding it when that is the lowest id (one entry per lane, or
+// one such lane), else a butterfly min of those lanes' ids, so all lanes agree
 // on the winner, whose lane then moves on to its next entry.  Lane j keeps pick
 // j; the weights are the softmax of the k picks renormalised over them,
 // exp(l_j - l_0) / sum_i exp(l_i - l_0), computed in fp64 and stored as fp32.
@@ -172,73 +173,156 @@ __device__ __forceinline__ void sort_lane(int (&sk)[NV], int (&si)[NV])
             order_pair(sk[t], si[t], sk[t + 1], si[t + 1]);
 }
 
-// The k picks of one token with one wave from its loaded logits.  Writes
-// ids[0 .. k+S) (and, when lds_ids is not null, the same ids into LDS) and
-// returns, in lane j < k, the logit of pick j (for route_weights).  Each lane
-// sorts its logits (lane, lane+64, ...) once into pick order; every pick is
-// then the wave maximum of the lanes' first entries, and among the lanes whose
-// first entry equals it the lowest expert id (the same order as comparing
-// (logit, id) pairs); the lane that holds it moves on to its next entry.
+// The id of a pick whose key the lanes in `tied` hold as their first entry:
+// the lowest of their ids.  With one entry per lane (NV = 1) lane L holds id L,
+// and with a single such lane there is nothing to compare, so the id is read
+// from the lowest lane of the ballot; otherwise a butterfly min of the ids.
+template <int NV>
+__device__ __forceinline__ int pick_id(bool tied, int id)
+{
+    constexpr int kNone = 0x7fffffff;
+    const uint64_t b = __ballot(tied);
+    if (NV == 1 || (b & (b - 1)) == 0)
+        return __builtin_amdgcn_readlane(id, (int)__builtin_ctzll(b));
+    return wave_min(tied ? id : kNone);
+}
+
+// The k picks of R tokens with one wave from their loaded logits (token r's
+// in v[r]).  Writes token r's ids[0 .. k+S) at ids + r * step (and, when
+// lds_ids is not null, at lds_ids + r * step) unless live[r] is false, and
+// leaves in pv[r], in lane j < k, the logit of its pick j (for
+// route_weights).  Each lane sorts its logits (lane, lane+64, ...) once into
+// pick order; every pick is then the wave maximum of the lanes' first entries,
+// and among the lanes whose first entry equals it the lowest expert id (the
+// same order as comparing (logit, id) pairs); the lane that holds it moves on
+// to its next entry.  The R tokens' cross-lane steps are independent, so a
+// round issues them together and their latencies overlap.
+template <int NV, int R>
+__device__ void route_ids_n(const float (&v)[R][NV], const bool (&live)[R], int E, int k, int S, int lane,
+                            int32_t *ids, int step, int32_t *lds_ids, float (&pv)[R])
+{
+    constexpr int kNone = 0x7fffffff, kEmpty = (int)0x80000000; // id / key of a lane's used-up entries
+    int sk[R][NV], si[R][NV];
+#pragma unroll
+    for (int r = 0; r < R; r++) {
+#pragma unroll
+        for (int i = 0; i < NV; i++) {
+            const int e = lane + 64 * i;
+            sk[r][i] = e < E ? order_key(v[r][i]) : kEmpty;
+            si[r][i] = e < E ? e : kNone;
+        }
+        sort_lane<NV>(sk[r], si[r]);
+    }
+    int my_k[R], my_id[R];
+#pragma unroll
+    for (int r = 0; r < R; r++)
+        my_k[r] = my_id[r] = 0;
+    for (int j = 0; j < k; j++) {
+        int m[R], bi[R];
+#pragma unroll
+        for (int r = 0; r < R; r++)
+            m[r] = wave_max(sk[r][0]);
+#pragma unroll
+        for (int r = 0; r < R; r++)
+            bi[r] = pick_id<NV>(sk[r][0] == m[r], si[r][0]);
+#pragma unroll
+        for (int r = 0; r < R; r++) {
+            if (lane == j) {
+                my_k[r] = m[r];
+                my_id[r] = bi[r];
+            }
+            // the lane holding the pick drops it: its entries move up by one.
+            // A bitwise blend, not a select between neighbours (which the
+            // compiler turns into an indexed access and then into compare chains)
+            const int msk = -(int)(si[r][0] == bi[r]);
+#pragma unroll
+            for (int t = 0; t + 1 < NV; t++) {
+                sk[r][t] ^= (sk[r][t] ^ sk[r][t + 1]) & msk;
+                si[r][t] ^= (si[r][t] ^ si[r][t + 1]) & msk;
+            }
+            sk[r][NV - 1] ^= (sk[r][NV - 1] ^ kEmpty) & msk;
+            si[r][NV - 1] ^= (si[r][NV - 1] ^ kNone) & msk;
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < R; r++) {
+        pv[r] = key_value(my_k[r]);
+        if (!live[r])
+            continue;
+        int32_t *o = ids + r * step;
+        if (lane < k) {
+            o[lane] = my_id[r];
+            if (lds_ids)
+                lds_ids[r * step + lane] = my_id[r];
+        }
+        if (S && lane == k) {
+            o[k] = E;
+            if (lds_ids)
+                lds_ids[r * step + k] = E;
+        }
+    }
+}
+
+// One token: returns its pick logits.
 template <int NV>
 __device__ float route_ids(const float (&v)[NV], int E, int k, int S, int lane, int32_t *ids, int32_t *lds_ids)
 {
-    constexpr int kNone = 0x7fffffff, kEmpty = (int)0x80000000; // id / key of a lane's used-up entries
-    int sk[NV], si[NV];
+    float vr[1][NV];
 #pragma unroll
-    for (int i = 0; i < NV; i++) {
-        const int e = lane + 64 * i;
-        sk[i] = e < E ? order_key(v[i]) : kEmpty;
-        si[i] = e < E ? e : kNone;
-    }
-    sort_lane<NV>(sk, si);
-    int my_k = 0, my_id = 0;
-    for (int j = 0; j < k; j++) {
-        const int m = wave_max(sk[0]);
-        const int bi = wave_min(sk[0] == m ? si[0] : kNone);
-        if (lane == j) {
-            my_k = m;
-            my_id = bi;
-        }
-        // the lane holding the pick drops it: its entries move up by one.  A
-        // bitwise blend, not a select between neighbours (which the compiler
-        // turns into an indexed access and then into compare chains)
-        const int msk = -(int)(si[0] == bi);
-#pragma unroll
-        for (int t = 0; t + 1 < NV; t++) {
-            sk[t] ^= (sk[t] ^ sk[t + 1]) & msk;
-            si[t] ^= (si[t] ^ si[t + 1]) & msk;
-        }
-        sk[NV - 1] ^= (sk[NV - 1] ^ kEmpty) & msk;
-        si[NV - 1] ^= (si[NV - 1] ^ kNone) & msk;
-    }
-    if (lane < k) {
-        ids[lane] = my_id;
-        if (lds_ids)
-            lds_ids[lane] = my_id;
-    }
-    if (S && lane == k) {
-        ids[k] = E;
-        if (lds_ids)
-            lds_ids[k] = E;
-    }
-    return key_value(my_k);
+    for (int i = 0; i < NV; i++)
+        vr[0][i] = v[i];
+    const bool live[1] = {true};
+    float pv[1];
+    route_ids_n<NV, 1>(vr, live, E, k, S, lane, ids, 0, lds_ids, pv);
+    return pv[0];
 }
 
-// The routing weights of one token from route_ids' per-lane pick logits:
+// The routing weights of R tokens from route_ids_n's per-lane pick logits
+// (token r's at w + r * step unless live[r] is false):
 // w[j] = exp(l_j - l_0) / sum_i exp(l_i - l_0) over the k picks, and 1 for
 // the shared expert (pick k).  Computed in fp64, rounded once to fp32: the
 // difference of two fp32 logits is exact in fp64, so exp of it keeps its
 // relative accuracy at any logit gap (in fp32 the rounding of l_j - l_0 alone
 // is |l_j - l_0| * 2^-24 relative after exp, 3e-6 at a gap of 50).
+template <int R>
+__device__ __forceinline__ void route_weights_n(const float (&pv)[R], const bool (&live)[R], int k, int S, int lane,
+                                                float *w, int step)
+{
+    double ex[R], sum[R];
+#pragma unroll
+    for (int r = 0; r < R; r++) {
+        const float lmax = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, pv[r])));
+        ex[r] = lane < k ? exp((double)pv[r] - (double)lmax) : 0.0;
+    }
+#pragma unroll
+    for (int r = 0; r < R; r++)
+        sum[r] = wave_sum(ex[r], lane); // commutative pairs: every lane ends with the same sum
+#pragma unroll
+    for (int r = 0; r < R; r++) {
+        if (!live[r])
+            continue;
+        if (lane < k)
+            w[r * step + lane] = (float)(ex[r] / sum[r]);
+        if (S && lane == k)
+            w[r * step + k] = 1.f;
+    }
+}
+
 __device__ __forceinline__ void route_weights(float my_v, int k, int S, int lane, float *w)
 {
-    const float lmax = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, my_v)));
-    const double ex = lane < k ? exp((double)my_v - (double)lmax) : 0.0;
-    const double sum = wave_sum(ex, lane); // commutative pairs: every lane ends with the same sum
-    if (lane < k)
-        w[lane] = (float)(ex / sum);
-    if (S && lane == k)
-        w[k] = 1.f;
+    const float pv[1] = {my_v};
+    const bool live[1] = {true};
+    route_weights_n<1>(pv, live, k, S, lane, w, 0);
+}
+
+// Route R tokens: ids and weights.
+template <int NV, int R>
+__device__ void route_token_n(const float (&v)[R][NV], const bool (&live)[R], int E, int k, int S, int lane,
+                              int32_t *ids, float *w, int step, int32_t *lds_ids)
+{
+    float pv[R];
+    route_ids_n<NV, R>(v, live, E, k, S, lane, ids, step, lds_ids, pv);
+    route_weights_n<R>(pv, live, k, S, lane, w, step);
 }
 
 // Route one token: ids and weights.
