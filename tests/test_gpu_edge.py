@@ -2,8 +2,8 @@
 oracle: one expert with k = 1, k = E, every token on one expert (one expert
 owning many blocks at every tile height), the smallest shapes (d = f = 64, and
 d not a multiple of 128), a ragged token count, a shared expert beside two
-routed ones, the largest expert count (E + S = 1024), and a batch with enough
-128-row blocks for the 512-column down tiles.  Routing ids,
+routed ones, the largest expert count (E + S = 1024), a batch with enough
+128-row blocks for the 512-column down tiles, and the empty batch (T = 0).  Routing ids,
 aligned order and block map are compared bit for bit, y within the bar, and
 paged against contiguous weights bit for bit."""
 import dataclasses
@@ -129,3 +129,42 @@ def test_edge_decode_steps(T):
         assert torch.equal(y1, y2), name
         assert max_rel_err(y_f64(y1), ref) <= TOL, name
         c.pool.close()
+
+
+def test_empty_batch_is_a_no_op():
+    """T = 0 at every entry point (route, paged, contiguous, one-call and
+    allocation-free forward): success, nothing written (the caller's buffers
+    keep their sentinels), and the next batch on the same handle and
+    workspace is unaffected."""
+    layer = synth.make_layer(EDGE["shared_beside_two"])
+    c = Case(layer)
+    s = c.s
+    logits0, x0 = c.dev.logits[:0], c.dev.x[:0]
+    for bm in (16, 128):
+        ws = pm.workspace(c.pool, 0, bm)
+        r = pm.RouteOut(c.pool, 0, bm)
+        r.num_padded.fill_(-7)
+        r.sorted_ids.fill_(-7)
+        r.block_expert.fill_(-7)
+        pm.moe_route(c.pool, logits0, bm, r.topk_ids, r.topk_w, r.sorted_ids, r.block_expert, r.num_padded, ws)
+        y = pm.paged_forward(c.pool, x0, r, c.active, ws)
+        yc = pm.contiguous_forward(c.pool, c.dev.w13, c.dev.w2, x0, r, ws)
+        y1, r1 = pm.route_forward(c.pool, logits0, x0, c.active, ws, bm)
+        r1.num_padded.fill_(-7)
+        pm.moe_route_forward_noalloc(c.pool, logits0, x0, bm, r1.topk_ids, r1.topk_w, r1.sorted_ids,
+                                     r1.block_expert, r1.num_padded, c.active, y1)
+        torch.cuda.synchronize()
+        assert y.shape[0] == yc.shape[0] == y1.shape[0] == 0
+        for t in (r.num_padded, r.sorted_ids, r.block_expert, r1.num_padded):
+            assert bool(torch.all(t == -7)), f"block_m {bm}: an empty batch wrote a routing output"
+    # a batch after the empty calls, on a workspace an empty call used
+    ids, w = oracle.route(layer.logits, s.k, s.S)
+    ref = oracle.moe(layer.x, layer.w13, layer.w2, ids, w)
+    bm = 16
+    ws = pm.workspace(c.pool, layer.T, bm)
+    pm.moe_route(c.pool, logits0, bm, r.topk_ids, r.topk_w, r.sorted_ids, r.block_expert, r.num_padded, ws)
+    y, r2 = pm.route_forward(c.pool, c.dev.logits, c.dev.x, c.active, ws, bm)
+    torch.cuda.synchronize()
+    assert np.array_equal(r2.topk_ids.cpu().numpy(), ids)
+    assert max_rel_err(y_f64(y), ref) <= TOL
+    c.pool.close()
