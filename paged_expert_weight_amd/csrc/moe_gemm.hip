@@ -652,8 +652,10 @@ __device__ __forceinline__ int stage_col(int r)
     return w * G::WN + (q % 16) * G::FN + q / 16;
 }
 
-// One output tile (block b, column tile nt) of a grouped GEMM.
-template <class G, bool G1, bool PAGED, bool ATOMIC, bool E_KNOWN>
+// One output tile (block b, column tile nt) of a grouped GEMM.  Its rows are
+// rows b*RU .. b*RU + BM - 1 of the aligned order: RU = BM, or RU = 128 for a
+// 256-row tile over a pair of 128-row blocks (k_gemm's paired blocks).
+template <class G, bool G1, bool PAGED, bool ATOMIC, bool E_KNOWN, int RU = G::BM_>
 __device__ __forceinline__ void gemm_tile(const FwdArgs &a, G &g, int b, int nt, BlockInfo bi, int nblocks,
                                           int ks = 0, int nks = 1, float *part = nullptr)
 {
@@ -671,7 +673,7 @@ __device__ __forceinline__ void gemm_tile(const FwdArgs &a, G &g, int b, int nt,
     int flat_a[IA];
 #pragma unroll
     for (int i = 0; i < IA; i++)
-        flat_a[i] = a.sorted_ids[b * BM + (g.wt + G::NT * i) * Geo::ROWS_PER_LD + lrow];
+        flat_a[i] = a.sorted_ids[b * RU + (g.wt + G::NT * i) * Geo::ROWS_PER_LD + lrow];
     int e, single;
     if constexpr (E_KNOWN) {
         e = bi.e >= 0 && bi.e < a.E_tot ? bi.e : -1;
@@ -713,7 +715,7 @@ __device__ __forceinline__ void gemm_tile(const FwdArgs &a, G &g, int b, int nt,
             if constexpr (G1) // the token's x row
                 off = pick ? (uint32_t)(flat / a.keff) * (uint32_t)d * 2u : kOOB;
             else // the block's h row
-                off = pick ? (uint32_t)(b * BM + row) * (uint32_t)f * 2u : kOOB;
+                off = pick ? (uint32_t)(b * RU + row) * (uint32_t)f * 2u : kOOB;
         } else {
             const int br = (row - BM) % BN; // B stage row (W1 / W2 rows, then W3 rows)
             off = (uint32_t)(n0 + stage_col<G>(br)) * (uint32_t)K * 2u;
@@ -734,7 +736,7 @@ __device__ __forceinline__ void gemm_tile(const FwdArgs &a, G &g, int b, int nt,
 #pragma unroll
             for (int r = 0; r < 4; r++) {
                 const int row = g.wm * G::WM + i * 16 + 4 * g.lg + r;
-                const int flat = a.sorted_ids[b * BM + row];
+                const int flat = a.sorted_ids[b * RU + row];
                 eflat[i][r] = (flat >= 0 && flat < nflat) ? flat : -1;
             }
     };
@@ -807,7 +809,7 @@ __device__ __forceinline__ void gemm_tile(const FwdArgs &a, G &g, int b, int nt,
         epilogue_weights();
 
     if constexpr (G1) { // rows without a pick (padding) are not stored: the down GEMM never reads them
-        uint16_t *hb = a.h + (int64_t)b * BM * f + n0;
+        uint16_t *hb = a.h + (int64_t)b * RU * f + n0;
 #pragma unroll
         for (int i = 0; i < G::FM; i++)
 #pragma unroll
@@ -846,24 +848,46 @@ __device__ __forceinline__ void gemm_tile(const FwdArgs &a, G &g, int b, int nt,
     }
 }
 
-template <class G, int GM, bool G1, bool PAGED, bool ATOMIC, bool TAIL, int CHUNK>
+// A tile's per-wave state: its LDS rings and the wave's place in the tile.
+template <class T>
+__device__ __forceinline__ void tile_state(T &g, uint8_t *lds)
+{
+    const int tid = threadIdx.x, lane = tid & 63;
+    g.lds = lds;
+    g.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    g.wt = g.wave % T::NT;  // wave within the tile
+    g.kg = g.wave / T::NT;  // K range of this wave
+    g.wm = g.wt / T::WAVES_N_;
+    g.wn = g.wt % T::WAVES_N_;
+    g.l16 = lane & 15;
+    g.lg = lane >> 4;
+}
+
+template <class GP>
+struct PairLds {
+    static constexpr int bytes = GP::LDS_BYTES;
+};
+template <>
+struct PairLds<void> {
+    static constexpr int bytes = 0;
+};
+
+// GP (not void; 128-row blocks, block-major tiles): blocks 2i and 2i+1 of one
+// expert run as one 256-row GP tile, GP::BN_ = BN / 2 columns wide, so the
+// pair's weight rows are staged once per 256 rows instead of once per 128
+// (the tile count per block is unchanged: block b's tile nt is the pair's
+// column tile ntiles * (b mod 2) + nt).  Other blocks run G tiles.
+template <class G, int GM, bool G1, bool PAGED, bool ATOMIC, bool TAIL, int CHUNK, class GP = void>
 __global__ __launch_bounds__(64 * G::NW) void k_gemm(const FwdArgs a)
 {
     // The host pass only needs this kernel's signature (for its launch stub);
     // the pipeline's gfx950 builtins are compiled in the device pass.
 #if defined(__HIP_DEVICE_COMPILE__)
     constexpr int BM = G::BM_, BN = G::BN_;
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[G::LDS_BYTES];
+    constexpr int LB = PairLds<GP>::bytes > G::LDS_BYTES ? PairLds<GP>::bytes : G::LDS_BYTES;
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[LB];
     G g;
-    g.lds = lds;
-    const int tid = threadIdx.x, lane = tid & 63;
-    g.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    g.wt = g.wave % G::NT;  // wave within the tile
-    g.kg = g.wave / G::NT;  // K range of this wave
-    g.wm = g.wt / G::WAVES_N_;
-    g.wn = g.wt % G::WAVES_N_;
-    g.l16 = lane & 15;
-    g.lg = lane >> 4;
+    tile_state(g, lds);
     const int ntiles = (G1 ? a.f : a.d) / BN;
     int b, nt;
     if constexpr (TAIL) {
@@ -891,6 +915,23 @@ __global__ __launch_bounds__(64 * G::NW) void k_gemm(const FwdArgs a)
     int nblocks;
     if (!tile_of<GM, TAIL, CHUNK>(a, BM, ntiles, b, nt, bi, nblocks))
         return;
+    if constexpr (!std::is_void<GP>::value) {
+        static_assert(!TAIL && GM == 1 && BM == 128 && GP::BM_ == 256 && 2 * GP::BN_ == BN && GP::NW == G::NW,
+                      "paired 128-row blocks");
+        // the block's expert and its neighbours' (read here instead of in gemm_tile)
+        const int ep = b > 0 ? a.block_expert[b - 1] : -1;
+        const int e = block_owner(a, b);
+        const int en = b + 1 < nblocks ? a.block_expert[b + 1] : -1;
+        if (e >= 0 && ((b & 1) ? ep : en) == e) {
+            GP gp;
+            tile_state(gp, lds);
+            gemm_tile<GP, G1, PAGED, ATOMIC, true, BM>(a, gp, b & ~1, ntiles * (b & 1) + nt, BlockInfo{e, 0},
+                                                       nblocks);
+        } else {
+            gemm_tile<G, G1, PAGED, ATOMIC, true>(a, g, b, nt, BlockInfo{e, ep != e && en != e}, nblocks);
+        }
+        return;
+    }
     gemm_tile<G, G1, PAGED, ATOMIC, TAIL>(a, g, b, nt, bi, nblocks);
 #endif
 }
@@ -1054,11 +1095,14 @@ __global__ __launch_bounds__(256) void k_resolve(const ResolveArgs r, const FwdA
 
 // Tile shapes per block height: the gate/up and down GEMMs,
 // Gemm<BM, BN, waves M, waves N, split-K waves, BK, stages, gate/up>.
-template <int BM_, class G1T, class G2T, int CHUNK1_ = 0, int CHUNK2_ = 0>
+template <int BM_, class G1T, class G2T, int CHUNK1_ = 0, int CHUNK2_ = 0, class P1T = void, class P2T = void>
 struct Tiles {
     static constexpr int BM = BM_;
     using K1 = G1T;
     using K2 = G2T;
+    // tiles of paired 128-row blocks (void: none)
+    using P1 = P1T;
+    using P2 = P2T;
     // tiles dealt to the XCDs in chunks of this many (0: contiguous eighths), per launch
     static constexpr int CHUNK1 = CHUNK1_, CHUNK2 = CHUNK2_;
     static_assert(G1T::BM_ == BM_ && G2T::BM_ == BM_, "block height");
@@ -1089,7 +1133,8 @@ using Tiles128d = Tiles<128, Gate128, Down128w>;
 // 400 -> 376 us); with few blocks the halved tile count leaves CUs idle (a
 // 1024-token Qwen1.5-shaped layer: 69 -> 70 us), hence kWideDownTiles
 using Down128x = Gemm<128, 512, 2, 4, 1, 64, 2, false>;
-using Tiles128wx = Tiles<128, Gemm<128, 256, 2, 4, 1, 64, 2, true>, Down128x, kXcdChunkWide>;
+using Tiles128wx = Tiles<128, Gemm<128, 256, 2, 4, 1, 64, 2, true>, Down128x, kXcdChunkWide, 0,
+                         Gemm<256, 128, 4, 2, 1, 64, 2, true>, Gemm<256, 256, 4, 2, 1, 64, 2, false>>;
 using Tiles128dx = Tiles<128, Gate128, Down128x>;
 constexpr int64_t kWideDownTiles = 1024; // 512-column down tiles from this many on (at most blocks x d / 512)
 // when d is not a multiple of 128 (d and f are multiples of 64)
@@ -1164,8 +1209,8 @@ hipError_t launch_tiles_t(const FwdArgs &a_in, hipStream_t s)
     // the split-tail launches deal their tiles in chunks (kXcdChunk unless the table says otherwise)
     constexpr int C1 = C::CHUNK1 ? C::CHUNK1 : (TAIL ? kXcdChunk : 0);
     constexpr int C2 = C::CHUNK2 ? C::CHUNK2 : (TAIL ? kXcdChunk : 0);
-    auto k1 = k_gemm<G1T, GM, true, PAGED, false, TAIL, C1>;
-    auto k2 = k_gemm<G2T, GM, false, PAGED, ATOMIC, TAIL, C2>;
+    auto k1 = k_gemm<G1T, GM, true, PAGED, false, TAIL, C1, typename C::P1>;
+    auto k2 = k_gemm<G2T, GM, false, PAGED, ATOMIC, TAIL, C2, typename C::P2>;
     a.slots[0] = a.slots[1] = 0;
     if constexpr (TAIL) {
         const int p1 = resident_slots((const void *)k1, T1), p2 = resident_slots((const void *)k2, T2);

@@ -2,8 +2,9 @@
 oracle: one expert with k = 1, k = E, every token on one expert (one expert
 owning many blocks at every tile height), the smallest shapes (d = f = 64, and
 d not a multiple of 128), a ragged token count, a shared expert beside two
-routed ones, the largest expert count (E + S = 1024), a batch with enough
-128-row blocks for the 512-column down tiles, and the empty batch (T = 0).  Routing ids,
+routed ones, the largest expert count (E + S = 1024), batches with enough
+128-row blocks for the 512-column down tiles (one of them with experts whose
+blocks run in pairs as 256-row tiles), and the empty batch (T = 0).  Routing ids,
 aligned order and block map are compared bit for bit, y within the bar, and
 paged against contiguous weights bit for bit."""
 import dataclasses
@@ -44,6 +45,11 @@ EDGE = {
     # tiles, with f not a multiple of 256 (64-column gate/up tiles beside them)
     "wide_down": _spec("wide_down", T=600, d=512, f=192, E=1023, k=2, S=1, pool_pages=3 * 1024 + 5,
                        loadbuf_experts=tuple(range(1010, 1023)), loadbuf_slots=16, seed=4009),
+    # the same with f a multiple of 256 (256 + 256-column gate/up tiles) and skewed routing, so
+    # that experts with several 128-row blocks run pairs of them as 256-row tiles (the shared
+    # expert's 2000 rows are 16 blocks), beside single-block experts and odd last blocks
+    "wide_pairs": _spec("wide_pairs", T=2000, d=512, f=256, E=1023, k=2, S=1, pool_pages=3 * 1024 + 5,
+                        loadbuf_experts=tuple(range(1010, 1023)), loadbuf_slots=16, zipf_s=1.1, seed=4010),
 }
 
 
