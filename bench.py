@@ -40,12 +40,12 @@ HBM_PEAK_GBS = 8000.0
 # WRITE_SIZE), keyed by workload, T, block_m, atomic combine and a hash of that kernel's
 # sources as the counters were taken on them.  Reported only while that hash matches.
 MEASURED_TRAFFIC = {
-    ("mixtral", 4096, 256, False, "4aa6c51d8c2dd39b"): 3804437061,
-    ("qwen15", 1024, 128, False, "4aa6c51d8c2dd39b"): 718600743,
-    ("qwen3n", 8192, 128, False, "4aa6c51d8c2dd39b"): 2766481218,
-    ("decode", 1, 16, False, "fe5e8ea014cba59d"): 46334767,
-    ("decode", 8, 16, False, "fe5e8ea014cba59d"): 300422732,
-    ("decode", 32, 16, False, "4aa6c51d8c2dd39b"): 577644276,
+    ("mixtral", 4096, 256, False, "d6fda7df82d698e1"): 3812226821,
+    ("qwen15", 1024, 128, False, "d6fda7df82d698e1"): 718600108,
+    ("qwen3n", 8192, 128, False, "d6fda7df82d698e1"): 2774475391,
+    ("decode", 1, 16, False, "fe5e8ea014cba59d"): 46334585,
+    ("decode", 8, 16, False, "fe5e8ea014cba59d"): 300421338,
+    ("decode", 32, 16, False, "d6fda7df82d698e1"): 577641550,
 }
 GEMM_SOURCES = ("paged_expert_weight_amd/csrc/moe_gemm.hip", "paged_expert_weight_amd/csrc/internal.h")
 DECODE_SOURCES = ("paged_expert_weight_amd/csrc/decode.hip", "paged_expert_weight_amd/csrc/route_token.h",
